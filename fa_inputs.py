@@ -1,0 +1,72 @@
+"""Seeded synthetic inputs and the named workloads for exact-attention forward.
+
+This module serves both the GPU library's tests/benchmark and the CPU oracle's
+tests.  It holds no arithmetic of the method: it only draws i.i.d. N(0, 1)
+values in fp32 from a seeded CPU generator and rounds them (round to nearest
+even, torch's cast) to the workload's dtype, so the GPU path and the oracle see
+identical bits.
+
+Workload shapes follow the pages' own examples: a GPT-style causal call with
+the default scale (FlashAttention技术解析 page, section 2.2), seq 4096 with
+head_dim 64 (the benchmark row on the Flash-Attention compile-guide page,
+section 性能与内存占用测试验证), the (128, 128) sliding window (same page,
+section 滑动窗口注意力), and a 16K causal sequence (the V2 page's A100 16K
+figure, section 二.2) with a 32K variant (table 1 of the first page).  Batch
+and head counts are not stated on the pages and are fixed here.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    S: int
+    D: int
+    dtype: torch.dtype
+    causal: bool
+    window: tuple
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    def describe(self) -> str:
+        dt = {torch.float32: "fp32", torch.float16: "fp16", torch.bfloat16: "bf16"}[self.dtype]
+        mask = "causal" if self.causal else "full"
+        if self.window != (-1, -1):
+            mask = f"window{self.window}" + ("+causal" if self.causal else "")
+        return f"B{self.B} H{self.H} S{self.S} D{self.D} {dt} {mask}"
+
+
+WORKLOADS = {
+    "tiny_fp32": Workload("tiny_fp32", 1, 2, 128, 64, torch.float32, False, (-1, -1), 1),
+    "gpt_causal_2k": Workload("gpt_causal_2k", 2, 16, 2048, 64, torch.bfloat16, True, (-1, -1), 2),
+    "full_4k_d64": Workload("full_4k_d64", 4, 16, 4096, 64, torch.float16, False, (-1, -1), 3),
+    "window_8k": Workload("window_8k", 2, 16, 8192, 128, torch.bfloat16, False, (128, 128), 4),
+    "causal_16k": Workload("causal_16k", 1, 16, 16384, 128, torch.bfloat16, True, (-1, -1), 5),
+    "causal_32k": Workload("causal_32k", 1, 16, 32768, 128, torch.bfloat16, True, (-1, -1), 6),
+}
+
+
+def make_qkv(B: int, S: int, H: int, D: int, dtype: torch.dtype, seed: int):
+    """q, k, v as contiguous CPU tensors [B, S, H, D], drawn in that order from
+    one torch CPU generator seeded with ``seed``, fp32 N(0, 1), then cast."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    out = []
+    for _ in range(3):
+        t = torch.randn((B, S, H, D), generator=g, dtype=torch.float32)
+        out.append(t.to(dtype).contiguous())
+    return tuple(out)
+
+
+def workload_qkv(w: Workload, seed: int | None = None):
+    return make_qkv(w.B, w.S, w.H, w.D, w.dtype, w.seed if seed is None else seed)

@@ -1,0 +1,152 @@
+"""CPU oracle for exact attention (forward): plain, slow, fp64.
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares
+no code with the GPU library (``io_aware_exact_22_amd``) and imports nothing
+from it; the two meet only in the seeded input generator, which holds none of
+the method's arithmetic.
+
+The arithmetic lives in ``fa_oracle.c`` (the definition of exact attention,
+materialising the score matrix in fp64, one head at a time).  This module only
+builds and loads that file and marshals arguments to it.
+
+Pages are cited by title: the formula is in "大模型加速新突破：Flash Attention V2
+核心网络算子解析" section 二.1; the causal/window/scale arguments are in
+"FlashAttention技术解析：加速GPT训练的核心优化" section 2.2.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libfa_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+DTYPE_CODES = {"fp32": 0, "fp16": 1, "bf16": 2}
+
+
+def build(force: bool = True) -> str:
+    """Compile fa_oracle.c with gcc (CPU only) into libfa_oracle.so."""
+    if not force and os.path.exists(_LIB_PATH) and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-shared", "-fPIC", "-Wall", "-Wextra",
+           _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        override = os.environ.get("FA_ORACLE_LIB")  # a prebuilt variant, for the mutation tests
+        if override:
+            lib = ctypes.CDLL(override)
+        else:
+            build(force=False)
+            lib = ctypes.CDLL(_LIB_PATH)
+        i64, vp, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double
+        lib.fa_oracle_fwd.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, dp,
+                                      ctypes.c_int, i64, i64, vp, vp, ctypes.c_int]
+        lib.fa_oracle_fwd.restype = ctypes.c_int
+        lib.fa_oracle_fwd_rows.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, dp,
+                                           ctypes.c_int, i64, i64, i64, i64, i64, i64, vp, vp,
+                                           ctypes.c_int]
+        lib.fa_oracle_fwd_rows.restype = ctypes.c_int
+        lib.fa_oracle_allowed_pairs.argtypes = [i64, ctypes.c_int, i64, i64]
+        lib.fa_oracle_allowed_pairs.restype = i64
+        lib.fa_oracle_decode.argtypes = [vp, ctypes.c_int, i64, vp]
+        lib.fa_oracle_decode.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    codes = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+    if t.dtype not in codes:
+        raise TypeError(f"oracle: unsupported dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _check_inputs(q, k, v):
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cpu":
+            raise TypeError(f"oracle: {name} must be a CPU torch tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"oracle: {name} must be contiguous [B, S, H, D]")
+        if t.dim() != 4 or t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("oracle: q, k, v must share shape [B, S, H, D] and dtype")
+
+
+def _window(window_size):
+    wl, wr = window_size
+    return int(wl), int(wr)
+
+
+def fwd(q, k, v, scale: float, causal: bool = False, window_size=(-1, -1), nthreads: int = 0):
+    """Exact attention over all rows.  q, k, v: CPU tensors [B, S, H, D] in fp32,
+    fp16 or bf16 (their bits are decoded exactly).  Returns (out [B,S,H,D] fp64,
+    lse [B,H,S] fp64) as numpy arrays."""
+    _check_inputs(q, k, v)
+    lib = _load()
+    B, S, H, D = q.shape
+    wl, wr = _window(window_size)
+    out = np.empty((B, S, H, D), dtype=np.float64)
+    lse = np.empty((B, H, S), dtype=np.float64)
+    rc = lib.fa_oracle_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), B, H, S, D,
+                           float(scale), int(bool(causal)), wl, wr, out.ctypes.data,
+                           lse.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle: fa_oracle_fwd failed ({rc})")
+    return out, lse
+
+
+def fwd_rows(q, k, v, scale: float, causal: bool, window_size, b: int, h: int, i0: int, i1: int,
+             nthreads: int = 0):
+    """Exact attention for query rows [i0, i1) of head (b, h).  Returns
+    (out [(i1-i0), D] fp64, lse [(i1-i0)] fp64)."""
+    _check_inputs(q, k, v)
+    lib = _load()
+    B, S, H, D = q.shape
+    wl, wr = _window(window_size)
+    R = i1 - i0
+    out = np.empty((max(R, 0), D), dtype=np.float64)
+    lse = np.empty((max(R, 0),), dtype=np.float64)
+    rc = lib.fa_oracle_fwd_rows(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q), B, H, S,
+                                D, float(scale), int(bool(causal)), wl, wr, b, h, i0, i1,
+                                out.ctypes.data, lse.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle: fa_oracle_fwd_rows failed ({rc})")
+    return out, lse
+
+
+def allowed_pairs(S: int, causal: bool, window_size=(-1, -1)) -> int:
+    """Brute-force count of allowed (query, key) pairs, i.e. S * S_eff."""
+    wl, wr = _window(window_size)
+    return int(_load().fa_oracle_allowed_pairs(S, int(bool(causal)), wl, wr))
+
+
+def decode(t) -> np.ndarray:
+    """The oracle's own decoding of every element of a contiguous CPU tensor
+    (fp32, fp16 or bf16) to fp64, flattened."""
+    if not t.is_contiguous():
+        raise ValueError("oracle: decode needs a contiguous tensor")
+    out = np.empty((t.numel(),), dtype=np.float64)
+    rc = _load().fa_oracle_decode(t.data_ptr(), _dtype_code(t), t.numel(), out.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle: decode failed")
+    return out

@@ -1,0 +1,240 @@
+/*
+ * fa_oracle.c -- the CPU oracle for exact attention (forward).
+ *
+ * TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the tests, the smoke check and
+ * the CPU-baseline leg of the benchmark may load this library.  It shares no
+ * code, header, table or constant with the GPU library, and the GPU library
+ * never calls it.
+ *
+ * What it computes is the plain definition of exact attention, written out in
+ * fp64 with the full score matrix materialised, one (batch, head) at a time:
+ *
+ *   allowed(i,j) = (!causal || j <= i) && (wl < 0 || i - j <= wl)
+ *                                       && (wr < 0 || j - i <= wr)
+ *   s_ij  = scale * sum_d q[b,i,h,d] * k[b,j,h,d]     (allowed j only)
+ *   p_ij  = exp(s_ij - m_i) / sum_j' exp(s_ij' - m_i),  m_i = max_j s_ij
+ *   O[b,i,h,:]  = sum_j p_ij * v[b,j,h,:]
+ *   LSE[b,h,i]  = m_i + ln(sum_j exp(s_ij - m_i))   (= ln sum_j exp(s_ij))
+ *
+ * Sources (pages are named by their titles):
+ *  - the formula Softmax(QK^T / sqrt(d_k)) V: "大模型加速新突破：Flash Attention
+ *    V2核心网络算子解析", section 二.1 (算法核心创新), the core formula;
+ *  - the arguments softmax_scale (default 1/sqrt(head_dim)), causal and
+ *    window_size=(left,right) with (-1,-1) meaning full attention:
+ *    "FlashAttention技术解析：加速GPT训练的核心优化", section 2.2, the
+ *    configuration example and its parameter notes; the window example
+ *    window_size=(128,128) in "突破大模型训练瓶颈：Flash-Attention编译优化与
+ *    内存占用解决方案", section 滑动窗口注意力;
+ *  - the input layout (batch, seq_len, head, dim): the V2 page, section 三.1
+ *    (代码实现要点), the comment on the input shape;
+ *  - the result is exact, not approximated: the project tagline quoted on the
+ *    compile-guide page ("exact attention");
+ *  - the log-domain statistic (log of the sum of exponentials) that LSE is:
+ *    the V2 page, section 二.1, step 2 (增量软最大值).
+ *
+ * Readings where the pages are silent:
+ *  - window bounds are inclusive and "left" means earlier positions;
+ *  - causal together with a window is the intersection of the two masks;
+ *  - a row with no allowed key (unreachable with windows >= -1, since j = i is
+ *    always allowed) gets O = 0 and LSE = -inf;
+ *  - NaN propagates as in IEEE arithmetic: the max of a set holding a NaN is
+ *    NaN, so a NaN score makes the whole row NaN;
+ *  - bf16/fp16/fp32 inputs are decoded exactly to fp64 (subnormals kept).
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC fa_oracle.c -o libfa_oracle.so -lm
+ * No -ffast-math: the oracle depends on IEEE inf/NaN semantics.
+ */
+#include <math.h>
+#include <omp.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_FP32 0
+#define ORC_FP16 1
+#define ORC_BF16 2
+
+/* IEEE-754 binary32: reinterpret the 32 bits. */
+static double orc_decode_fp32(uint32_t bits) {
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* IEEE-754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
+ * bits.  Written from the format's definition, subnormals included. */
+static double orc_decode_fp16(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)f, -24); /* 0.f * 2^-14 */
+    else if (e == 31)
+        mag = (f == 0) ? INFINITY : NAN;
+    else
+        mag = ldexp(1024.0 + (double)f, e - 25); /* 1.f * 2^(e-15) */
+    return sign ? -mag : mag;
+}
+
+/* bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits -- the
+ * upper half of a binary32.  Written from the field definition. */
+static double orc_decode_bf16(uint16_t b) {
+    int sign = (b >> 15) & 1;
+    int e = (b >> 7) & 0xff;
+    int f = b & 0x7f;
+    double mag;
+    if (e == 0)
+        mag = ldexp((double)f, -133); /* 0.f * 2^-126 */
+    else if (e == 255)
+        mag = (f == 0) ? INFINITY : NAN;
+    else
+        mag = ldexp(128.0 + (double)f, e - 134); /* 1.f * 2^(e-127) */
+    return sign ? -mag : mag;
+}
+
+static double orc_load(const void* base, int dtype, int64_t idx) {
+    switch (dtype) {
+    case ORC_FP32: return orc_decode_fp32(((const uint32_t*)base)[idx]);
+    case ORC_FP16: return orc_decode_fp16(((const uint16_t*)base)[idx]);
+    default: return orc_decode_bf16(((const uint16_t*)base)[idx]);
+    }
+}
+
+static int orc_allowed(int64_t i, int64_t j, int causal, int64_t wl, int64_t wr) {
+    if (causal && j > i) return 0;
+    if (wl >= 0 && i - j > wl) return 0;
+    if (wr >= 0 && j - i > wr) return 0;
+    return 1;
+}
+
+/* Decodes n elements of raw input bits to fp64, so the tests can check the
+ * decoders against other implementations of the formats. */
+int fa_oracle_decode(const void* base, int dtype, int64_t n, double* out) {
+    if (dtype != ORC_FP32 && dtype != ORC_FP16 && dtype != ORC_BF16) return -1;
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_load(base, dtype, i);
+    return 0;
+}
+
+/* Number of (i, j) pairs with allowed(i, j), over 0 <= i, j < S. */
+int64_t fa_oracle_allowed_pairs(int64_t S, int causal, int64_t wl, int64_t wr) {
+    int64_t n = 0;
+    for (int64_t i = 0; i < S; ++i)
+        for (int64_t j = 0; j < S; ++j) n += orc_allowed(i, j, causal, wl, wr);
+    return n;
+}
+
+static int orc_check(int dtype, int64_t B, int64_t H, int64_t S, int64_t D,
+                     int64_t wl, int64_t wr) {
+    if (dtype != ORC_FP32 && dtype != ORC_FP16 && dtype != ORC_BF16) return -1;
+    if (B < 1 || H < 1 || S < 1 || D < 1) return -1;
+    if (wl < -1 || wr < -1) return -1;
+    return 0;
+}
+
+/*
+ * Query rows [i0, i1) of one (b, h).  out_rows is [(i1 - i0), D] fp64,
+ * lse_rows is [(i1 - i0)] fp64.  The (i1 - i0) x S score matrix of this head
+ * is materialised in full; rows run in parallel over nthreads OpenMP threads
+ * (0 = the OpenMP default).
+ */
+int fa_oracle_fwd_rows(const void* q, const void* k, const void* v, int dtype,
+                       int64_t B, int64_t H, int64_t S, int64_t D, double scale,
+                       int causal, int64_t wl, int64_t wr, int64_t b, int64_t h,
+                       int64_t i0, int64_t i1, double* out_rows, double* lse_rows,
+                       int nthreads) {
+    if (orc_check(dtype, B, H, S, D, wl, wr)) return -1;
+    if (b < 0 || b >= B || h < 0 || h >= H || i0 < 0 || i1 > S || i0 > i1) return -1;
+    const int64_t R = i1 - i0;
+    if (R == 0) return 0;
+    /* element (b, s, h, d) of a [B, S, H, D] tensor */
+#define ORC_IDX(s_, d_) ((((b) * S + (s_)) * H + (h)) * D + (d_))
+    double* Q = (double*)malloc(sizeof(double) * (size_t)(R * D));
+    double* K = (double*)malloc(sizeof(double) * (size_t)(S * D));
+    double* V = (double*)malloc(sizeof(double) * (size_t)(S * D));
+    double* P = (double*)malloc(sizeof(double) * (size_t)(R * S)); /* scores, then probabilities */
+    if (!Q || !K || !V || !P) {
+        free(Q); free(K); free(V); free(P);
+        return -2;
+    }
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t d = 0; d < D; ++d) Q[r * D + d] = orc_load(q, dtype, ORC_IDX(i0 + r, d));
+    for (int64_t j = 0; j < S; ++j)
+        for (int64_t d = 0; d < D; ++d) {
+            K[j * D + d] = orc_load(k, dtype, ORC_IDX(j, d));
+            V[j * D + d] = orc_load(v, dtype, ORC_IDX(j, d));
+        }
+#undef ORC_IDX
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads)
+    for (int64_t r = 0; r < R; ++r) {
+        const int64_t i = i0 + r;
+        double* prow = P + r * S;
+        /* 1. scores of the allowed keys; -inf elsewhere */
+        for (int64_t j = 0; j < S; ++j) {
+            if (!orc_allowed(i, j, causal, wl, wr)) {
+                prow[j] = -INFINITY;
+                continue;
+            }
+            double dot = 0.0;
+            for (int64_t d = 0; d < D; ++d) dot += Q[r * D + d] * K[j * D + d];
+            prow[j] = scale * dot;
+        }
+        /* 2. row max (a NaN anywhere makes it NaN) */
+        double m = -INFINITY;
+        for (int64_t j = 0; j < S; ++j) {
+            if (isnan(prow[j])) {
+                m = prow[j];
+                break;
+            }
+            if (prow[j] > m) m = prow[j];
+        }
+        double* orow = out_rows + r * D;
+        if (m == -INFINITY) { /* no allowed key */
+            for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
+            lse_rows[r] = -INFINITY;
+            continue;
+        }
+        /* 3. softmax: exp(s - m), sum, divide */
+        double l = 0.0;
+        for (int64_t j = 0; j < S; ++j) {
+            prow[j] = exp(prow[j] - m);
+            l += prow[j];
+        }
+        for (int64_t j = 0; j < S; ++j) prow[j] /= l;
+        /* 4. O = P V */
+        for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
+        for (int64_t j = 0; j < S; ++j) {
+            if (!orc_allowed(i, j, causal, wl, wr)) continue; /* p = 0 exactly */
+            const double p = prow[j];
+            for (int64_t d = 0; d < D; ++d) orow[d] += p * V[j * D + d];
+        }
+        lse_rows[r] = m + log(l);
+    }
+    free(Q); free(K); free(V); free(P);
+    return 0;
+}
+
+/*
+ * Every (b, h), all rows.  out is [B, S, H, D] fp64 and lse is [B, H, S] fp64.
+ */
+int fa_oracle_fwd(const void* q, const void* k, const void* v, int dtype, int64_t B,
+                  int64_t H, int64_t S, int64_t D, double scale, int causal, int64_t wl,
+                  int64_t wr, double* out, double* lse, int nthreads) {
+    if (orc_check(dtype, B, H, S, D, wl, wr)) return -1;
+    double* rows = (double*)malloc(sizeof(double) * (size_t)(S * D));
+    if (!rows) return -2;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < H; ++h) {
+            int rc = fa_oracle_fwd_rows(q, k, v, dtype, B, H, S, D, scale, causal, wl, wr, b,
+                                        h, 0, S, rows, lse + (b * H + h) * S, nthreads);
+            if (rc) {
+                free(rows);
+                return rc;
+            }
+            for (int64_t i = 0; i < S; ++i)
+                memcpy(out + ((b * S + i) * H + h) * D, rows + i * D, sizeof(double) * (size_t)D);
+        }
+    free(rows);
+    return 0;
+}

@@ -1,0 +1,43 @@
+"""Plants plausible mistakes in copies of the CPU oracle (on the CPU only) and
+checks that the pins in test_oracle_pins.py catch every one of them."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "fa_oracle.c")
+
+MUTANTS = {
+    "scale_dropped": ("prow[j] = scale * dot;", "prow[j] = dot;"),
+    "causal_off_by_one": ("if (causal && j > i) return 0;", "if (causal && j >= i) return 0;"),
+    "window_left_off_by_one": ("if (wl >= 0 && i - j > wl) return 0;", "if (wl >= 0 && i - j >= wl) return 0;"),
+    "window_right_mirrored": ("if (wr >= 0 && j - i > wr) return 0;", "if (wr >= 0 && i - j > wr) return 0;"),
+    "k_replaced_by_v": ("dot += Q[r * D + d] * K[j * D + d];", "dot += Q[r * D + d] * V[j * D + d];"),
+    "no_normalisation": ("prow[j] /= l;", "prow[j] /= 1.0;"),
+    "lse_without_max": ("lse_rows[r] = m + log(l);", "lse_rows[r] = log(l);"),
+    "exp_sign_flipped": ("prow[j] = exp(prow[j] - m);", "prow[j] = exp(m - prow[j]);"),
+    "head_seq_strides_swapped": ("((((b) * S + (s_)) * H + (h)) * D + (d_))",
+                                 "((((b) * H + (h)) * S + (s_)) * D + (d_))"),
+    "fp16_bias_off": ("mag = ldexp(1024.0 + (double)f, e - 25);", "mag = ldexp(1024.0 + (double)f, e - 24);"),
+    "bf16_subnormal_off": ("mag = ldexp((double)f, -133);", "mag = ldexp((double)f, -134);"),
+    "max_ignores_nan": ("if (isnan(prow[j])) {", "if (0) {"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site not found once: {old}"
+    mpath = tmp_path / "mutant.c"
+    mpath.write_text(src.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-shared", "-fPIC", str(mpath), "-o",
+                    str(lib), "-lm"], check=True)
+    env = dict(os.environ, FA_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
