@@ -1,0 +1,122 @@
+/*
+ * fa_mi355x.h -- C ABI of libfa_mi355x: exact attention forward on MI355X
+ * (gfx950), fused so the S x S score matrix never reaches HBM.
+ *
+ * Pages are cited by their titles:
+ *   [V2]  "大模型加速新突破：Flash Attention V2核心网络算子解析"
+ *   [FA]  "FlashAttention技术解析：加速GPT训练的核心优化"
+ *   [CG]  "突破大模型训练瓶颈：Flash-Attention编译优化与内存占用解决方案"
+ *   [AN]  "FlashAttention 剖析"
+ *
+ * What fa_fwd computes, for every batch b, head h and query row i:
+ *   allowed(i,j) = (!causal || j <= i) && (wl < 0 || i - j <= wl)
+ *                                       && (wr < 0 || j - i <= wr)
+ *   O[b,i,h,:]   = sum_j softmax_j(scale * q_i . k_j over allowed j) * v[b,j,h,:]
+ *   LSE[b,h,i]   = ln sum_{allowed j} exp(scale * q_i . k_j)
+ * The formula is [V2] section 二.1; softmax_scale, causal and
+ * window_size = (left, right) with -1 = unbounded are [FA] section 2.2 and
+ * [CG] section 滑动窗口注意力 (bounds inclusive, "left" = earlier keys, causal
+ * with a window = both masks); the (batch, seq_len, head, dim) layout is [V2]
+ * section 三.1.  The method -- tiles of Q, K, V, a running row max and row sum
+ * ("online renormalisation", [FA] section 1; [AN] section 3), intermediates
+ * kept on chip ([CG] 项目核心价值; [AN] section 2) -- reaches this exact result
+ * up to floating-point rounding.
+ *
+ * Every function is thread-safe and re-entrant.  The library keeps no state
+ * and allocates no memory.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_DTYPE_FP32 = 0, /* IEEE binary32 inputs and output; fp32 MFMA arithmetic */
+    FA_DTYPE_FP16 = 1, /* IEEE binary16 inputs and output; fp32 accumulation */
+    FA_DTYPE_BF16 = 2  /* bfloat16 inputs and output; fp32 accumulation */
+} fa_dtype_t;
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = -1,     /* a required pointer is NULL */
+    FA_ERR_SHAPE = -2,    /* B, H or S < 1, or a size overflows int64 / the index range */
+    FA_ERR_HEAD_DIM = -3, /* D not supported (supported: 64, 128) */
+    FA_ERR_WINDOW = -4,   /* window_left or window_right < -1, or causal not 0/1 */
+    FA_ERR_DTYPE = -5,    /* dtype not one of fa_dtype_t */
+    FA_ERR_SCALE = -6,    /* scale NaN, infinite or negative */
+    FA_ERR_ALIGN = -7,    /* q, k, v or out not 16-byte aligned, or lse not 4-byte aligned */
+    FA_ERR_ALIAS = -8,    /* out or lse overlaps an input, or out overlaps lse */
+    FA_ERR_HIP = -9       /* the kernel launch failed (hipGetLastError) */
+} fa_status_t;
+
+/*
+ * fa_fwd -- one fused attention forward over all (b, h).
+ *
+ * q, k, v  device pointers, contiguous [B, S, H, D] of `dtype` (row stride
+ *          H*D elements).  Read only.
+ * out      device pointer, contiguous [B, S, H, D] of `dtype`; fully written.
+ *          O is rounded to nearest-even from fp32.
+ * lse      device pointer, contiguous [B, H, S] fp32; fully written with the
+ *          natural-log log-sum-exp of the scaled, masked scores of each row.
+ * B, H, S  batch, heads, sequence length (one S for queries and keys), >= 1.
+ * D        head dimension: 64 or 128.
+ * scale    softmax scale applied to q.k in fp32 (finite, >= 0); callers that
+ *          want the pages' default pass 1/sqrt(D).
+ * causal   0 or 1.
+ * window_left, window_right   >= -1; -1 = unbounded on that side; a value
+ *          >= S behaves as unbounded.
+ * stream   hipStream_t to enqueue on; NULL = the default stream.
+ *
+ * Ownership: the caller owns all five buffers; the library allocates nothing.
+ * The call validates its arguments first (no HIP call, no write on error),
+ * then enqueues one kernel and returns without synchronising.  Results are
+ * valid once `stream` has been synchronised; faults during execution surface
+ * there.  Repeated calls on the same inputs give bitwise identical results.
+ * Returns FA_OK or a negative fa_status_t.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
+           int64_t H, int64_t S, int64_t D, float scale, int causal, int64_t window_left,
+           int64_t window_right, int dtype, void* stream);
+
+/*
+ * fa_fwd_check_args -- the validation fa_fwd performs, as a pure function: no
+ * HIP call, no memory access through the pointers (they are compared only).
+ * Returns FA_OK or the status fa_fwd would return before launching.
+ */
+int fa_fwd_check_args(const void* q, const void* k, const void* v, const void* out,
+                      const float* lse, int64_t B, int64_t H, int64_t S, int64_t D, float scale,
+                      int causal, int64_t window_left, int64_t window_right, int dtype);
+
+/* fa_status_string -- a static, human-readable message for a status code. */
+const char* fa_status_string(int status);
+
+/*
+ * fa_fwd_tile_schedule -- host-side description of the tile schedule fa_fwd
+ * uses for one Q tile (tiles of Q and of K/V: [V2] section 二.1 step 1; [AN]
+ * section 3).  Pure function, no HIP call.
+ *
+ * For Q tile `q_tile` (rows [q_tile*BM, min(S, (q_tile+1)*BM))), writes the
+ * tile shape (*bm, *bn), the number of Q tiles (*n_q_tiles) and the
+ * half-open range [*kt_begin, *kt_end) of K/V tiles the kernel visits; K/V
+ * tiles outside it hold no allowed key for any row of the Q tile and are
+ * skipped.  If needs_mask is non-NULL and has room for (*kt_end - *kt_begin)
+ * entries (max_tiles), needs_mask[t - *kt_begin] is 1 when tile t holds at
+ * least one key that is not allowed for some row of the Q tile (or lies past
+ * S), else 0 (the kernel skips the mask there).
+ * Returns FA_OK, or FA_ERR_* for bad arguments / q_tile out of range /
+ * max_tiles too small.
+ */
+int fa_fwd_tile_schedule(int64_t S, int64_t D, int dtype, int causal, int64_t window_left,
+                         int64_t window_right, int64_t q_tile, int64_t* bm, int64_t* bn,
+                         int64_t* n_q_tiles, int64_t* kt_begin, int64_t* kt_end,
+                         uint8_t* needs_mask, int64_t max_tiles);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

@@ -1,0 +1,15 @@
+"""io_aware_exact_22_amd -- exact attention forward for MI355X (gfx950).
+
+``libfa_mi355x.so`` holds the hand-written HIP kernels and a C ABI
+(``include/fa_mi355x.h``); this package is a thin ctypes binding over it.
+PyTorch supplies device memory and streams only: every arithmetic step of the
+forward pass runs in the library's kernels, and the binding raises if the
+library is missing rather than falling back to anything else.
+"""
+from .fa import (FA_DTYPE_BF16, FA_DTYPE_FP16, FA_DTYPE_FP32, FaError, fa_fwd, fa_fwd_check_args,
+                 fa_fwd_tile_schedule, fa_status_string, flash_attn_fwd, library_path)
+
+__all__ = [
+    "FA_DTYPE_BF16", "FA_DTYPE_FP16", "FA_DTYPE_FP32", "FaError", "fa_fwd", "fa_fwd_check_args",
+    "fa_fwd_tile_schedule", "fa_status_string", "flash_attn_fwd", "library_path",
+]

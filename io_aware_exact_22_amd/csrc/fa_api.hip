@@ -1,0 +1,144 @@
+// fa_api.hip -- the C ABI of libfa_mi355x (declared in include/fa_mi355x.h):
+// argument validation, status strings, the host view of the tile schedule and
+// the dispatch to the gfx950 kernels.  No allocation, no global state.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_launch.h"
+#include "fa_mi355x.h"
+#include "fa_schedule.h"
+
+#define FA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+bool mul_ok(int64_t a, int64_t b, int64_t* r) { return !__builtin_mul_overflow(a, b, r); }
+
+// [p, p + n) and [q, q + m) overlap (byte ranges)
+bool overlaps(const void* p, int64_t n, const void* q, int64_t m) {
+    const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+    return a < b + (uintptr_t)m && b < a + (uintptr_t)n;
+}
+
+int64_t elem_size(int dtype) { return dtype == fa::kDtypeFp32 ? 4 : 2; }
+
+// Shape / window / dtype checks shared by fa_fwd_check_args and
+// fa_fwd_tile_schedule; *tensor_bytes and *lse_bytes are set on success.
+int check_problem(int64_t B, int64_t H, int64_t S, int64_t D, int causal, int64_t wl, int64_t wr,
+                  int dtype, int64_t* tensor_bytes, int64_t* lse_bytes) {
+    if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16)
+        return FA_ERR_DTYPE;
+    if (B < 1 || H < 1 || S < 1) return FA_ERR_SHAPE;
+    if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+    if ((causal != 0 && causal != 1) || wl < -1 || wr < -1) return FA_ERR_WINDOW;
+    // the kernels index rows with 32-bit S, B, H and launch B*H*ceil(S/128)
+    // workgroups of 256 threads (grid limit: 2^32 - 1 work-items)
+    if (S > INT32_MAX || B > INT32_MAX || H > INT32_MAX) return FA_ERR_SHAPE;
+    const int64_t n_qt = (S + fa::q_tile_rows() - 1) / fa::q_tile_rows();
+    int64_t n_wg, t;
+    if (!mul_ok(B, H, &t) || !mul_ok(t, n_qt, &n_wg) || n_wg > (int64_t)(UINT32_MAX / 256))
+        return FA_ERR_SHAPE;
+    int64_t elems, rows;
+    if (!mul_ok(B, S, &rows) || !mul_ok(rows, H, &t) || !mul_ok(t, D, &elems) ||
+        !mul_ok(elems, elem_size(dtype), tensor_bytes))
+        return FA_ERR_SHAPE;
+    if (!mul_ok(rows, H, &t) || !mul_ok(t, 4, lse_bytes)) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+}  // namespace
+
+FA_API const char* fa_status_string(int status) {
+    switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "B, H and S must be >= 1 and the sizes must fit the index ranges";
+    case FA_ERR_HEAD_DIM: return "unsupported head dimension D (supported: 64, 128)";
+    case FA_ERR_WINDOW: return "causal must be 0 or 1 and window bounds must be >= -1";
+    case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_FP32, FA_DTYPE_FP16 or FA_DTYPE_BF16";
+    case FA_ERR_SCALE: return "scale must be finite and >= 0";
+    case FA_ERR_ALIGN: return "q, k, v, out must be 16-byte aligned and lse 4-byte aligned";
+    case FA_ERR_ALIAS: return "out and lse must not overlap the inputs or each other";
+    case FA_ERR_HIP: return "the HIP kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+FA_API int fa_fwd_check_args(const void* q, const void* k, const void* v, const void* out,
+                             const float* lse, int64_t B, int64_t H, int64_t S, int64_t D,
+                             float scale, int causal, int64_t window_left, int64_t window_right,
+                             int dtype) {
+    if (!q || !k || !v || !out || !lse) return FA_ERR_NULL;
+    int64_t nbytes = 0, lbytes = 0;
+    const int rc = check_problem(B, H, S, D, causal, window_left, window_right, dtype, &nbytes,
+                                 &lbytes);
+    if (rc != FA_OK) return rc;
+    if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) & 15u) return FA_ERR_ALIGN;
+    if ((uintptr_t)lse & 3u) return FA_ERR_ALIGN;
+    const void* ins[3] = {q, k, v};
+    for (const void* in : ins)
+        if (overlaps(out, nbytes, in, nbytes) || overlaps(lse, lbytes, in, nbytes))
+            return FA_ERR_ALIAS;
+    if (overlaps(out, nbytes, lse, lbytes)) return FA_ERR_ALIAS;
+    return FA_OK;
+}
+
+FA_API int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
+                  int64_t H, int64_t S, int64_t D, float scale, int causal, int64_t window_left,
+                  int64_t window_right, int dtype, void* stream) {
+    const int rc = fa_fwd_check_args(q, k, v, out, lse, B, H, S, D, scale, causal, window_left,
+                                     window_right, dtype);
+    if (rc != FA_OK) return rc;
+    fa::LaunchArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.lse = lse;
+    a.B = B;
+    a.H = H;
+    a.S = S;
+    a.D = D;
+    // exp(scale * s) = exp2(scale * log2(e) * s): one FMA feeds v_exp_f32
+    a.c = (float)((double)scale * 1.4426950408889634);
+    a.causal = causal;
+    a.wl = window_left >= S ? -1 : window_left;  // a window reaching past S is unbounded
+    a.wr = window_right >= S ? -1 : window_right;
+    a.dtype = dtype;
+    a.stream = (hipStream_t)stream;
+    const hipError_t e = fa::launch_fwd(a);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+FA_API int fa_fwd_tile_schedule(int64_t S, int64_t D, int dtype, int causal, int64_t window_left,
+                                int64_t window_right, int64_t q_tile, int64_t* bm, int64_t* bn,
+                                int64_t* n_q_tiles, int64_t* kt_begin, int64_t* kt_end,
+                                uint8_t* needs_mask, int64_t max_tiles) {
+    if (!bm || !bn || !n_q_tiles || !kt_begin || !kt_end) return FA_ERR_NULL;
+    int64_t nbytes, lbytes;
+    const int rc = check_problem(1, 1, S, D, causal, window_left, window_right, dtype, &nbytes,
+                                 &lbytes);
+    if (rc != FA_OK) return rc;
+    const int64_t BM = fa::q_tile_rows(), BN = fa::kv_tile_keys(dtype);
+    const int64_t nq = (S + BM - 1) / BM;
+    if (q_tile < 0 || q_tile >= nq) return FA_ERR_SHAPE;
+    const fa::MaskSpec m{S, causal, window_left >= S ? -1 : window_left,
+                         window_right >= S ? -1 : window_right};
+    int64_t t0, t1;
+    fa::q_tile_kv_range(m, q_tile, BM, BN, &t0, &t1);
+    *bm = BM;
+    *bn = BN;
+    *n_q_tiles = nq;
+    *kt_begin = t0;
+    *kt_end = t1;
+    if (needs_mask) {
+        if (max_tiles < t1 - t0) return FA_ERR_SHAPE;
+        const int64_t r0 = q_tile * BM;
+        for (int64_t t = t0; t < t1; ++t)
+            needs_mask[t - t0] = fa::tile_needs_mask(m, r0, r0 + BM - 1, t * BN, BN) ? 1 : 0;
+    }
+    return FA_OK;
+}

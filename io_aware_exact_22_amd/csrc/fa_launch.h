@@ -1,0 +1,34 @@
+// fa_launch.h -- internal interface between the C ABI (fa_api.hip) and the
+// kernel launchers (fa_fwd_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+constexpr int kDtypeFp32 = 0;
+constexpr int kDtypeFp16 = 1;
+constexpr int kDtypeBf16 = 2;
+
+struct LaunchArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    void* out;
+    float* lse;
+    int64_t B, H, S, D;
+    float c;  // scale * log2(e): scores enter exp2 directly
+    int causal;
+    int64_t wl, wr;  // already clamped to [-1, S]
+    int dtype;
+    hipStream_t stream;
+};
+
+// Enqueues the forward kernel for validated arguments.
+hipError_t launch_fwd(const LaunchArgs& a);
+// Tile shape the kernels use: Q rows per workgroup, keys per K/V tile.
+int64_t q_tile_rows();
+int64_t kv_tile_keys(int dtype);
+
+}  // namespace fa

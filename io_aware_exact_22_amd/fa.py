@@ -1,0 +1,161 @@
+"""ctypes binding of libfa_mi355x (declared in include/fa_mi355x.h).
+
+Same names as the C ABI: ``fa_fwd``, ``fa_fwd_check_args``,
+``fa_status_string``, ``fa_fwd_tile_schedule``; plus ``flash_attn_fwd``, the
+tensor-level call that mirrors the pages' ``flash_attention(q, k, v,
+softmax_scale=None, causal=..., window_size=(-1, -1))`` argument list
+("FlashAttention技术解析：加速GPT训练的核心优化", section 2.2).  This module only
+marshals arguments; it computes nothing of the method itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+FA_DTYPE_FP32 = 0
+FA_DTYPE_FP16 = 1
+FA_DTYPE_BF16 = 2
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libfa_mi355x.so")
+_lock = threading.Lock()
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A non-zero fa_status_t from the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_string(status)} (status {status})")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                f"{_LIB_PATH} is not built; build it with io_aware_exact_22_amd.build.build() "
+                "(or __graft_entry__.build()).  There is no fallback implementation.")
+        # torch first: its HIP runtime (same soname) must be the one the library binds to, so
+        # that torch's streams and allocations are valid in the library
+        import torch  # noqa: F401
+
+        lib = ctypes.CDLL(_LIB_PATH)
+        i64, vp, cint = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, cint, i64,
+                               i64, cint, vp]
+        lib.fa_fwd.restype = cint
+        lib.fa_fwd_check_args.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float,
+                                          cint, i64, i64, cint]
+        lib.fa_fwd_check_args.restype = cint
+        lib.fa_status_string.argtypes = [cint]
+        lib.fa_status_string.restype = ctypes.c_char_p
+        p64 = ctypes.POINTER(ctypes.c_int64)
+        lib.fa_fwd_tile_schedule.argtypes = [i64, i64, cint, cint, i64, i64, i64, p64, p64, p64,
+                                             p64, p64, vp, i64]
+        lib.fa_fwd_tile_schedule.restype = cint
+        _lib = lib
+        return lib
+
+
+# ------------------------------------------------------------------ raw C ABI
+def fa_fwd(q: int, k: int, v: int, out: int, lse: int, B: int, H: int, S: int, D: int,
+           scale: float, causal: int, window_left: int, window_right: int, dtype: int,
+           stream: int | None) -> int:
+    """The C entry point with raw device pointers (ints); returns the status."""
+    return _load().fa_fwd(q, k, v, out, lse, B, H, S, D, scale, causal, window_left, window_right,
+                          dtype, stream)
+
+
+def fa_fwd_check_args(q: int, k: int, v: int, out: int, lse: int, B: int, H: int, S: int, D: int,
+                      scale: float, causal: int, window_left: int, window_right: int,
+                      dtype: int) -> int:
+    return _load().fa_fwd_check_args(q, k, v, out, lse, B, H, S, D, scale, causal, window_left,
+                                     window_right, dtype)
+
+
+def fa_status_string(status: int) -> str:
+    return _load().fa_status_string(int(status)).decode()
+
+
+def fa_fwd_tile_schedule(S: int, D: int, dtype: int, causal: int, window_left: int,
+                         window_right: int, q_tile: int) -> dict:
+    """Host view of the K/V tiles the kernel visits for one Q tile."""
+    lib = _load()
+    vals = [ctypes.c_int64() for _ in range(5)]
+    rc = lib.fa_fwd_tile_schedule(S, D, dtype, causal, window_left, window_right, q_tile,
+                                  *[ctypes.byref(x) for x in vals], None, 0)
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_tile_schedule")
+    bm, bn, nq, t0, t1 = (x.value for x in vals)
+    mask = (ctypes.c_uint8 * max(1, t1 - t0))()
+    rc = lib.fa_fwd_tile_schedule(S, D, dtype, causal, window_left, window_right, q_tile,
+                                  *[ctypes.byref(x) for x in vals], mask, t1 - t0)
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_tile_schedule")
+    return {"bm": bm, "bn": bn, "n_q_tiles": nq, "kt_begin": t0, "kt_end": t1,
+            "needs_mask": [int(mask[i]) for i in range(t1 - t0)]}
+
+
+# ------------------------------------------------------------------ tensor call
+def _dtype_code(t) -> int:
+    import torch
+
+    codes = {torch.float32: FA_DTYPE_FP32, torch.float16: FA_DTYPE_FP16,
+             torch.bfloat16: FA_DTYPE_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype} (fp32, fp16, bf16)")
+    return codes[t.dtype]
+
+
+def flash_attn_fwd(q, k, v, softmax_scale: float | None = None, causal: bool = False,
+                   window_size=(-1, -1), out=None, lse=None, dropout_p: float = 0.0,
+                   alibi_slopes=None, stream=None):
+    """Exact attention forward on the GPU.
+
+    q, k, v: CUDA (HIP) tensors [B, S, H, D], contiguous, one dtype (fp32,
+    fp16 or bf16), D in {64, 128}.  softmax_scale None means 1/sqrt(D).
+    Returns (out [B, S, H, D] in the input dtype, lse [B, H, S] fp32).  Runs
+    on ``stream`` (a torch stream) or torch's current stream, asynchronously.
+    """
+    import torch
+
+    if dropout_p != 0.0:
+        raise NotImplementedError("dropout is not part of the exact forward pass")
+    if alibi_slopes is not None:
+        raise NotImplementedError("ALiBi slopes are not supported")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise TypeError(f"{name} must be a GPU tensor")
+        if t.dim() != 4 or t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must share shape [B, S, H, D], dtype and device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, S, H, D]")
+    B, S, H, D = q.shape
+    dtype = _dtype_code(q)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 tensor [B, H, S]")
+    wl, wr = (int(x) for x in window_size)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
+                    S, D, scale, int(bool(causal)), wl, wr, dtype, st.cuda_stream)
+    if rc != 0:
+        raise FaError(rc, "fa_fwd")
+    return out, lse

@@ -1,0 +1,152 @@
+"""Host-side tests of libfa_mi355x (no GPU needed): the library loads, exports
+every function include/fa_mi355x.h declares, validates arguments as the header
+states, and its tile schedule covers exactly the allowed (query, key) pairs."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+import io_aware_exact_22_amd as fa
+from io_aware_exact_22_amd import fa as fam
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_mi355x.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == {"fa_fwd", "fa_fwd_check_args", "fa_status_string", "fa_fwd_tile_schedule"}
+    lib = ctypes.CDLL(fa.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(names) <= exported
+    # nothing else of ours leaks out (hidden visibility)
+    assert not [s for s in exported if s.startswith("_ZN2fa")]
+
+
+def test_status_strings():
+    for st in range(0, -10, -1):
+        s = fa.fa_status_string(st)
+        assert s and s != "unknown status"
+    assert fa.fa_status_string(-99) == "unknown status"
+
+
+# fake, aligned, disjoint device addresses: fa_fwd_check_args never dereferences
+Q, K, V, OUT, LSE = 1 << 32, 2 << 32, 3 << 32, 4 << 32, 5 << 32
+GOOD = dict(q=Q, k=K, v=V, out=OUT, lse=LSE, B=2, H=4, S=300, D=128, scale=0.125, causal=1,
+            window_left=-1, window_right=-1, dtype=fa.FA_DTYPE_BF16)
+
+
+def check(**kw):
+    a = dict(GOOD, **kw)
+    return fa.fa_fwd_check_args(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["S"],
+                                a["D"], a["scale"], a["causal"], a["window_left"],
+                                a["window_right"], a["dtype"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, 0),
+    ({"q": 0}, -1), ({"k": 0}, -1), ({"v": 0}, -1), ({"out": 0}, -1), ({"lse": 0}, -1),
+    ({"B": 0}, -2), ({"H": 0}, -2), ({"S": 0}, -2), ({"S": -5}, -2),
+    ({"S": 1 << 40}, -2), ({"B": 1 << 40, "H": 1 << 30}, -2),
+    ({"D": 96}, -3), ({"D": 0}, -3), ({"D": 256}, -3),
+    ({"window_left": -2}, -4), ({"window_right": -7}, -4), ({"causal": 2}, -4),
+    ({"dtype": 3}, -5), ({"dtype": -1}, -5),
+    ({"scale": float("nan")}, -6), ({"scale": float("inf")}, -6), ({"scale": -0.5}, -6),
+    ({"scale": 0.0}, 0), ({"window_left": 0, "window_right": 0}, 0), ({"window_left": 10**9}, 0),
+    ({"q": Q + 8}, -7), ({"out": OUT + 2}, -7), ({"lse": LSE + 2}, -7), ({"lse": LSE + 4}, 0),
+    ({"out": Q}, -8), ({"out": K + 64}, -8), ({"lse": V + 1024}, -8),
+    ({"lse": OUT + 2 * 300 * 4 * 128 * 2 - 16}, -8), ({"lse": OUT + 2 * 300 * 4 * 128 * 2}, 0),
+    ({"q": K}, 0),  # inputs may alias each other (read only)
+])
+def test_check_args(kw, status):
+    assert check(**kw) == status
+
+
+def test_fa_fwd_rejects_before_any_hip_call():
+    # invalid arguments return the status without touching the GPU (none here)
+    rc = fa.fa_fwd(Q, K, V, OUT, LSE, 1, 1, 128, 96, 0.1, 0, -1, -1, fa.FA_DTYPE_BF16, None)
+    assert rc == -3
+    rc = fa.fa_fwd(0, K, V, OUT, LSE, 1, 1, 128, 64, 0.1, 0, -1, -1, fa.FA_DTYPE_BF16, None)
+    assert rc == -1
+
+
+def allowed(i, j, causal, wl, wr):
+    return (not causal or j <= i) and (wl < 0 or i - j <= wl) and (wr < 0 or j - i <= wr)
+
+
+SCHEDULES = [
+    (1, 0, -1, -1), (7, 1, -1, -1), (63, 0, 3, 0), (129, 1, -1, -1), (200, 0, 20, 40),
+    (300, 1, 5, -1), (300, 0, 0, 0), (257, 0, -1, 100), (1000, 1, 64, 64), (520, 0, 128, 128),
+    (2048 + 5, 1, -1, -1), (700, 0, 700, 699), (1500, 1, 1499, 3),
+]
+
+
+@pytest.mark.parametrize("S,causal,wl,wr", SCHEDULES)
+@pytest.mark.parametrize("dtype", [fa.FA_DTYPE_BF16, fa.FA_DTYPE_FP32])
+def test_tile_schedule_against_brute_force(S, causal, wl, wr, dtype):
+    """Every allowed pair lies in a visited tile; every visited tile holds an
+    allowed pair of the Q tile; a tile marked mask-free has every pair
+    allowed (rows of the Q tile, keys < S)."""
+    first = fa.fa_fwd_tile_schedule(S, 128, dtype, causal, wl, wr, 0)
+    bm, bn, nq = first["bm"], first["bn"], first["n_q_tiles"]
+    assert nq == (S + bm - 1) // bm
+    for qt in range(nq):
+        sch = fa.fa_fwd_tile_schedule(S, 128, dtype, causal, wl, wr, qt)
+        rows = range(qt * bm, min(S, (qt + 1) * bm))
+        t0, t1 = sch["kt_begin"], sch["kt_end"]
+        for t in range(-(-S // bn)):
+            keys = range(t * bn, min(S, (t + 1) * bn))
+            any_ok = any(allowed(i, j, causal, wl, wr) for i in rows for j in keys)
+            assert any_ok == (t0 <= t < t1), (qt, t)
+            if t0 <= t < t1 and not sch["needs_mask"][t - t0]:
+                assert (t + 1) * bn <= S
+                assert all(allowed(i, j, causal, wl, wr) for i in rows for j in keys)
+
+
+def test_tile_schedule_counts_causal_16k():
+    """S = 16384 causal at 128 x 64 tiles: 129 * 128 - ... visited tiles per
+    head: Q tile t visits 2t + 2 tiles, two of which need the mask."""
+    tot, masked = 0, 0
+    for qt in range(128):
+        s = fa.fa_fwd_tile_schedule(16384, 128, fa.FA_DTYPE_BF16, 1, -1, -1, qt)
+        assert s["kt_end"] - s["kt_begin"] == 2 * qt + 2
+        tot += s["kt_end"] - s["kt_begin"]
+        masked += sum(s["needs_mask"])
+    assert tot == 16512 and masked == 256
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(fam, "_LIB_PATH", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(fam, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        fam.fa_status_string(0)
+
+
+@pytest.mark.parametrize("S,causal,window", [(128, False, (-1, -1)), (2048, True, (-1, -1)),
+                                             (1000, False, (128, 128)), (777, True, (30, 5)),
+                                             (300, False, (0, 0)), (50, False, (100, 3))])
+def test_bench_pair_count_matches_oracle(S, causal, window):
+    """bench.py's closed-form S_eff count against the oracle's brute force."""
+    import bench
+    import oracle
+
+    assert bench.allowed_pairs(S, causal, window) == oracle.allowed_pairs(S, causal, window)
+
+
+def test_bench_refuses_several_gpus():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "8"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
