@@ -70,42 +70,36 @@ def measured_traffic(workload: str):
 
 
 def cpu_baseline(w, q, k, v, target_s: float = 15.0):
-    """Time the CPU oracle (as it stands) on a block of consecutive middle rows
-    of head (0, 0); report the rate on the metric's FLOP count."""
-    import numpy as np
-
+    """Time the CPU oracle (as it stands) on whole heads of the workload: one
+    head first, then as many heads (b, h) in order as fit about target_s
+    seconds; report the rate on the metric's FLOP count."""
     import oracle
 
     threads = min(16, len(os.sched_getaffinity(0)))
-    wl, wr = w.window
+    per_head_flops = 4.0 * allowed_pairs(w.S, w.causal, w.window) * w.D
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
 
-    def n_keys(rows):
-        i = np.asarray(rows, dtype=np.int64)
-        lo = np.zeros_like(i) if wl < 0 else np.maximum(0, i - wl)
-        hi = np.full_like(i, w.S - 1) if wr < 0 else np.minimum(w.S - 1, i + wr)
-        if w.causal:
-            hi = np.minimum(hi, i)
-        return int(np.maximum(0, hi - lo + 1).sum())
-
-    def run(R):
-        r0 = max(0, w.S // 2 - R // 2)
-        r1 = min(w.S, r0 + R)
+    def run(hs):
         t0 = time.perf_counter()
-        oracle.fwd_rows(q, k, v, w.scale, w.causal, w.window, 0, 0, r0, r1, nthreads=threads)
-        dt = time.perf_counter() - t0
-        return r0, r1, dt, 4.0 * n_keys(range(r0, r1)) * w.D
+        for b, h in hs:
+            oracle.fwd_rows(q, k, v, w.scale, w.causal, w.window, b, h, 0, w.S, nthreads=threads)
+        return time.perf_counter() - t0
 
-    R = 64
-    r0, r1, dt, fl = run(R)
-    R = int(min(w.S, max(R, R * target_s / max(dt, 1e-3))))
-    r0, r1, dt, fl = run(R)
+    dt1 = run(heads[:1])
+    n = int(max(1, min(len(heads), target_s / max(dt1, 1e-3))))
+    if n > 1:
+        dt, used = run(heads[:n]), n
+    else:
+        dt, used = dt1, 1
+    fl = per_head_flops * used
     return {
         "value": fl / dt / 1e12,
         "unit": "TFLOPS",
         "cores": threads,
         "kind": "oracle",
-        "sample": (f"{w.name}: rows [{r0}, {r1}) of head (b=0, h=0), fp64 oracle materialising "
-                   f"the score rows; {fl / 1e9:.1f} GFLOP (metric count) in {dt:.1f} s"),
+        "sample": (f"{w.name}: {used} of {len(heads)} (batch, head) pairs in full, fp64 oracle "
+                   f"materialising each head's score matrix; {fl / 1e9:.1f} GFLOP (metric count) "
+                   f"in {dt:.1f} s on {threads} threads"),
     }
 
 
@@ -116,6 +110,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="instead of the benchmark, run --steps plain device copies of this many "
+                         "MiB (the reference kernel for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -131,6 +128,17 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                          "steps": args.steps}))
+        return 0
     w = WORKLOADS[args.workload]
     dt_name = {torch.float32: "fp32", torch.float16: "fp16", torch.bfloat16: "bf16"}[w.dtype]
     q, k, v = workload_qkv(w)

@@ -50,8 +50,20 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}) building libfa_mi355x.so")
     if verbose and msgs:
         print("\n".join(msgs))
+    check_launch_stubs(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def check_launch_stubs(path: str) -> None:
+    """hipcc's host pass can drop a kernel's launch stub without a diagnostic
+    (e.g. when a device-only builtin sits inside a lambda of a kernel
+    template); the library then fails to load.  Refuse such a build."""
+    r = subprocess.run(["nm", "-C", "--undefined-only", path], capture_output=True, text=True)
+    missing = [ln.split(None, 1)[-1] for ln in r.stdout.splitlines() if "__device_stub__" in ln]
+    if missing:
+        os.remove(path)
+        raise RuntimeError("hipcc emitted no host launch stub for: " + "; ".join(missing))
 
 
 if __name__ == "__main__":

@@ -61,6 +61,12 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kWaveRows = 32;             // query rows per wave
 constexpr int kBM = kWaves * kWaveRows;   // query rows per workgroup
 constexpr float kNegInf = -__builtin_inff();
+// word 3 of a raw (stride 0) buffer resource on gfx9-family GPUs
+constexpr int kBufferFlags = 0x00020000;
+// log2-domain slack before the running reference max is moved (weights <= 2^8)
+constexpr float kRescaleSlack = 8.f;
+
+template <bool B> struct BoolTag { static constexpr bool value = B; };
 
 // ---------------------------------------------------------------- dtype traits
 template <typename T> struct Mfma;
@@ -116,32 +122,57 @@ __device__ inline int k_row_for_mfma_row(int m) {
 }
 
 // ---------------------------------------------------------------- bf16 / fp16
-// LDS row strides (elements), padded for conflict-free MFMA operand reads.
-template <int D> struct Lds {
-    static constexpr int BN = 64;
-    static constexpr int KS = D + 8;   // K rows: 16-byte reads of 32 different rows
-    static constexpr int VS = D + 32;  // V rows: transposing 8-byte reads of 8 rows
-    static constexpr int K_ELEMS = BN * KS;
-    static constexpr int V_ELEMS = BN * VS;
-    static constexpr int STAGE = K_ELEMS + V_ELEMS;
-    static constexpr int CHUNKS = BN * D / 8;             // 16-byte chunks per K (or V) tile
-    static constexpr int PER_THREAD = CHUNKS / kThreads;  // per thread, per matrix
+// K and V tiles live in LDS unpadded (rows of D elements) and are filled by
+// direct-to-LDS buffer loads: each wave instruction writes 1 KiB contiguously
+// (lane i -> bytes [16i, 16i+16)), so the LDS image is permuted at 16-byte
+// chunk granularity instead of padded: logical chunk c of row r is stored at
+// chunk c ^ swz(r).  swz makes the 16-row K operand reads and the 4-row
+// transposing V reads hit distinct banks, and turns every operand address
+// into (per-lane base) XOR (compile-time constant).
+template <int D> struct Tile {
+    static constexpr int BN = 64;                   // keys per K/V tile
+    static constexpr int RB = D * 2;                // bytes per LDS row
+    static constexpr int MAT = BN * RB;             // bytes per K (or V) tile
+    static constexpr int STAGE = 2 * MAT;           // K then V
+    static constexpr int DMA_PER_WAVE = MAT / (1024 * kWaves);  // 1 KiB wave loads per matrix
+    static_assert(MAT % (1024 * kWaves) == 0, "tile must split into 1 KiB wave loads");
+    // chunk permutation of row r (D = 128: 16 chunks per row; D = 64: 8)
+    __host__ __device__ static constexpr int swz(int r) {
+        if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+        const int g = (r >> 1) & 7;
+        return ((g & 1) << 2) | (g >> 1);
+    }
 };
+
+// Direct-to-LDS loads of one K and one V tile by one wave: load j of each
+// matrix writes the 1 KiB at base + j * kWaves KiB (lane i -> 16 bytes at
+// +16i) from byte offset voff[j] of the matrix's buffer resource.
+template <int MAT, int N>
+__device__ inline void dma_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                unsigned char* base, const int* voff) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (FA_LDS void*)(base + j * kWaves * 1024), 16,
+                                                 voff[j], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (FA_LDS void*)(base + MAT + j * kWaves * 1024),
+                                                 16, voff[j], 0, 0, 0);
+    }
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads, 2) void fa_fwd_mfma_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ out,
     float* __restrict__ lse, int B, int H, int S, float c, int causal, int wl, int wr, int n_qt) {
-    typedef Lds<D> L;
+    typedef Tile<D> L;
     constexpr int BN = L::BN;
+    constexpr int RB = L::RB;
     constexpr int KSTEPS = D / 16;  // 16-wide d chunks of the score MFMA
     constexpr int DB = D / 32;      // 32-wide d blocks of the output
-    static_assert(L::CHUNKS % kThreads == 0, "tile chunks must split evenly");
-    __shared__ __attribute__((aligned(16))) T lds[2 * L::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * L::STAGE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
     const int hh = lane >> 5;   // wave half
     const int ql = lane & 31;   // query row of this lane within the wave
 
@@ -163,160 +194,183 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_mfma_kernel(
     const int qw0 = q0 + wave * kWaveRows;  // first row of this wave
     const int qrow = qw0 + ql;              // this lane's query row
 
+    // ---- buffer resources over rows [r0, S) of this head: a row past S lies
+    // past num_records, so the hardware returns zeros for it
+    auto rows_rsrc = [&](const T* base, int64_t r0) {
+        const T* p = base + head_base + r0 * row_stride;
+        const int64_t bytes = ((S - r0 - 1) * row_stride + D) * (int64_t)sizeof(T);
+        const int64_t nrec = bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes;
+        return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)(uint32_t)nrec,
+                                                 kBufferFlags);
+    };
+
     // ---- Q fragment (B operand of S^T = K Q^T): row qrow, d = 16*ks + 8*hh .. +8
     u32x4 qf[KSTEPS];
     {
-        const bool ok = qrow < S;
-        const T* qp = q + head_base + (int64_t)(ok ? qrow : 0) * row_stride + 8 * hh;
+        const __amdgpu_buffer_rsrc_t rq = rows_rsrc(q, qw0 < S ? qw0 : S - 1);
+        const int voff = (ql * (int)row_stride + 8 * hh) * (int)sizeof(T);
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            u32x4 x = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
-            qf[ks] = ok ? x : u32x4{0, 0, 0, 0};
+        for (int ks = 0; ks < KSTEPS; ++ks)
+            qf[ks] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, voff + 32 * ks, 0, 0));
+        if (qw0 >= S) {
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = u32x4{0, 0, 0, 0};
         }
     }
 
-    // ---- K/V tile loader: 16-byte chunks, rows past S read as zero
-    auto load_tile = [&](int64_t kt, u32x4* kr, u32x4* vr) {
-        const int64_t k0 = kt * BN;
+    // ---- K/V tile loader: wave `wave`, load j writes LDS bytes
+    // [(j*kWaves + wave) * 1024 + 16*lane, +16) of the matrix; the source is
+    // the logical chunk stored there.
+    int dma_voff[L::DMA_PER_WAVE];
 #pragma unroll
-        for (int u = 0; u < L::PER_THREAD; ++u) {
-            const int id = u * kThreads + tid;
-            const int r = id / (D / 8), cc = id % (D / 8);
-            const int64_t key = k0 + r;
-            const bool ok = key < S;
-            const int64_t off = head_base + (ok ? key : 0) * row_stride + cc * 8;
-            u32x4 xk = *reinterpret_cast<const u32x4*>(k + off);
-            u32x4 xv = *reinterpret_cast<const u32x4*>(v + off);
-            kr[u] = ok ? xk : u32x4{0, 0, 0, 0};
-            vr[u] = ok ? xv : u32x4{0, 0, 0, 0};
-        }
-    };
-    auto store_tile = [&](int stage, const u32x4* kr, const u32x4* vr) {
-        T* ks = lds + stage * L::STAGE;
-        T* vs = ks + L::K_ELEMS;
-#pragma unroll
-        for (int u = 0; u < L::PER_THREAD; ++u) {
-            const int id = u * kThreads + tid;
-            const int r = id / (D / 8), cc = id % (D / 8);
-            *reinterpret_cast<u32x4*>(ks + r * L::KS + cc * 8) = kr[u];
-            *reinterpret_cast<u32x4*>(vs + r * L::VS + cc * 8) = vr[u];
-        }
+    for (int j = 0; j < L::DMA_PER_WAVE; ++j) {
+        const int byte = (j * kWaves + wave) * 1024 + 16 * lane;
+        const int r = byte / RB, pc = (byte % RB) / 16;
+        dma_voff[j] = r * (int)row_stride * (int)sizeof(T) + 16 * (pc ^ L::swz(r));
+    }
+    auto load_tile = [&](int64_t kt, int stage) {
+        dma_tile<L::MAT, L::DMA_PER_WAVE>(rows_rsrc(k, kt * BN), rows_rsrc(v, kt * BN),
+                                          lds + stage * L::STAGE + wave * 1024, dma_voff);
     };
 
+    // ---- per-lane LDS operand addresses (bytes within a stage)
+    // K: MFMA row m of the score block is key k_row_for_mfma_row(m); lane reads
+    // logical chunk 2*kk + hh of it: byte = kbase ^ (32*kk) (+ 32*RB per block)
+    const int krow = k_row_for_mfma_row(ql);
+    const int kbase = krow * RB + 16 * (hh ^ L::swz(krow));
+    // V (transposing reads): row 16*cch + 8*hh + 4*rd + jv, element column
+    // 32*d + tcol; byte = 16*cch*RB + (vbase[rd] ^ (64*d))
+    const int jv = (lane & 15) >> 2;
+    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    int vbase[2];
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+        const int r = 8 * hh + 4 * rd + jv;
+        vbase[rd] = L::MAT + r * RB + 16 * ((tcol / 8) ^ L::swz(r)) + 2 * (tcol % 8);
+    }
+
     // ---- running statistics (log2 domain: m is a max of c * s)
-    float m_run = kNegInf;  // running max
+    float m_run = kNegInf;  // running reference max
     float l_run = 0.f;      // running sum over this half's keys
     f32x16 o[DB];
 #pragma unroll
     for (int d = 0; d < DB; ++d) o[d] = f32x16{0};
 
-    u32x4 kr[L::PER_THREAD], vr[L::PER_THREAD];
-    if (kt0 < kt1) {
-        load_tile(kt0, kr, vr);
-        store_tile(0, kr, vr);
-    }
-    __syncthreads();
-
-    const int krow0 = k_row_for_mfma_row(ql);  // K row this lane feeds to the score MFMA
-    for (int64_t kt = kt0; kt < kt1; ++kt) {
-        const int stage = (int)((kt - kt0) & 1);
-        const bool has_next = kt + 1 < kt1;
-        if (has_next) load_tile(kt + 1, kr, vr);  // in flight during this tile's math
-
-        const int64_t k0 = kt * BN;
-        const bool skip = tile_fully_masked(ms, qw0, qw0 + kWaveRows - 1, k0, BN);
-        if (!skip) {
-            const T* ks = lds + stage * L::STAGE;
-            const T* vs = ks + L::K_ELEMS;
-            // S^T for two 32-key blocks
-            f32x16 s[2];
+    // One K/V tile of this wave's 32 rows.  MASK: some (row, key) pair of the
+    // tile is not allowed (diagonal / window edge / past S); interior tiles
+    // compile without any mask arithmetic.
+    auto tile_math = [&](int stage, int64_t k0, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        const unsigned char* st = lds + stage * L::STAGE;
+        // S^T for two 32-key blocks
+        f32x16 s[2];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                s[kb] = f32x16{0};
-                const T* kp = ks + (32 * kb + krow0) * L::KS + 8 * hh;
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = f32x16{0};
 #pragma unroll
-                for (int kk = 0; kk < KSTEPS; ++kk) {
-                    u32x4 a = *reinterpret_cast<const u32x4*>(kp + 16 * kk);
-                    s[kb] = Mfma<T>::mma(a, qf[kk], s[kb]);
-                }
+            for (int kk = 0; kk < KSTEPS; ++kk) {
+                u32x4 a = *reinterpret_cast<const u32x4*>(st + 32 * kb * RB + (kbase ^ (32 * kk)));
+                s[kb] = Mfma<T>::mma(a, qf[kk], s[kb]);
             }
-            // mask (boundary tiles only)
-            const bool need_mask = tile_needs_mask(ms, qw0, qw0 + kWaveRows - 1, k0, BN);
-            if (need_mask) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = (int)k0 + 32 * kb + score_key(i, hh);
-                        bool ok = key < S;
-                        if (causal) ok = ok && key <= qrow;
-                        if (wl >= 0) ok = ok && qrow - key <= wl;
-                        if (wr >= 0) ok = ok && key - qrow <= wr;
-                        s[kb][i] = ok ? s[kb][i] : kNegInf;
-                    }
-            }
-            // row max over the tile (in-lane, then across halves)
-            float mx = kNegInf;
+        }
+        if (MASK) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-            mx = halves_max(mx);
-            const float mt = (mx == kNegInf) ? kNegInf : mx * c;  // scaled; c may be 0
-            const float m_new = fmaxf(m_run, mt);
-            const float m_use = (m_new == kNegInf) ? 0.f : m_new;  // row fully masked so far
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            m_run = m_new;
-            // probabilities, row sum, pack to the input dtype for P V
-            u32x4 p[4];
-            float rs = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                float e[16];
-#pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, -m_use));
-                    if (need_mask) x = (s[kb][i] == kNegInf) ? 0.f : x;
-                    e[i] = x;
-                    rs += x;
+                    const int key = (int)k0 + 32 * kb + score_key(i, hh);
+                    bool ok = key < S;
+                    if (causal) ok = ok && key <= qrow;
+                    if (wl >= 0) ok = ok && qrow - key <= wl;
+                    if (wr >= 0) ok = ok && key - qrow <= wr;
+                    s[kb][i] = ok ? s[kb][i] : kNegInf;
                 }
+        }
+        // row max over the tile (in-lane, then across the two wave halves)
+        float mx = kNegInf;
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    u32x4 pk;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int t = 0; t < 4; ++t)
-                        pk[t] = Mfma<T>::pack2(e[8 * half + 2 * t], e[8 * half + 2 * t + 1]);
-                    p[2 * kb + half] = pk;
-                }
+            for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+        mx = halves_max(mx);
+        const float mt = (mx == kNegInf) ? kNegInf : mx * c;  // scaled; c may be 0
+        // The reference max only moves when the tile's max exceeds it by more
+        // than kRescaleSlack: weights stay <= 2^kRescaleSlack and the O / l
+        // rescale is rare.  O, l and LSE all use the same reference, so the
+        // result is unchanged up to rounding.
+        const float m_new = (mt > m_run + kRescaleSlack) ? mt : m_run;
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;  // row fully masked so far
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        const bool moved = m_new != m_run;
+        m_run = m_new;
+        // probabilities, row sum, pack to the input dtype for P V
+        u32x4 p[4];
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            float e[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, -m_use));
+                if (MASK) x = (s[kb][i] == kNegInf) ? 0.f : x;  // c == 0 would give NaN
+                e[i] = x;
+                rs += x;
             }
-            l_run = alpha * l_run + rs;
-            if (__any(alpha != 1.f)) {  // skip the rescale when no row max moved
 #pragma unroll
-                for (int d = 0; d < DB; ++d) o[d] *= alpha;
-            }
-            // O^T += V^T P^T: V^T via transposing LDS reads of the row-major V tile
-            const int tr_row = 8 * hh + ((lane & 15) >> 2);
-            const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+            for (int half = 0; half < 2; ++half) {
+                u32x4 pk;
 #pragma unroll
-            for (int d = 0; d < DB; ++d) {
-#pragma unroll
-                for (int cch = 0; cch < 4; ++cch) {
-                    const T* vp = vs + (16 * cch + tr_row) * L::VS + 32 * d + tr_col;
-                    i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(vp));
-                    i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(vp + 4 * L::VS));
-                    u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-                    u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
-                    o[d] = Mfma<T>::mma(a, p[cch], o[d]);
-                }
+                for (int t = 0; t < 4; ++t)
+                    pk[t] = Mfma<T>::pack2(e[8 * half + 2 * t], e[8 * half + 2 * t + 1]);
+                p[2 * kb + half] = pk;
             }
         }
-        if (has_next) store_tile(stage ^ 1, kr, vr);
+        if (__any(moved)) {  // wave-uniform: rescale only when some row's reference moved
+            l_run *= alpha;
+#pragma unroll
+            for (int d = 0; d < DB; ++d) o[d] *= alpha;
+        }
+        l_run += rs;
+        // O^T += V^T P^T: V^T via transposing LDS reads of the row-major V tile
+#pragma unroll
+        for (int d = 0; d < DB; ++d) {
+#pragma unroll
+            for (int cch = 0; cch < 4; ++cch) {
+                const unsigned char* vp = st + 16 * cch * RB;
+                i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (FA_LDS i16x4*)(vp + (vbase[0] ^ (64 * d))));
+                i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (FA_LDS i16x4*)(vp + (vbase[1] ^ (64 * d))));
+                u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
+                o[d] = Mfma<T>::mma(a, p[cch], o[d]);
+            }
+        }
+    };
+
+    if (kt0 < kt1) load_tile(kt0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    for (int64_t kt = kt0; kt < kt1; ++kt) {
+        const int stage = (int)((kt - kt0) & 1);
+        if (kt + 1 < kt1) load_tile(kt + 1, stage ^ 1);  // lands during this tile's math
+        const int64_t k0 = kt * BN;
+        if (!tile_fully_masked(ms, qw0, qw0 + kWaveRows - 1, k0, BN)) {
+            if (tile_needs_mask(ms, qw0, qw0 + kWaveRows - 1, k0, BN))
+                tile_math(stage, k0, BoolTag<true>{});
+            else
+                tile_math(stage, k0, BoolTag<false>{});
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // next tile is in LDS
         __syncthreads();
     }
 
     // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
+    // l == 0 only for a row with no allowed key; a NaN l (NaN scores) propagates
     const float l_tot = halves_sum(l_run);
-    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
     if (qrow < S) {
         T* op = out + head_base + (int64_t)qrow * row_stride + 4 * hh;
 #pragma unroll
@@ -329,7 +383,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_mfma_kernel(
             }
         if (hh == 0) {
             const float m_fin = (m_run == kNegInf) ? 0.f : m_run;
-            const float lse_v = (l_tot > 0.f) ? 0.69314718055994531f * (m_fin + __log2f(l_tot)) : kNegInf;
+            const float lse_v =
+                (l_tot == 0.f) ? kNegInf : 0.69314718055994531f * (m_fin + __log2f(l_tot));
             lse[((int64_t)bb * H + h) * S + qrow] = lse_v;
         }
     }
@@ -408,9 +463,12 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp32_kernel(
 #pragma unroll
         for (int kk = 0; kk < D / 2; ++kk)
             s = __builtin_amdgcn_mfma_f32_32x32x2f32(ks[ql * L::KS + 2 * kk + hh], qf[kk], s, 0, 0, 0);
-        // register i holds key 8*(i/4) + 4*hh + (i%4)
-        const bool need_mask = tile_needs_mask(ms, qw0, qw0 + kWaveRows - 1, k0, BN);
-        if (need_mask) {
+        // scaled scores t = c * s (log2 domain); masked keys -> -inf.  Scaling
+        // before the max makes the max element's weight exp2(0) = 1 exactly.
+        // Register i holds key 8*(i/4) + 4*hh + (i%4).
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[i] *= c;
+        if (tile_needs_mask(ms, qw0, qw0 + kWaveRows - 1, k0, BN)) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int key = (int)k0 + 8 * (i >> 2) + 4 * hh + (i & 3);
@@ -424,19 +482,15 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp32_kernel(
         float mx = kNegInf;
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[i]);
-        mx = halves_max(mx);
-        const float mt = (mx == kNegInf) ? kNegInf : mx * c;
-        const float m_new = fmaxf(m_run, mt);
+        const float m_new = fmaxf(m_run, halves_max(mx));
         const float m_use = (m_new == kNegInf) ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
         m_run = m_new;
         float p[16], rs = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -m_use));
-            if (need_mask) x = (s[i] == kNegInf) ? 0.f : x;
-            p[i] = x;
-            rs += x;
+            p[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
+            rs += p[i];
         }
         l_run = alpha * l_run + rs;
 #pragma unroll
@@ -451,8 +505,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp32_kernel(
                                                             0, 0, 0);
             }
     }
+    // l == 0 only for a row with no allowed key; a NaN l (NaN scores) propagates
     const float l_tot = halves_sum(l_run);
-    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+    const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
     if (qrow < S) {
         float* op = out + head_base + (int64_t)qrow * row_stride + 4 * hh;
 #pragma unroll
@@ -465,7 +520,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp32_kernel(
             }
         if (hh == 0) {
             const float m_fin = (m_run == kNegInf) ? 0.f : m_run;
-            const float lse_v = (l_tot > 0.f) ? 0.69314718055994531f * (m_fin + __log2f(l_tot)) : kNegInf;
+            const float lse_v = (l_tot == 0.f) ? kNegInf : 0.69314718055994531f * (m_fin + __log2f(l_tot));
             lse[((int64_t)bb * H + h) * S + qrow] = lse_v;
         }
     }
@@ -501,6 +556,6 @@ hipError_t launch_fwd(const LaunchArgs& a) {
 }
 
 int64_t q_tile_rows() { return kBM; }
-int64_t kv_tile_keys(int dtype) { return dtype == kDtypeFp32 ? Lds32<64>::BN : Lds<64>::BN; }
+int64_t kv_tile_keys(int dtype) { return dtype == kDtypeFp32 ? Lds32<64>::BN : Tile<64>::BN; }
 
 }  // namespace fa
