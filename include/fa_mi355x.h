@@ -43,7 +43,8 @@ typedef enum {
 typedef enum {
     FA_OK = 0,
     FA_ERR_NULL = -1,     /* a required pointer is NULL */
-    FA_ERR_SHAPE = -2,    /* B, H or S < 1, or a size overflows int64 / the index range */
+    FA_ERR_SHAPE = -2,    /* B, H or S < 1, a size overflows int64 / the index range, or
+                             64 rows of one tensor (64*H*D elements) exceed 2^31 - 1 bytes */
     FA_ERR_HEAD_DIM = -3, /* D not supported (supported: 64, 128) */
     FA_ERR_WINDOW = -4,   /* window_left or window_right < -1, or causal not 0/1 */
     FA_ERR_DTYPE = -5,    /* dtype not one of fa_dtype_t */

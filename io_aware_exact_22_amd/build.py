@@ -25,6 +25,9 @@ HIPCC_FLAGS = [
     "-Wall",
     # keep the compiler from forming packed-fp32 VALU ops (v_pk_*_f32)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the score tile feeds VALU code directly, with no
+    # v_accvgpr_read copies
+    "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form",
 ]
 
 

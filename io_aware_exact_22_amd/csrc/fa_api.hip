@@ -3,6 +3,7 @@
 // the dispatch to the gfx950 kernels.  No allocation, no global state.
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <cmath>
 #include <cstdint>
 
@@ -36,7 +37,8 @@ int check_problem(int64_t B, int64_t H, int64_t S, int64_t D, int causal, int64_
     // the kernels index rows with 32-bit S, B, H and launch B*H*ceil(S/128)
     // workgroups of 256 threads (grid limit: 2^32 - 1 work-items)
     if (S > INT32_MAX || B > INT32_MAX || H > INT32_MAX) return FA_ERR_SHAPE;
-    const int64_t n_qt = (S + fa::q_tile_rows() - 1) / fa::q_tile_rows();
+    const int64_t bm = fa::q_tile_rows(dtype, D);
+    const int64_t n_qt = (S + bm - 1) / bm;
     int64_t n_wg, t;
     if (!mul_ok(B, H, &t) || !mul_ok(t, n_qt, &n_wg) || n_wg > (int64_t)(UINT32_MAX / 256))
         return FA_ERR_SHAPE;
@@ -45,6 +47,9 @@ int check_problem(int64_t B, int64_t H, int64_t S, int64_t D, int causal, int64_
         !mul_ok(elems, elem_size(dtype), tensor_bytes))
         return FA_ERR_SHAPE;
     if (!mul_ok(rows, H, &t) || !mul_ok(t, 4, lse_bytes)) return FA_ERR_SHAPE;
+    // the kernels address the rows of one 64-row K/V tile with 32-bit byte
+    // offsets (row stride H * D elements)
+    if (H * D * elem_size(dtype) * 64 > (int64_t)INT32_MAX) return FA_ERR_SHAPE;
     return FA_OK;
 }
 
@@ -102,8 +107,13 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* out, float*
     a.H = H;
     a.S = S;
     a.D = D;
-    // exp(scale * s) = exp2(scale * log2(e) * s): one FMA feeds v_exp_f32
-    a.c = (float)((double)scale * 1.4426950408889634);
+    // exp(scale * s) = exp2(scale * log2(e) * s): one FMA feeds v_exp_f32.
+    // c is kept >= FLT_MIN so that a masked score -inf scales to -inf (weight
+    // exactly 0) even for scale = 0; a finite score s then scales to at most
+    // |s| * 1.2e-38, whose weight exp2(.) rounds to exactly 1 -- the uniform
+    // weights scale = 0 asks for.
+    const float c = (float)((double)scale * 1.4426950408889634);
+    a.c = c < FLT_MIN ? FLT_MIN : c;
     a.causal = causal;
     a.wl = window_left >= S ? -1 : window_left;  // a window reaching past S is unbounded
     a.wr = window_right >= S ? -1 : window_right;
@@ -122,7 +132,7 @@ FA_API int fa_fwd_tile_schedule(int64_t S, int64_t D, int dtype, int causal, int
     const int rc = check_problem(1, 1, S, D, causal, window_left, window_right, dtype, &nbytes,
                                  &lbytes);
     if (rc != FA_OK) return rc;
-    const int64_t BM = fa::q_tile_rows(), BN = fa::kv_tile_keys(dtype);
+    const int64_t BM = fa::q_tile_rows(dtype, D), BN = fa::kv_tile_keys(dtype);
     const int64_t nq = (S + BM - 1) / BM;
     if (q_tile < 0 || q_tile >= nq) return FA_ERR_SHAPE;
     const fa::MaskSpec m{S, causal, window_left >= S ? -1 : window_left,
@@ -137,8 +147,14 @@ FA_API int fa_fwd_tile_schedule(int64_t S, int64_t D, int dtype, int causal, int
     if (needs_mask) {
         if (max_tiles < t1 - t0) return FA_ERR_SHAPE;
         const int64_t r0 = q_tile * BM;
-        for (int64_t t = t0; t < t1; ++t)
-            needs_mask[t - t0] = fa::tile_needs_mask(m, r0, r0 + BM - 1, t * BN, BN) ? 1 : 0;
+        if (dtype == FA_DTYPE_FP32) {  // the fp32 kernel decides per tile
+            for (int64_t t = t0; t < t1; ++t)
+                needs_mask[t - t0] = fa::tile_needs_mask(m, r0, r0 + BM - 1, t * BN, BN) ? 1 : 0;
+        } else {  // the bf16/fp16 kernel runs [ki0, ki1) without the mask
+            int64_t i0, i1;
+            fa::q_tile_interior_range(m, r0, BM, BN, t0, t1, &i0, &i1);
+            for (int64_t t = t0; t < t1; ++t) needs_mask[t - t0] = (t < i0 || t >= i1) ? 1 : 0;
+        }
     }
     return FA_OK;
 }

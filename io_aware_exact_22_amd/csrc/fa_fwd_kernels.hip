@@ -18,26 +18,34 @@
 // the scale ([CG] 内存优化编译选项, CK_TILE_FMHA_FWD_FAST_EXP2).
 //
 // gfx950 design (what differs from the pages' CUDA/Tensor Core design):
-//  * A workgroup is 4 wave64s and owns a 128-row Q tile; each wave owns 32
-//    query rows.  K/V tiles of 64 keys stream through double-buffered LDS.
+//  * A workgroup is NW wave64s and owns a 32*NW-row Q tile; each wave owns 32
+//    query rows.  K/V tiles of 64 keys stream through LDS: K double-buffered
+//    two tiles ahead, V double-buffered one tile ahead, one barrier per tile.
 //  * The scores are computed transposed, S^T = K Q^T, on the 32x32x16
-//    bf16/f16 MFMA: in the MFMA result layout every lane then holds one query
-//    row (lane % 32) and 16 of the tile's keys per 32-key block, so the row
-//    max / row sum are in-lane reductions plus one exchange between the two
-//    wave halves (v_permlane32_swap) instead of a 32-lane shuffle tree.
+//    bf16/f16 MFMA: in the MFMA result layout every lane holds one query row
+//    (lane % 32) and 16 of the tile's keys per 32-key block, so the row max /
+//    row sum are in-lane reductions plus one exchange between the two wave
+//    halves (v_permlane32_swap) instead of a 32-lane shuffle tree.
 //  * The output is accumulated transposed too, O^T += V^T P^T: P^T is the
 //    B operand straight from the score registers (the K rows of the score MFMA
 //    are permuted so each lane's keys come out as 8 consecutive keys per
 //    16-key chunk), and V^T is read from the row-major V tile in LDS with the
 //    gfx950 transposing LDS read ds_read_b64_tr_b16.  The per-row rescale
 //    factor then multiplies whole lanes -- no cross-lane traffic at all.
-//  * Whole K/V tiles outside the causal / window mask are not visited; tiles
-//    inside it for every row skip the mask; a wave skips the arithmetic of a
-//    tile that is fully masked for its 32 rows.
+//  * Software pipeline within each wave: the score MFMAs of tile j+1 run
+//    while the VALU computes exp / pack / row sum of tile j, and the P V MFMAs
+//    of tile j run while the VALU takes the row max of tile j+1.  The
+//    interleave is fixed with scheduling-group barriers so the matrix cores
+//    and the vector ALU work at the same time.
+//  * Whole K/V tiles outside the causal / window mask are not visited; the
+//    tiles inside it for every row of the workgroup run a loop body that has
+//    no mask code at all; the few boundary tiles apply the mask.
 //  * Workgroup ids are remapped so each XCD holds whole (batch, head) groups
 //    (L2 reuse of K/V), and causal Q tiles run heaviest first.
 //  * Probabilities are rounded to the input dtype (RNE, v_cvt_pk_*) for the
-//    P V MFMA; max, sum, exp and the accumulators stay fp32.
+//    P V MFMA.  The row sum adds the fp32 weights for bf16 and the fp16-rounded
+//    weights two at a time (v_dot2c with ones) for fp16.  Max, exp and the
+//    accumulators stay fp32.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,7 +55,9 @@
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(16)));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(4)));
 typedef _Float16 f16x8 __attribute__((__vector_size__(16)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((__vector_size__(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -56,10 +66,7 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 #define FA_LDS __attribute__((address_space(3)))
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kWaveRows = 32;             // query rows per wave
-constexpr int kBM = kWaves * kWaveRows;   // query rows per workgroup
+constexpr int kWaveRows = 32;  // query rows per wave
 constexpr float kNegInf = -__builtin_inff();
 // word 3 of a raw (stride 0) buffer resource on gfx9-family GPUs
 constexpr int kBufferFlags = 0x00020000;
@@ -67,36 +74,49 @@ constexpr int kBufferFlags = 0x00020000;
 constexpr float kRescaleSlack = 8.f;
 
 template <bool B> struct BoolTag { static constexpr bool value = B; };
+template <int N> struct IntTag { static constexpr int value = N; };
+
+// scheduling-group masks of __builtin_amdgcn_sched_group_barrier
+constexpr int kSgMfma = 0x008;
+constexpr int kSgValu = 0x002 | 0x400;  // VALU including transcendental
+constexpr int kSgDsRead = 0x100;
 
 // ---------------------------------------------------------------- dtype traits
 template <typename T> struct Mfma;
 template <> struct Mfma<__bf16> {
-    typedef bf16x8 vec8;
     __device__ static inline f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
     }
     // two fp32 -> two RNE-rounded bf16 packed in one dword (v_cvt_pk_bf16_f32)
     __device__ static inline unsigned pack2(float x, float y) {
-        typedef __bf16 bf16x2 __attribute__((__vector_size__(4)));
         bf16x2 r;
         r[0] = (__bf16)x;
         r[1] = (__bf16)y;
         return __builtin_bit_cast(unsigned, r);
     }
+    // The row sum adds the fp32 weights: a sum of bf16-rounded weights is off
+    // by up to 2^-8 relative on rows with few keys, which would reach LSE.
+    static constexpr bool kSumRounded = false;
+    __device__ static inline float sum2(unsigned, float acc) { return acc; }
 };
 template <> struct Mfma<_Float16> {
-    typedef f16x8 vec8;
     __device__ static inline f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
     }
     __device__ static inline unsigned pack2(float x, float y) {
-        typedef _Float16 f16x2 __attribute__((__vector_size__(4)));
         f16x2 r;
         r[0] = (_Float16)x;
         r[1] = (_Float16)y;
         return __builtin_bit_cast(unsigned, r);
+    }
+    // The row sum adds the fp16-rounded weights (relative error <= 2^-11,
+    // i.e. <= 4.9e-4 in LSE) two at a time: v_dot2c_f32_f16 with ones.
+    static constexpr bool kSumRounded = true;
+    __device__ static inline float sum2(unsigned x, float acc) {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, x),
+                                      __builtin_bit_cast(f16x2, 0x3c003c00u), acc, false);
     }
 };
 
@@ -114,8 +134,8 @@ __device__ inline float halves_sum(float x) {
 // Key offset (within a 32-key block) of score register i in wave half hh:
 // the K row fed to MFMA row m = 8*(m/8) + 4*hh' + (m%4) is chosen so that
 // register i of half hh holds key 16*(i/8) + 8*hh + (i%8).
-__device__ inline int score_key(int i, int hh) { return 16 * (i >> 3) + 8 * hh + (i & 7); }
-// K row fed to MFMA row m (the inverse view of score_key).
+__host__ __device__ constexpr int score_key_base(int i) { return 16 * (i >> 3) + (i & 7); }
+// K row fed to MFMA row m (the inverse view of the key map above).
 __device__ inline int k_row_for_mfma_row(int m) {
     const int g = m >> 3, hh = (m >> 2) & 1, r = m & 3;
     return 16 * (g >> 1) + 8 * hh + 4 * (g & 1) + r;
@@ -129,13 +149,19 @@ __device__ inline int k_row_for_mfma_row(int m) {
 // chunk c ^ swz(r).  swz makes the 16-row K operand reads and the 4-row
 // transposing V reads hit distinct banks, and turns every operand address
 // into (per-lane base) XOR (compile-time constant).
-template <int D> struct Tile {
+//
+// LDS map: [K stage 0][K stage 1][V stage 0][V stage 1], one 64-key tile each.
+template <int D, int NW> struct Tile {
     static constexpr int BN = 64;                   // keys per K/V tile
+    static constexpr int BM = NW * kWaveRows;       // query rows per workgroup
     static constexpr int RB = D * 2;                // bytes per LDS row
     static constexpr int MAT = BN * RB;             // bytes per K (or V) tile
-    static constexpr int STAGE = 2 * MAT;           // K then V
-    static constexpr int DMA_PER_WAVE = MAT / (1024 * kWaves);  // 1 KiB wave loads per matrix
-    static_assert(MAT % (1024 * kWaves) == 0, "tile must split into 1 KiB wave loads");
+    static constexpr int LDS_BYTES = 4 * MAT;
+    static constexpr int DMA_PER_WAVE = MAT / (1024 * NW);  // 1 KiB wave loads per matrix
+    static_assert(MAT % (1024 * NW) == 0, "tile must split into 1 KiB wave loads");
+    static_assert(LDS_BYTES <= 65536, "LDS operand offsets must fit the 16-bit ds offset");
+    __host__ __device__ static constexpr int koff(int stage) { return stage * MAT; }
+    __host__ __device__ static constexpr int voff(int stage) { return 2 * MAT + stage * MAT; }
     // chunk permutation of row r (D = 128: 16 chunks per row; D = 64: 8)
     __host__ __device__ static constexpr int swz(int r) {
         if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
@@ -144,31 +170,29 @@ template <int D> struct Tile {
     }
 };
 
-// Direct-to-LDS loads of one K and one V tile by one wave: load j of each
-// matrix writes the 1 KiB at base + j * kWaves KiB (lane i -> 16 bytes at
-// +16i) from byte offset voff[j] of the matrix's buffer resource.
-template <int MAT, int N>
-__device__ inline void dma_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                unsigned char* base, const int* voff) {
+// Direct-to-LDS loads of one K or V tile by one wave: load j writes the 1 KiB
+// at wave_base + j * NW KiB (lane i -> 16 bytes at +16i) from byte offset
+// voff[j] of the tile's buffer resource.
+template <int N, int NW>
+__device__ inline void dma_matrix(__amdgpu_buffer_rsrc_t r, unsigned char* wave_base,
+                                  const int* voff) {
 #pragma unroll
-    for (int j = 0; j < N; ++j) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (FA_LDS void*)(base + j * kWaves * 1024), 16,
+    for (int j = 0; j < N; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)(wave_base + j * NW * 1024), 16,
                                                  voff[j], 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (FA_LDS void*)(base + MAT + j * kWaves * 1024),
-                                                 16, voff[j], 0, 0, 0);
-    }
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads, 2) void fa_fwd_mfma_kernel(
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ out,
     float* __restrict__ lse, int B, int H, int S, float c, int causal, int wl, int wr, int n_qt) {
-    typedef Tile<D> L;
+    typedef Tile<D, NW> L;
     constexpr int BN = L::BN;
+    constexpr int BM = L::BM;
     constexpr int RB = L::RB;
     constexpr int KSTEPS = D / 16;  // 16-wide d chunks of the score MFMA
     constexpr int DB = D / 32;      // 32-wide d blocks of the output
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * L::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[L::LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -184,19 +208,40 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_mfma_kernel(
     if (causal) qt = n_qt - 1 - qt;  // heaviest Q tiles first
     const int bb = (int)(bh / H), h = (int)(bh % H);
 
+    // ---- K/V tiles of this Q tile: [kt0, kt1); mask-free ones: [ki0, ki1)
     const MaskSpec ms{S, causal, wl, wr};
-    int64_t kt0, kt1;
-    q_tile_kv_range(ms, qt, kBM, BN, &kt0, &kt1);
+    int kt0, kt1, ki0, ki1;
+    {
+        int64_t a0, a1, b0, b1;
+        q_tile_kv_range(ms, qt, BM, BN, &a0, &a1);
+        q_tile_interior_range(ms, (int64_t)qt * BM, BM, BN, a0, a1, &b0, &b1);
+        kt0 = (int)a0;
+        kt1 = (int)a1;
+        ki0 = (int)b0;
+        ki1 = (int)b1;
+    }
 
     const int64_t row_stride = (int64_t)H * D;                      // elements between rows
     const int64_t head_base = ((int64_t)bb * S * H + h) * D;        // element (b, 0, h, 0)
-    const int q0 = qt * kBM;
+    const int q0 = qt * BM;
     const int qw0 = q0 + wave * kWaveRows;  // first row of this wave
     const int qrow = qw0 + ql;              // this lane's query row
 
+    // allowed keys of this lane's row: [key_lo, key_lo + key_w] (rows past S
+    // are padding: any finite range will do, their results are not stored)
+    int key_lo = 0, key_w = S - 1;
+    if (qrow < S) {
+        int64_t lo = 0, hi = S - 1;
+        if (wl >= 0) lo = (int64_t)qrow - wl > 0 ? (int64_t)qrow - wl : 0;
+        if (causal && qrow < hi) hi = qrow;
+        if (wr >= 0 && (int64_t)qrow + wr < hi) hi = (int64_t)qrow + wr;
+        key_lo = (int)lo;
+        key_w = (int)(hi - lo);
+    }
+
     // ---- buffer resources over rows [r0, S) of this head: a row past S lies
     // past num_records, so the hardware returns zeros for it
-    auto rows_rsrc = [&](const T* base, int64_t r0) {
+    auto rows_rsrc = [&](const T* base, int64_t r0) __attribute__((always_inline)) {
         const T* p = base + head_base + r0 * row_stride;
         const int64_t bytes = ((S - r0 - 1) * row_stride + D) * (int64_t)sizeof(T);
         const int64_t nrec = bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes;
@@ -220,152 +265,249 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_mfma_kernel(
     }
 
     // ---- K/V tile loader: wave `wave`, load j writes LDS bytes
-    // [(j*kWaves + wave) * 1024 + 16*lane, +16) of the matrix; the source is
-    // the logical chunk stored there.
+    // [(j*NW + wave) * 1024 + 16*lane, +16) of the tile; the source is the
+    // logical chunk stored there.
     int dma_voff[L::DMA_PER_WAVE];
 #pragma unroll
     for (int j = 0; j < L::DMA_PER_WAVE; ++j) {
-        const int byte = (j * kWaves + wave) * 1024 + 16 * lane;
+        const int byte = (j * NW + wave) * 1024 + 16 * lane;
         const int r = byte / RB, pc = (byte % RB) / 16;
         dma_voff[j] = r * (int)row_stride * (int)sizeof(T) + 16 * (pc ^ L::swz(r));
     }
-    auto load_tile = [&](int64_t kt, int stage) {
-        dma_tile<L::MAT, L::DMA_PER_WAVE>(rows_rsrc(k, kt * BN), rows_rsrc(v, kt * BN),
-                                          lds + stage * L::STAGE + wave * 1024, dma_voff);
+    unsigned char* const wave_lds = lds + wave * 1024;
+    auto load_k = [&](int kt, int stage) __attribute__((always_inline)) {
+        dma_matrix<L::DMA_PER_WAVE, NW>(rows_rsrc(k, (int64_t)kt * BN), wave_lds + L::koff(stage),
+                                        dma_voff);
+    };
+    auto load_v = [&](int kt, int stage) __attribute__((always_inline)) {
+        dma_matrix<L::DMA_PER_WAVE, NW>(rows_rsrc(v, (int64_t)kt * BN), wave_lds + L::voff(stage),
+                                        dma_voff);
     };
 
-    // ---- per-lane LDS operand addresses (bytes within a stage)
+    // ---- per-lane LDS operand addresses (bytes within a tile)
     // K: MFMA row m of the score block is key k_row_for_mfma_row(m); lane reads
-    // logical chunk 2*kk + hh of it: byte = kbase ^ (32*kk) (+ 32*RB per block)
-    const int krow = k_row_for_mfma_row(ql);
-    const int kbase = krow * RB + 16 * (hh ^ L::swz(krow));
-    // V (transposing reads): row 16*cch + 8*hh + 4*rd + jv, element column
-    // 32*d + tcol; byte = 16*cch*RB + (vbase[rd] ^ (64*d))
-    const int jv = (lane & 15) >> 2;
-    const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-    int vbase[2];
+    // logical chunk 2*kk + hh of it: byte = kaddr[kk] (+ 32*RB per 32-key block)
+    int kaddr[KSTEPS];
+    {
+        const int krow = k_row_for_mfma_row(ql);
+        const int kbase = krow * RB + 16 * (hh ^ L::swz(krow));
 #pragma unroll
-    for (int rd = 0; rd < 2; ++rd) {
-        const int r = 8 * hh + 4 * rd + jv;
-        vbase[rd] = L::MAT + r * RB + 16 * ((tcol / 8) ^ L::swz(r)) + 2 * (tcol % 8);
+        for (int kk = 0; kk < KSTEPS; ++kk) kaddr[kk] = kbase ^ (32 * kk);
+    }
+    // V (transposing reads): row 16*cch + 8*hh + 4*rd + jv, element column
+    // 32*d + tcol; byte = 16*cch*RB + vaddr[rd][d]
+    int vaddr[2][DB];
+    {
+        const int jv = (lane & 15) >> 2;
+        const int tcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd) {
+            const int r = 8 * hh + 4 * rd + jv;
+            const int vb = r * RB + 16 * ((tcol / 8) ^ L::swz(r)) + 2 * (tcol % 8);
+#pragma unroll
+            for (int d = 0; d < DB; ++d) vaddr[rd][d] = vb ^ (64 * d);
+        }
     }
 
-    // ---- running statistics (log2 domain: m is a max of c * s)
+    // ---- running statistics (log2 domain: m is a max of c * s).  c >= FLT_MIN
+    // (the host clamps it), so a masked score -inf stays -inf after scaling
+    // and its weight exp2(-inf) is exactly 0.
     float m_run = kNegInf;  // running reference max
+    float m_use = 0.f;      // reference the current tile's weights use
+    float alpha = 1.f;      // factor O and l take before the current tile
+    bool moved = false;     // the reference moved for the current tile
     float l_run = 0.f;      // running sum over this half's keys
     f32x16 o[DB];
 #pragma unroll
     for (int d = 0; d < DB; ++d) o[d] = f32x16{0};
 
-    // One K/V tile of this wave's 32 rows.  MASK: some (row, key) pair of the
-    // tile is not allowed (diagonal / window edge / past S); interior tiles
-    // compile without any mask arithmetic.
-    auto tile_math = [&](int stage, int64_t k0, auto mask_tag) {
-        constexpr bool MASK = decltype(mask_tag)::value;
-        const unsigned char* st = lds + stage * L::STAGE;
-        // S^T for two 32-key blocks
-        f32x16 s[2];
+    // S^T of one tile for this wave's 32 rows (two 32-key blocks)
+    auto qk = [&](f32x16(&s)[2], int kst) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = f32x16{0};
+        for (int kk = 0; kk < KSTEPS; ++kk)
 #pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk) {
-                u32x4 a = *reinterpret_cast<const u32x4*>(st + 32 * kb * RB + (kbase ^ (32 * kk)));
-                s[kb] = Mfma<T>::mma(a, qf[kk], s[kb]);
+            for (int kb = 0; kb < 2; ++kb) {
+                const u32x4 a =
+                    *reinterpret_cast<const u32x4*>(lds + kst + 32 * kb * RB + kaddr[kk]);
+                s[kb] = Mfma<T>::mma(a, qf[kk], kk == 0 ? f32x16{0} : s[kb]);
             }
-        }
-        if (MASK) {
+    };
+    // keys outside this lane's allowed range -> -inf
+    auto apply_mask = [&](f32x16(&s)[2], int k0) __attribute__((always_inline)) {
+        const int a = k0 + 8 * hh - key_lo;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = (int)k0 + 32 * kb + score_key(i, hh);
-                    bool ok = key < S;
-                    if (causal) ok = ok && key <= qrow;
-                    if (wl >= 0) ok = ok && qrow - key <= wl;
-                    if (wr >= 0) ok = ok && key - qrow <= wr;
-                    s[kb][i] = ok ? s[kb][i] : kNegInf;
-                }
-        }
-        // row max over the tile (in-lane, then across the two wave halves)
+            for (int i = 0; i < 16; ++i) {
+                const bool ok = (unsigned)(a + 32 * kb + score_key_base(i)) <= (unsigned)key_w;
+                s[kb][i] = ok ? s[kb][i] : kNegInf;
+            }
+    };
+    // row max of a tile -> next reference.  The reference only moves when the
+    // tile's max exceeds it by more than kRescaleSlack: weights stay below
+    // 2^kRescaleSlack and the O / l rescale is rare.  O, l and LSE all use the
+    // same reference, so the result is unchanged up to rounding.
+    auto update_max = [&](const f32x16(&s)[2]) __attribute__((always_inline)) {
         float mx = kNegInf;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-        mx = halves_max(mx);
-        const float mt = (mx == kNegInf) ? kNegInf : mx * c;  // scaled; c may be 0
-        // The reference max only moves when the tile's max exceeds it by more
-        // than kRescaleSlack: weights stay <= 2^kRescaleSlack and the O / l
-        // rescale is rare.  O, l and LSE all use the same reference, so the
-        // result is unchanged up to rounding.
+        const float mt = halves_max(mx) * c;
         const float m_new = (mt > m_run + kRescaleSlack) ? mt : m_run;
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;  // row fully masked so far
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        const bool moved = m_new != m_run;
+        m_use = (m_new == kNegInf) ? 0.f : m_new;  // row fully masked so far
+        alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        moved = m_new != m_run;
         m_run = m_new;
-        // probabilities, row sum, pack to the input dtype for P V
-        u32x4 p[4];
-        float rs = 0.f;
+    };
+    // weights of a tile, rounded and packed as the B operand of O^T += V^T P^T;
+    // the row sum adds the rounded weights
+    auto softmax = [&](const f32x16(&s)[2], u32x4(&p)[4]) __attribute__((always_inline)) {
+        float la = 0.f, lb = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            float e[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float x = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, -m_use));
-                if (MASK) x = (s[kb][i] == kNegInf) ? 0.f : x;  // c == 0 would give NaN
-                e[i] = x;
-                rs += x;
-            }
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 u32x4 pk;
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    pk[t] = Mfma<T>::pack2(e[8 * half + 2 * t], e[8 * half + 2 * t + 1]);
+                for (int t = 0; t < 4; ++t) {
+                    const int i = 8 * half + 2 * t;
+                    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, -m_use));
+                    const float e1 =
+                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i + 1], c, -m_use));
+                    pk[t] = Mfma<T>::pack2(e0, e1);
+                    if (!Mfma<T>::kSumRounded) {
+                        la += e0;
+                        lb += e1;
+                    }
+                }
                 p[2 * kb + half] = pk;
+                if (Mfma<T>::kSumRounded) {
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        if (t & 1)
+                            lb = Mfma<T>::sum2(pk[t], lb);
+                        else
+                            la = Mfma<T>::sum2(pk[t], la);
+                    }
+                }
             }
-        }
-        if (__any(moved)) {  // wave-uniform: rescale only when some row's reference moved
+        l_run += la + lb;
+    };
+    // O^T += V^T P^T with V^T from transposing LDS reads of the row-major tile
+    auto pv = [&](const u32x4(&p)[4], int vst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int cch = 0; cch < 4; ++cch)
+#pragma unroll
+            for (int d = 0; d < DB; ++d) {
+                const unsigned char* vp = lds + vst + 16 * cch * RB;
+                const i16x4 lo =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(vp + vaddr[0][d]));
+                const i16x4 hi =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(vp + vaddr[1][d]));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                const u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
+                o[d] = Mfma<T>::mma(a, p[cch], o[d]);
+            }
+    };
+    auto rescale_if_moved = [&]() __attribute__((always_inline)) {
+        if (__any(moved)) {  // wave-uniform: only when some row's reference moved
             l_run *= alpha;
 #pragma unroll
             for (int d = 0; d < DB; ++d) o[d] *= alpha;
         }
-        l_run += rs;
-        // O^T += V^T P^T: V^T via transposing LDS reads of the row-major V tile
-#pragma unroll
-        for (int d = 0; d < DB; ++d) {
-#pragma unroll
-            for (int cch = 0; cch < 4; ++cch) {
-                const unsigned char* vp = st + 16 * cch * RB;
-                i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (FA_LDS i16x4*)(vp + (vbase[0] ^ (64 * d))));
-                i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (FA_LDS i16x4*)(vp + (vbase[1] ^ (64 * d))));
-                u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-                u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
-                o[d] = Mfma<T>::mma(a, p[cch], o[d]);
-            }
-        }
     };
 
-    if (kt0 < kt1) load_tile(kt0, 0);
+    // ---- prologue: K of the first two tiles, V of the first, scores of the first
+    f32x16 sc[2];  // scores of the current tile (masked)
+    load_k(kt0, 0);
+    if (kt0 + 1 < kt1) load_k(kt0 + 1, 1);
+    load_v(kt0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    qk(sc, L::koff(0));
+    if (kt0 < ki0 || kt0 >= ki1) apply_mask(sc, kt0 * BN);
+    update_max(sc);
+    moved = false;  // O and l are still zero
 
-    for (int64_t kt = kt0; kt < kt1; ++kt) {
-        const int stage = (int)((kt - kt0) & 1);
-        if (kt + 1 < kt1) load_tile(kt + 1, stage ^ 1);  // lands during this tile's math
-        const int64_t k0 = kt * BN;
-        if (!tile_fully_masked(ms, qw0, qw0 + kWaveRows - 1, k0, BN)) {
-            if (tile_needs_mask(ms, qw0, qw0 + kWaveRows - 1, k0, BN))
-                tile_math(stage, k0, BoolTag<true>{});
-            else
-                tile_math(stage, k0, BoolTag<false>{});
+    // ---- one pipelined step for tile j: S_{j+1} = K_{j+1} Q^T and the weights
+    // of tile j, then O += P_j V_j and the row max of tile j+1.  STAGE = (j -
+    // kt0) & 1: K_j sat in K stage STAGE (its slot is free now), K_{j+1} is in
+    // K stage STAGE^1, V_j in V stage STAGE.  MASK_NEXT: tile j+1 needs the
+    // mask.  LAST: j is the final tile.
+    auto step = [&](int j, auto stage_tag, auto mask_next_tag, auto last_tag) __attribute__((always_inline)) {
+        constexpr int ST = decltype(stage_tag)::value;
+        constexpr bool MASK_NEXT = decltype(mask_next_tag)::value;
+        constexpr bool LAST = decltype(last_tag)::value;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K_{j+1}, V_j have landed
+        __syncthreads();  // ... for every wave; every wave is done with tile j-1
+        if (!LAST) {
+            if (j + 2 < kt1) load_k(j + 2, ST);
+            load_v(j + 1, ST ^ 1);
         }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // next tile is in LDS
-        __syncthreads();
-    }
+        rescale_if_moved();
+        u32x4 p[4];
+        if (!LAST) {
+            f32x16 sn[2];
+            qk(sn, L::koff(ST ^ 1));
+            softmax(sc, p);
+            pv(p, L::voff(ST));
+            if (MASK_NEXT) apply_mask(sn, (j + 1) * BN);
+            update_max(sn);
+            sc[0] = sn[0];
+            sc[1] = sn[1];
+            // interleave: score MFMAs with the exp / pack / sum VALU work, then
+            // the P V MFMAs with the row max of the next tile
+            // operand reads from LDS run kLead MFMAs ahead of their MFMA
+            constexpr int NQK = 2 * KSTEPS, NPV = 4 * DB, kLead = 2;
+            // fma + exp per score, one cvt per pair, and the row sum
+            constexpr int NVALU = 64 + 16 + (Mfma<T>::kSumRounded ? 16 : 32);
+            constexpr int VALU_QK = (NVALU + NQK - 1) / NQK;
+            __builtin_amdgcn_sched_group_barrier(kSgDsRead, kLead, 0);
+#pragma unroll
+            for (int i = 0; i < NQK; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSgValu, VALU_QK, 0);
+                if (i + kLead < NQK) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * kLead, 0);
+#pragma unroll
+            for (int i = 0; i < NPV; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSgValu, 2, 0);
+                if (i + kLead < NPV) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+            }
+        } else {
+            softmax(sc, p);
+            pv(p, L::voff(ST));
+        }
+    };
+    // iterations [j0, j1), none of them the last; the stage alternates
+    auto run = [&](int j0, int j1, auto mask_next_tag) __attribute__((always_inline)) {
+        int j = j0;
+        if (j < j1 && ((j - kt0) & 1)) {
+            step(j, IntTag<1>{}, mask_next_tag, BoolTag<false>{});
+            ++j;
+        }
+        for (; j + 1 < j1; j += 2) {
+            step(j, IntTag<0>{}, mask_next_tag, BoolTag<false>{});
+            step(j + 1, IntTag<1>{}, mask_next_tag, BoolTag<false>{});
+        }
+        if (j < j1) step(j, IntTag<0>{}, mask_next_tag, BoolTag<false>{});
+    };
+    // iteration j has a mask-free next tile iff ki0 <= j + 1 < ki1
+    const int jl = kt1 - 1;
+    int ja = ki0 - 1 > kt0 ? ki0 - 1 : kt0;
+    if (ja > jl) ja = jl;
+    int jb = ki1 - 1 < jl ? ki1 - 1 : jl;
+    if (jb < ja) jb = ja;
+    run(kt0, ja, BoolTag<true>{});
+    run(ja, jb, BoolTag<false>{});
+    run(jb, jl, BoolTag<true>{});
+    if ((jl - kt0) & 1)
+        step(jl, IntTag<1>{}, BoolTag<false>{}, BoolTag<true>{});
+    else
+        step(jl, IntTag<0>{}, BoolTag<false>{}, BoolTag<true>{});
 
     // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
     // l == 0 only for a row with no allowed key; a NaN l (NaN scores) propagates
@@ -394,6 +536,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_mfma_kernel(
 // fp32 inputs run the same transposed-score structure on the fp32 MFMA
 // (v_mfma_f32_32x32x2_f32), so every product is an fp32 product; one key
 // (or one d) per lane per MFMA means V needs no transposition.
+constexpr int kThreads32 = 256;  // 4 waves
+constexpr int kBM32 = 4 * kWaveRows;
 template <int D> struct Lds32 {
     static constexpr int BN = 32;
     static constexpr int KS = D + 1;
@@ -401,7 +545,7 @@ template <int D> struct Lds32 {
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp32_kernel(
+__global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ out, float* __restrict__ lse, int B, int H, int S, float c, int causal,
     int wl, int wr, int n_qt) {
@@ -421,10 +565,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp32_kernel(
     const int bb = (int)(bh / H), h = (int)(bh % H);
     const MaskSpec ms{S, causal, wl, wr};
     int64_t kt0, kt1;
-    q_tile_kv_range(ms, qt, kBM, BN, &kt0, &kt1);
+    q_tile_kv_range(ms, qt, kBM32, BN, &kt0, &kt1);
     const int64_t row_stride = (int64_t)H * D;
     const int64_t head_base = ((int64_t)bb * S * H + h) * D;
-    const int qw0 = qt * kBM + wave * kWaveRows;
+    const int qw0 = qt * kBM32 + wave * kWaveRows;
     const int qrow = qw0 + ql;
 
     // Q fragment: lane supplies d = 2*kk + hh of its row
@@ -443,7 +587,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp32_kernel(
     for (int64_t kt = kt0; kt < kt1; ++kt) {
         const int64_t k0 = kt * BN;
         __syncthreads();
-        for (int id = tid; id < BN * (D / 4); id += kThreads) {
+        for (int id = tid; id < BN * (D / 4); id += kThreads32) {
             const int r = id / (D / 4), cc = id % (D / 4);
             const int64_t key = k0 + r;
             const bool ok = key < S;
@@ -527,21 +671,25 @@ __global__ __launch_bounds__(kThreads, 2) void fa_fwd_fp32_kernel(
 }
 
 // ---------------------------------------------------------------- launchers
+// Waves per workgroup of the bf16/fp16 kernel for head dimension D.
+template <int D> struct MfmaConfig { static constexpr int NW = 4; };
+
 template <typename T, int D>
 static hipError_t launch_mfma(const LaunchArgs& a) {
-    const int n_qt = (int)((a.S + kBM - 1) / kBM);
+    constexpr int NW = MfmaConfig<D>::NW;
+    const int n_qt = (int)((a.S + Tile<D, NW>::BM - 1) / Tile<D, NW>::BM);
     const int64_t n_wg = a.B * a.H * n_qt;
-    hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D>), dim3((unsigned)n_wg), dim3(kThreads), 0, a.stream,
-                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B,
-                       (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt);
+    hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW>), dim3((unsigned)n_wg), dim3(NW * 64), 0,
+                       a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse,
+                       (int)a.B, (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt);
     return hipGetLastError();
 }
 
 template <int D>
 static hipError_t launch_fp32(const LaunchArgs& a) {
-    const int n_qt = (int)((a.S + kBM - 1) / kBM);
+    const int n_qt = (int)((a.S + kBM32 - 1) / kBM32);
     const int64_t n_wg = a.B * a.H * n_qt;
-    hipLaunchKernelGGL((fa_fwd_fp32_kernel<D>), dim3((unsigned)n_wg), dim3(kThreads), 0, a.stream,
+    hipLaunchKernelGGL((fa_fwd_fp32_kernel<D>), dim3((unsigned)n_wg), dim3(kThreads32), 0, a.stream,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out, a.lse,
                        (int)a.B, (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt);
     return hipGetLastError();
@@ -555,7 +703,10 @@ hipError_t launch_fwd(const LaunchArgs& a) {
     }
 }
 
-int64_t q_tile_rows() { return kBM; }
-int64_t kv_tile_keys(int dtype) { return dtype == kDtypeFp32 ? Lds32<64>::BN : Tile<64>::BN; }
+int64_t q_tile_rows(int dtype, int64_t D) {
+    if (dtype == kDtypeFp32) return kBM32;
+    return D == 64 ? Tile<64, MfmaConfig<64>::NW>::BM : Tile<128, MfmaConfig<128>::NW>::BM;
+}
+int64_t kv_tile_keys(int dtype) { return dtype == kDtypeFp32 ? Lds32<64>::BN : 64; }
 
 }  // namespace fa

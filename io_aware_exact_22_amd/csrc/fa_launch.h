@@ -18,7 +18,7 @@ struct LaunchArgs {
     void* out;
     float* lse;
     int64_t B, H, S, D;
-    float c;  // scale * log2(e): scores enter exp2 directly
+    float c;  // max(scale * log2(e), FLT_MIN): scores enter exp2 directly
     int causal;
     int64_t wl, wr;  // already clamped to [-1, S]
     int dtype;
@@ -28,7 +28,7 @@ struct LaunchArgs {
 // Enqueues the forward kernel for validated arguments.
 hipError_t launch_fwd(const LaunchArgs& a);
 // Tile shape the kernels use: Q rows per workgroup, keys per K/V tile.
-int64_t q_tile_rows();
+int64_t q_tile_rows(int dtype, int64_t D);
 int64_t kv_tile_keys(int dtype);
 
 }  // namespace fa

@@ -77,6 +77,30 @@ __host__ __device__ inline void q_tile_kv_range(const MaskSpec& m, int64_t qt, i
     *kt1 = hi / bn + 1;
 }
 
+// K/V tiles [*ki0, *ki1) inside [kt0, kt1) where every key is allowed for
+// every row of [r0, r0 + bm - 1] and lies below S: the kernel runs them
+// without the mask.  The set is contiguous: a tile qualifies when its first
+// key is >= F (left window edge of the last row) and its last key is <= L
+// (causal / right window edge of the first row, and S - 1).  Tiles of
+// [kt0, ki0) and [ki1, kt1) need the mask.
+__host__ __device__ inline void q_tile_interior_range(const MaskSpec& m, int64_t r0, int64_t bm,
+                                                      int64_t bn, int64_t kt0, int64_t kt1,
+                                                      int64_t* ki0, int64_t* ki1) {
+    int64_t F = 0;
+    if (m.wl >= 0) F = r0 + bm - 1 - m.wl > 0 ? r0 + bm - 1 - m.wl : 0;
+    int64_t L = m.S - 1;
+    if (m.causal && r0 < L) L = r0;
+    if (m.wr >= 0 && r0 + m.wr < L) L = r0 + m.wr;
+    int64_t a = (F + bn - 1) / bn;  // first tile with t * bn >= F
+    int64_t b = (L + 1) / bn;       // tiles with t * bn + bn - 1 <= L
+    if (a < kt0) a = kt0;
+    if (a > kt1) a = kt1;
+    if (b > kt1) b = kt1;
+    if (b < a) b = a;
+    *ki0 = a;
+    *ki1 = b;
+}
+
 // Workgroup id -> logical tile id.  Consecutive workgroup ids are dispatched
 // round-robin over the 8 XCDs of the MI355X; this gives each XCD a contiguous
 // block of logical ids, so the Q tiles of one (batch, head) -- which stream

@@ -61,6 +61,7 @@ def check(**kw):
     ({"q": 0}, -1), ({"k": 0}, -1), ({"v": 0}, -1), ({"out": 0}, -1), ({"lse": 0}, -1),
     ({"B": 0}, -2), ({"H": 0}, -2), ({"S": 0}, -2), ({"S": -5}, -2),
     ({"S": 1 << 40}, -2), ({"B": 1 << 40, "H": 1 << 30}, -2),
+    ({"H": 131072, "D": 128, "S": 1}, -2), ({"H": 131071, "D": 128, "S": 1}, 0),
     ({"D": 96}, -3), ({"D": 0}, -3), ({"D": 256}, -3),
     ({"window_left": -2}, -4), ({"window_right": -7}, -4), ({"causal": 2}, -4),
     ({"dtype": 3}, -5), ({"dtype": -1}, -5),
