@@ -37,7 +37,8 @@ int check_problem(int64_t B, int64_t H, int64_t S, int64_t D, int causal, int64_
     // the kernels index rows with 32-bit S, B, H and launch B*H*ceil(S/128)
     // workgroups of 256 threads (grid limit: 2^32 - 1 work-items)
     if (S > INT32_MAX || B > INT32_MAX || H > INT32_MAX) return FA_ERR_SHAPE;
-    const int64_t bm = fa::q_tile_rows(dtype, D);
+    // the smallest Q tile of any configuration bounds the grid
+    const int64_t bm = 4 * 32;
     const int64_t n_qt = (S + bm - 1) / bm;
     int64_t n_wg, t;
     if (!mul_ok(B, H, &t) || !mul_ok(t, n_qt, &n_wg) || n_wg > (int64_t)(UINT32_MAX / 256))
@@ -132,11 +133,12 @@ FA_API int fa_fwd_tile_schedule(int64_t S, int64_t D, int dtype, int causal, int
     const int rc = check_problem(1, 1, S, D, causal, window_left, window_right, dtype, &nbytes,
                                  &lbytes);
     if (rc != FA_OK) return rc;
-    const int64_t BM = fa::q_tile_rows(dtype, D), BN = fa::kv_tile_keys(dtype);
+    const int64_t wlc = window_left >= S ? -1 : window_left;
+    const int64_t wrc = window_right >= S ? -1 : window_right;
+    const int64_t BM = fa::q_tile_rows(dtype, D, S, wlc, wrc), BN = fa::kv_tile_keys(dtype, D, S, wlc, wrc);
     const int64_t nq = (S + BM - 1) / BM;
     if (q_tile < 0 || q_tile >= nq) return FA_ERR_SHAPE;
-    const fa::MaskSpec m{S, causal, window_left >= S ? -1 : window_left,
-                         window_right >= S ? -1 : window_right};
+    const fa::MaskSpec m{S, causal, wlc, wrc};
     int64_t t0, t1;
     fa::q_tile_kv_range(m, q_tile, BM, BN, &t0, &t1);
     *bm = BM;

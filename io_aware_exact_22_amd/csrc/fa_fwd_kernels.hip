@@ -73,6 +73,13 @@ constexpr int kBufferFlags = 0x00020000;
 // log2-domain slack before the running reference max is moved (weights <= 2^8)
 constexpr float kRescaleSlack = 8.f;
 
+#ifndef FA_LEAD_K
+#define FA_LEAD_K 3
+#endif
+#ifndef FA_LEAD_V
+#define FA_LEAD_V 4
+#endif
+
 template <bool B> struct BoolTag { static constexpr bool value = B; };
 template <int N> struct IntTag { static constexpr int value = N; };
 
@@ -150,18 +157,18 @@ __device__ inline int k_row_for_mfma_row(int m) {
 // transposing V reads hit distinct banks, and turns every operand address
 // into (per-lane base) XOR (compile-time constant).
 //
-// LDS map: [K stage 0][K stage 1][V stage 0][V stage 1], one 64-key tile each.
-template <int D, int NW> struct Tile {
-    static constexpr int BN = 64;                   // keys per K/V tile
+// LDS: two K stages and two V stages, one 64-key tile each.
+template <int D, int NW, int BN_ = 64> struct Tile {
+    static constexpr int BN = BN_;                  // keys per K/V tile (32 or 64)
+    static constexpr int KB = BN / 32;              // 32-key blocks of the score MFMA
+    static constexpr int NCH = BN / 16;             // 16-key chunks of the P V MFMA
     static constexpr int BM = NW * kWaveRows;       // query rows per workgroup
     static constexpr int RB = D * 2;                // bytes per LDS row
     static constexpr int MAT = BN * RB;             // bytes per K (or V) tile
-    static constexpr int LDS_BYTES = 4 * MAT;
+    static constexpr int LDS_BYTES = 4 * MAT;  // two K and two V stages
     static constexpr int DMA_PER_WAVE = MAT / (1024 * NW);  // 1 KiB wave loads per matrix
     static_assert(MAT % (1024 * NW) == 0, "tile must split into 1 KiB wave loads");
     static_assert(LDS_BYTES <= 65536, "LDS operand offsets must fit the 16-bit ds offset");
-    __host__ __device__ static constexpr int koff(int stage) { return stage * MAT; }
-    __host__ __device__ static constexpr int voff(int stage) { return 2 * MAT + stage * MAT; }
     // chunk permutation of row r (D = 128: 16 chunks per row; D = 64: 8)
     __host__ __device__ static constexpr int swz(int r) {
         if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
@@ -182,17 +189,26 @@ __device__ inline void dma_matrix(__amdgpu_buffer_rsrc_t r, unsigned char* wave_
                                                  voff[j], 0, 0, 0);
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, int BN_>
 __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ out,
     float* __restrict__ lse, int B, int H, int S, float c, int causal, int wl, int wr, int n_qt) {
-    typedef Tile<D, NW> L;
+    typedef Tile<D, NW, BN_> L;
     constexpr int BN = L::BN;
     constexpr int BM = L::BM;
+    constexpr int KB = L::KB;
+    constexpr int NCH = L::NCH;
     constexpr int RB = L::RB;
     constexpr int KSTEPS = D / 16;  // 16-wide d chunks of the score MFMA
     constexpr int DB = D / 32;      // 32-wide d blocks of the output
-    __shared__ __attribute__((aligned(1024))) unsigned char lds[L::LDS_BYTES];
+    constexpr int kLeadK = FA_LEAD_K, kLeadV = FA_LEAD_V;
+    // one object per K / V stage: the compiler then sees that the direct-to-LDS
+    // load of one stage never aliases the operand reads of the other, and does
+    // not wait for the load before them
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_k0[L::MAT];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_k1[L::MAT];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_v0[L::MAT];
+    __shared__ __attribute__((aligned(1024))) unsigned char lds_v1[L::MAT];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -274,13 +290,12 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(
         const int r = byte / RB, pc = (byte % RB) / 16;
         dma_voff[j] = r * (int)row_stride * (int)sizeof(T) + 16 * (pc ^ L::swz(r));
     }
-    unsigned char* const wave_lds = lds + wave * 1024;
-    auto load_k = [&](int kt, int stage) __attribute__((always_inline)) {
-        dma_matrix<L::DMA_PER_WAVE, NW>(rows_rsrc(k, (int64_t)kt * BN), wave_lds + L::koff(stage),
+    auto load_k = [&](int kt, unsigned char* buf) __attribute__((always_inline)) {
+        dma_matrix<L::DMA_PER_WAVE, NW>(rows_rsrc(k, (int64_t)kt * BN), buf + wave * 1024,
                                         dma_voff);
     };
-    auto load_v = [&](int kt, int stage) __attribute__((always_inline)) {
-        dma_matrix<L::DMA_PER_WAVE, NW>(rows_rsrc(v, (int64_t)kt * BN), wave_lds + L::voff(stage),
+    auto load_v = [&](int kt, unsigned char* buf) __attribute__((always_inline)) {
+        dma_matrix<L::DMA_PER_WAVE, NW>(rows_rsrc(v, (int64_t)kt * BN), buf + wave * 1024,
                                         dma_voff);
     };
 
@@ -322,21 +337,21 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(
     for (int d = 0; d < DB; ++d) o[d] = f32x16{0};
 
     // S^T of one tile for this wave's 32 rows (two 32-key blocks)
-    auto qk = [&](f32x16(&s)[2], int kst) __attribute__((always_inline)) {
+    auto qk = [&](f32x16(&s)[KB], const unsigned char* kst) __attribute__((always_inline)) {
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+            for (int kb = 0; kb < KB; ++kb) {
                 const u32x4 a =
-                    *reinterpret_cast<const u32x4*>(lds + kst + 32 * kb * RB + kaddr[kk]);
+                    *reinterpret_cast<const u32x4*>(kst + 32 * kb * RB + kaddr[kk]);
                 s[kb] = Mfma<T>::mma(a, qf[kk], kk == 0 ? f32x16{0} : s[kb]);
             }
     };
     // keys outside this lane's allowed range -> -inf
-    auto apply_mask = [&](f32x16(&s)[2], int k0) __attribute__((always_inline)) {
+    auto apply_mask = [&](f32x16(&s)[KB], int k0) __attribute__((always_inline)) {
         const int a = k0 + 8 * hh - key_lo;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const bool ok = (unsigned)(a + 32 * kb + score_key_base(i)) <= (unsigned)key_w;
@@ -347,60 +362,54 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(
     // tile's max exceeds it by more than kRescaleSlack: weights stay below
     // 2^kRescaleSlack and the O / l rescale is rare.  O, l and LSE all use the
     // same reference, so the result is unchanged up to rounding.
-    auto update_max = [&](const f32x16(&s)[2]) __attribute__((always_inline)) {
+    auto update_max = [&](const f32x16(&s)[KB], bool valid = true) __attribute__((always_inline)) {
         float mx = kNegInf;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
         const float mt = halves_max(mx) * c;
-        const float m_new = (mt > m_run + kRescaleSlack) ? mt : m_run;
+        const float m_new = (valid && mt > m_run + kRescaleSlack) ? mt : m_run;
         m_use = (m_new == kNegInf) ? 0.f : m_new;  // row fully masked so far
         alpha = __builtin_amdgcn_exp2f(m_run - m_use);
         moved = m_new != m_run;
         m_run = m_new;
     };
     // weights of a tile, rounded and packed as the B operand of O^T += V^T P^T;
-    // the row sum adds the rounded weights
-    auto softmax = [&](const f32x16(&s)[2], u32x4(&p)[4]) __attribute__((always_inline)) {
-        float la = 0.f, lb = 0.f;
+    // the row sum adds the weights.  The source is skewed (fma of weight i,
+    // exp of weight i - 4, pack and sum of weights i - 9 and i - 8) so that the
+    // interleave with the MFMAs hands each MFMA slot a mix of independent
+    // instructions rather than an exp and the pack that waits for it.
+    auto softmax = [&](const f32x16(&s)[KB], u32x4(&p)[NCH]) __attribute__((always_inline)) {
+        constexpr int kExpLag = 4, kPackLag = 8;
+        constexpr int NE = 16 * KB;  // weights per lane
+        float e[NE];
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                u32x4 pk;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    const int i = 8 * half + 2 * t;
-                    const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i], c, -m_use));
-                    const float e1 =
-                        __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][i + 1], c, -m_use));
-                    pk[t] = Mfma<T>::pack2(e0, e1);
-                    if (!Mfma<T>::kSumRounded) {
-                        la += e0;
-                        lb += e1;
-                    }
-                }
-                p[2 * kb + half] = pk;
+        for (int st = 0; st < NE + kPackLag; ++st) {
+            if (st < NE) e[st] = __builtin_fmaf(s[st >> 4][st & 15], c, -m_use);
+            const int ie = st - kExpLag;
+            if (ie >= 0 && ie < NE) e[ie] = __builtin_amdgcn_exp2f(e[ie]);
+            const int ip = st - kPackLag;
+            if (ip >= 1 && ip < NE && (ip & 1)) {
+                p[ip >> 3][(ip & 7) >> 1] = Mfma<T>::pack2(e[ip - 1], e[ip]);
                 if (Mfma<T>::kSumRounded) {
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        if (t & 1)
-                            lb = Mfma<T>::sum2(pk[t], lb);
-                        else
-                            la = Mfma<T>::sum2(pk[t], la);
-                    }
+                    ls[(ip >> 1) & 3] = Mfma<T>::sum2(p[ip >> 3][(ip & 7) >> 1], ls[(ip >> 1) & 3]);
+                } else {
+                    ls[(ip >> 1) & 3] += e[ip - 1];
+                    ls[((ip >> 1) + 2) & 3] += e[ip];
                 }
             }
-        l_run += la + lb;
+        }
+        l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     };
     // O^T += V^T P^T with V^T from transposing LDS reads of the row-major tile
-    auto pv = [&](const u32x4(&p)[4], int vst) __attribute__((always_inline)) {
+    auto pv = [&](const u32x4(&p)[NCH], const unsigned char* vst) __attribute__((always_inline)) {
 #pragma unroll
-        for (int cch = 0; cch < 4; ++cch)
+        for (int cch = 0; cch < NCH; ++cch)
 #pragma unroll
             for (int d = 0; d < DB; ++d) {
-                const unsigned char* vp = lds + vst + 16 * cch * RB;
+                const unsigned char* vp = vst + 16 * cch * RB;
                 const i16x4 lo =
                     __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(vp + vaddr[0][d]));
                 const i16x4 hi =
@@ -419,13 +428,13 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(
     };
 
     // ---- prologue: K of the first two tiles, V of the first, scores of the first
-    f32x16 sc[2];  // scores of the current tile (masked)
-    load_k(kt0, 0);
-    if (kt0 + 1 < kt1) load_k(kt0 + 1, 1);
-    load_v(kt0, 0);
+    f32x16 sc[KB];  // scores of the current tile (masked)
+    load_k(kt0, lds_k0);
+    if (kt0 + 1 < kt1) load_k(kt0 + 1, lds_k1);
+    load_v(kt0, lds_v0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    qk(sc, L::koff(0));
+    qk(sc, lds_k0);
     if (kt0 < ki0 || kt0 >= ki1) apply_mask(sc, kt0 * BN);
     update_max(sc);
     moved = false;  // O and l are still zero
@@ -439,47 +448,56 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(
         constexpr int ST = decltype(stage_tag)::value;
         constexpr bool MASK_NEXT = decltype(mask_next_tag)::value;
         constexpr bool LAST = decltype(last_tag)::value;
+        unsigned char* const k_this = ST ? lds_k1 : lds_k0;  // K_j (free), later K_{j+2}
+        unsigned char* const k_next = ST ? lds_k0 : lds_k1;  // K_{j+1}
+        unsigned char* const v_this = ST ? lds_v1 : lds_v0;  // V_j
+        unsigned char* const v_next = ST ? lds_v0 : lds_v1;  // V_{j+1}
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K_{j+1}, V_j have landed
         __syncthreads();  // ... for every wave; every wave is done with tile j-1
         if (!LAST) {
-            if (j + 2 < kt1) load_k(j + 2, ST);
-            load_v(j + 1, ST ^ 1);
+            if (j + 2 < kt1) load_k(j + 2, k_this);
+            load_v(j + 1, v_next);
         }
         rescale_if_moved();
-        u32x4 p[4];
+        u32x4 p[NCH];
         if (!LAST) {
-            f32x16 sn[2];
-            qk(sn, L::koff(ST ^ 1));
+            f32x16 sn[KB];
+            qk(sn, k_next);
             softmax(sc, p);
-            pv(p, L::voff(ST));
+            pv(p, v_this);
             if (MASK_NEXT) apply_mask(sn, (j + 1) * BN);
             update_max(sn);
-            sc[0] = sn[0];
-            sc[1] = sn[1];
-            // interleave: score MFMAs with the exp / pack / sum VALU work, then
-            // the P V MFMAs with the row max of the next tile
-            // operand reads from LDS run kLead MFMAs ahead of their MFMA
-            constexpr int NQK = 2 * KSTEPS, NPV = 4 * DB, kLead = 2;
-            // fma + exp per score, one cvt per pair, and the row sum
-            constexpr int NVALU = 64 + 16 + (Mfma<T>::kSumRounded ? 16 : 32);
-            constexpr int VALU_QK = (NVALU + NQK - 1) / NQK;
-            __builtin_amdgcn_sched_group_barrier(kSgDsRead, kLead, 0);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) sc[kb] = sn[kb];
+            // interleave: every MFMA of the step (score MFMAs first, then P V)
+            // carries the same share of the VALU work -- the weights of tile
+            // j, then the row max of tile j+1 -- so neither phase is
+            // VALU-bound while the other leaves the vector ALU idle.
+            // Operand reads from LDS run ahead of their MFMA: kLeadK score
+            // MFMAs, kLeadV P V MFMAs (LDS latency under load is several
+            // MFMAs).
+            constexpr int NQK = KB * KSTEPS, NPV = NCH * DB;
+            // fma + exp per weight, one cvt per pair, the row sum, the max
+            constexpr int NVALU = KB * (32 + 8 + 8 + (Mfma<T>::kSumRounded ? 8 : 16)) + 16;
+            constexpr int VALU_PER = (NVALU + NQK + NPV - 1) / (NQK + NPV);
+            __builtin_amdgcn_sched_group_barrier(kSgDsRead, kLeadK, 0);
 #pragma unroll
             for (int i = 0; i < NQK; ++i) {
                 __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(kSgValu, VALU_QK, 0);
-                if (i + kLead < NQK) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSgValu, VALU_PER, 0);
+                if (i + kLeadK < NQK) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+                // the first V reads start under the last score MFMAs
+                if (i + kLeadV >= NQK) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * kLead, 0);
 #pragma unroll
             for (int i = 0; i < NPV; ++i) {
                 __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(kSgValu, 2, 0);
-                if (i + kLead < NPV) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(kSgValu, VALU_PER, 0);
+                if (i + kLeadV < NPV) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
             }
         } else {
             softmax(sc, p);
-            pv(p, L::voff(ST));
+            pv(p, v_this);
         }
     };
     // iterations [j0, j1), none of them the last; the stage alternates
@@ -671,18 +689,23 @@ __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
 }
 
 // ---------------------------------------------------------------- launchers
-// Waves per workgroup of the bf16/fp16 kernel for head dimension D.
-template <int D> struct MfmaConfig { static constexpr int NW = 4; };
-
-template <typename T, int D>
-static hipError_t launch_mfma(const LaunchArgs& a) {
-    constexpr int NW = MfmaConfig<D>::NW;
-    const int n_qt = (int)((a.S + Tile<D, NW>::BM - 1) / Tile<D, NW>::BM);
+template <typename T, int D, int NW, int BN>
+static hipError_t launch_mfma_cfg(const LaunchArgs& a) {
+    constexpr int BM = Tile<D, NW, BN>::BM;
+    const int n_qt = (int)((a.S + BM - 1) / BM);
     const int64_t n_wg = a.B * a.H * n_qt;
-    hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW>), dim3((unsigned)n_wg), dim3(NW * 64), 0,
+    hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN>), dim3((unsigned)n_wg), dim3(NW * 64), 0,
                        a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse,
                        (int)a.B, (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt);
     return hipGetLastError();
+}
+
+// bf16 / fp16: 4 waves, 128-row Q tiles, 64-key K/V tiles
+constexpr int kMfmaWaves = 4, kMfmaKeys = 64;
+
+template <typename T, int D>
+static hipError_t launch_mfma(const LaunchArgs& a) {
+    return launch_mfma_cfg<T, D, kMfmaWaves, kMfmaKeys>(a);
 }
 
 template <int D>
@@ -703,10 +726,11 @@ hipError_t launch_fwd(const LaunchArgs& a) {
     }
 }
 
-int64_t q_tile_rows(int dtype, int64_t D) {
-    if (dtype == kDtypeFp32) return kBM32;
-    return D == 64 ? Tile<64, MfmaConfig<64>::NW>::BM : Tile<128, MfmaConfig<128>::NW>::BM;
+int64_t q_tile_rows(int dtype, int64_t, int64_t, int64_t, int64_t) {
+    return dtype == kDtypeFp32 ? kBM32 : kMfmaWaves * kWaveRows;
 }
-int64_t kv_tile_keys(int dtype) { return dtype == kDtypeFp32 ? Lds32<64>::BN : 64; }
+int64_t kv_tile_keys(int dtype, int64_t, int64_t, int64_t, int64_t) {
+    return dtype == kDtypeFp32 ? Lds32<64>::BN : kMfmaKeys;
+}
 
 }  // namespace fa

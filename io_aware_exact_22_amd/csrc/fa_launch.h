@@ -27,8 +27,10 @@ struct LaunchArgs {
 
 // Enqueues the forward kernel for validated arguments.
 hipError_t launch_fwd(const LaunchArgs& a);
-// Tile shape the kernels use: Q rows per workgroup, keys per K/V tile.
-int64_t q_tile_rows(int dtype, int64_t D);
-int64_t kv_tile_keys(int dtype);
+// Tile shape the kernels use: Q rows per workgroup (it depends on the
+// configuration the launcher picks for S and the window; wl, wr already
+// clamped to [-1, S)), keys per K/V tile.
+int64_t q_tile_rows(int dtype, int64_t D, int64_t S, int64_t wl, int64_t wr);
+int64_t kv_tile_keys(int dtype, int64_t D, int64_t S, int64_t wl, int64_t wr);
 
 }  // namespace fa

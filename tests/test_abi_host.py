@@ -92,6 +92,7 @@ SCHEDULES = [
     (1, 0, -1, -1), (7, 1, -1, -1), (63, 0, 3, 0), (129, 1, -1, -1), (200, 0, 20, 40),
     (300, 1, 5, -1), (300, 0, 0, 0), (257, 0, -1, 100), (1000, 1, 64, 64), (520, 0, 128, 128),
     (2048 + 5, 1, -1, -1), (700, 0, 700, 699), (1500, 1, 1499, 3),
+    (4096 + 37, 1, -1, -1), (4096, 0, -1, -1), (5000, 1, 5000, -1),
 ]
 
 
@@ -118,12 +119,15 @@ def test_tile_schedule_against_brute_force(S, causal, wl, wr, dtype):
 
 
 def test_tile_schedule_counts_causal_16k():
-    """S = 16384 causal at 128 x 64 tiles: 129 * 128 - ... visited tiles per
-    head: Q tile t visits 2t + 2 tiles, two of which need the mask."""
+    """S = 16384 causal at 128 x 64 tiles: Q tile t visits 2t + 2 K/V tiles,
+    the last two of which (the diagonal) need the mask."""
+    s0 = fa.fa_fwd_tile_schedule(16384, 128, fa.FA_DTYPE_BF16, 1, -1, -1, 0)
+    assert (s0["bm"], s0["bn"], s0["n_q_tiles"]) == (128, 64, 128)
     tot, masked = 0, 0
     for qt in range(128):
         s = fa.fa_fwd_tile_schedule(16384, 128, fa.FA_DTYPE_BF16, 1, -1, -1, qt)
         assert s["kt_end"] - s["kt_begin"] == 2 * qt + 2
+        assert s["needs_mask"] == [0] * (2 * qt) + [1] * 2
         tot += s["kt_end"] - s["kt_begin"]
         masked += sum(s["needs_mask"])
     assert tot == 16512 and masked == 256

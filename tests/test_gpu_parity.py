@@ -81,6 +81,16 @@ def test_parity_lengths(S, causal):
     check_full(1, S, H, 128 if causal else 64, dtype, causal, (-1, -1), seed=S)
 
 
+@pytest.mark.parametrize("S", [4096, 4100, 4415])
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float16, 128),
+                                     (torch.bfloat16, 64), (torch.float16, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_parity_long_sequences(S, dtype, D, causal):
+    """Sequences of 4096 and more, every element against the oracle, including
+    ragged last Q and K/V tiles."""
+    check_full(1, S, 2, D, dtype, causal, (-1, -1), seed=S + D)
+
+
 @pytest.mark.parametrize("window", [(0, 0), (0, 64), (64, 0), (300, 0), (5, 2000), (4096, 4096),
                                     (1, 1), (127, 129)])
 @pytest.mark.parametrize("causal", [False, True])
