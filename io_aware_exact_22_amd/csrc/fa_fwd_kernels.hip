@@ -290,13 +290,26 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(
         const int r = byte / RB, pc = (byte % RB) / 16;
         dma_voff[j] = r * (int)row_stride * (int)sizeof(T) + 16 * (pc ^ L::swz(r));
     }
+    // Buffer resource of K/V tile kt, built with a few scalar ops per tile:
+    // base = head start + kt * tile bytes, records = the head's bytes from
+    // there on, clamped to 32 bits.  tile_bytes < 2^31 (64 rows, checked on
+    // the host), so kt * tile_bytes is one 32 x 32 -> 64-bit product.
+    const uint32_t tile_bytes = (uint32_t)(BN * row_stride * (int64_t)sizeof(T));
+    const uint64_t head_bytes = (uint64_t)(((int64_t)S - 1) * row_stride + D) * sizeof(T);
+    const unsigned char* const k_head = (const unsigned char*)(k + head_base);
+    const unsigned char* const v_head = (const unsigned char*)(v + head_base);
+    auto tile_rsrc = [&](const unsigned char* head, int kt) __attribute__((always_inline)) {
+        const uint64_t off = (uint64_t)(uint32_t)kt * tile_bytes;
+        const uint64_t rem = head_bytes - off;  // > 0: tile kt starts below S
+        const uint32_t nrec = (rem >> 32) ? 0xFFFFFFFFu : (uint32_t)rem;
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(head + off), (short)0, (int)nrec,
+                                                 kBufferFlags);
+    };
     auto load_k = [&](int kt, unsigned char* buf) __attribute__((always_inline)) {
-        dma_matrix<L::DMA_PER_WAVE, NW>(rows_rsrc(k, (int64_t)kt * BN), buf + wave * 1024,
-                                        dma_voff);
+        dma_matrix<L::DMA_PER_WAVE, NW>(tile_rsrc(k_head, kt), buf + wave * 1024, dma_voff);
     };
     auto load_v = [&](int kt, unsigned char* buf) __attribute__((always_inline)) {
-        dma_matrix<L::DMA_PER_WAVE, NW>(rows_rsrc(v, (int64_t)kt * BN), buf + wave * 1024,
-                                        dma_voff);
+        dma_matrix<L::DMA_PER_WAVE, NW>(tile_rsrc(v_head, kt), buf + wave * 1024, dma_voff);
     };
 
     // ---- per-lane LDS operand addresses (bytes within a tile)
