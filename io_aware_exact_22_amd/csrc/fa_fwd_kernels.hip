@@ -167,6 +167,7 @@ template <int D, int NW, int BN_ = 64> struct Tile {
     static constexpr int MAT = BN * RB;             // bytes per K (or V) tile
     static constexpr int LDS_BYTES = 4 * MAT;  // two K and two V stages
     static constexpr int DMA_PER_WAVE = MAT / (1024 * NW);  // 1 KiB wave loads per matrix
+    static_assert(DMA_PER_WAVE <= 4, "a wave's loads of a tile must fit the 12-bit immediate offset");
     static_assert(MAT % (1024 * NW) == 0, "tile must split into 1 KiB wave loads");
     static_assert(LDS_BYTES <= 65536, "LDS operand offsets must fit the 16-bit ds offset");
     // chunk permutation of row r (D = 128: 16 chunks per row; D = 64: 8)
@@ -178,15 +179,18 @@ template <int D, int NW, int BN_ = 64> struct Tile {
 };
 
 // Direct-to-LDS loads of one K or V tile by one wave: load j writes the 1 KiB
-// at wave_base + j * NW KiB (lane i -> 16 bytes at +16i) from byte offset
-// voff[j] of the tile's buffer resource.
-template <int N, int NW>
+// at wave_base + j KiB (lane i -> 16 bytes at +16i) from byte offset
+// voff[j] + j KiB of the tile's buffer resource.  The j KiB step is the
+// instruction's immediate offset, which moves both the global and the LDS
+// address, so one M0 value serves all of a wave's loads of a tile.
+template <int N>
 __device__ inline void dma_matrix(__amdgpu_buffer_rsrc_t r, unsigned char* wave_base,
                                   const int* voff) {
-#pragma unroll
-    for (int j = 0; j < N; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)(wave_base + j * NW * 1024), 16,
-                                                 voff[j], 0, 0, 0);
+    FA_LDS void* const l = (FA_LDS void*)wave_base;
+    if (N > 0) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff[0], 0, 0, 0);
+    if (N > 1) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff[N > 1 ? 1 : 0], 0, 1024, 0);
+    if (N > 2) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff[N > 2 ? 2 : 0], 0, 2048, 0);
+    if (N > 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff[N > 3 ? 3 : 0], 0, 3072, 0);
 }
 
 template <typename T, int D, int NW, int BN_>
@@ -280,15 +284,18 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(
         }
     }
 
-    // ---- K/V tile loader: wave `wave`, load j writes LDS bytes
-    // [(j*NW + wave) * 1024 + 16*lane, +16) of the tile; the source is the
-    // logical chunk stored there.
+    // ---- K/V tile loader: wave `wave` fills the contiguous LDS bytes
+    // [wave * DMA_PER_WAVE KiB, +DMA_PER_WAVE KiB) of the tile; load j writes
+    // [(wave * DMA_PER_WAVE + j) * 1024 + 16*lane, +16) with the logical chunk
+    // stored there.  dma_voff[j] leaves out the j KiB the load's immediate
+    // offset adds (it is >= 0: chunk j starts at least j KiB into the tile's
+    // rows, whose stride H * D * e is at least the LDS row of D * e bytes).
     int dma_voff[L::DMA_PER_WAVE];
 #pragma unroll
     for (int j = 0; j < L::DMA_PER_WAVE; ++j) {
-        const int byte = (j * NW + wave) * 1024 + 16 * lane;
+        const int byte = (wave * L::DMA_PER_WAVE + j) * 1024 + 16 * lane;
         const int r = byte / RB, pc = (byte % RB) / 16;
-        dma_voff[j] = r * (int)row_stride * (int)sizeof(T) + 16 * (pc ^ L::swz(r));
+        dma_voff[j] = r * (int)row_stride * (int)sizeof(T) + 16 * (pc ^ L::swz(r)) - 1024 * j;
     }
     // Buffer resource of K/V tile kt, built with a few scalar ops per tile:
     // base = head start + kt * tile bytes, records = the head's bytes from
@@ -300,16 +307,21 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(
     const unsigned char* const v_head = (const unsigned char*)(v + head_base);
     auto tile_rsrc = [&](const unsigned char* head, int kt) __attribute__((always_inline)) {
         const uint64_t off = (uint64_t)(uint32_t)kt * tile_bytes;
-        const uint64_t rem = head_bytes - off;  // > 0: tile kt starts below S
+        // records run to the end of the head's last row; a tile that starts at
+        // or past S gets none, so the hardware range check turns every read of
+        // it into a zero instead of an access past the tensor
+        const uint64_t rem = off < head_bytes ? head_bytes - off : 0;
         const uint32_t nrec = (rem >> 32) ? 0xFFFFFFFFu : (uint32_t)rem;
         return __builtin_amdgcn_make_buffer_rsrc((void*)(head + off), (short)0, (int)nrec,
                                                  kBufferFlags);
     };
     auto load_k = [&](int kt, unsigned char* buf) __attribute__((always_inline)) {
-        dma_matrix<L::DMA_PER_WAVE, NW>(tile_rsrc(k_head, kt), buf + wave * 1024, dma_voff);
+        dma_matrix<L::DMA_PER_WAVE>(tile_rsrc(k_head, kt), buf + wave * L::DMA_PER_WAVE * 1024,
+                                    dma_voff);
     };
     auto load_v = [&](int kt, unsigned char* buf) __attribute__((always_inline)) {
-        dma_matrix<L::DMA_PER_WAVE, NW>(tile_rsrc(v_head, kt), buf + wave * 1024, dma_voff);
+        dma_matrix<L::DMA_PER_WAVE>(tile_rsrc(v_head, kt), buf + wave * L::DMA_PER_WAVE * 1024,
+                                    dma_voff);
     };
 
     // ---- per-lane LDS operand addresses (bytes within a tile)
