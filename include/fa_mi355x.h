@@ -116,6 +116,23 @@ int fa_fwd_tile_schedule(int64_t S, int64_t D, int dtype, int causal, int64_t wi
                          int64_t* n_q_tiles, int64_t* kt_begin, int64_t* kt_end,
                          uint8_t* needs_mask, int64_t max_tiles);
 
+/*
+ * fa_fwd_workgroup_tile -- host-side view of the launch order fa_fwd uses:
+ * the (b * H + h, Q tile) that workgroup `wg` of the grid processes.  Pure
+ * function, no HIP call.  The grid has B * H * n_q_tiles workgroups (n_q_tiles
+ * as fa_fwd_tile_schedule reports), and the map is a bijection onto the
+ * (batch-head, Q tile) pairs.  Workgroup ids are dispatched round-robin over
+ * the 8 XCDs, and each XCD gets a contiguous block of the head-major list of
+ * tiles (its heads' K/V stay in its L2); with causal = 1 each XCD visits its
+ * block's Q tiles heaviest first across heads (more K/V tiles to walk =
+ * earlier), so that light tiles end the launch (thread-block load balance,
+ * the note closing [FA] section 1).
+ * Returns FA_OK, or FA_ERR_* for bad arguments or wg outside the grid.
+ */
+int fa_fwd_workgroup_tile(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int causal,
+                          int64_t window_left, int64_t window_right, int64_t wg, int64_t* bh,
+                          int64_t* q_tile);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,9 +7,11 @@ forward pass runs in the library's kernels, and the binding raises if the
 library is missing rather than falling back to anything else.
 """
 from .fa import (FA_DTYPE_BF16, FA_DTYPE_FP16, FA_DTYPE_FP32, FaError, fa_fwd, fa_fwd_check_args,
-                 fa_fwd_tile_schedule, fa_status_string, flash_attn_fwd, library_path)
+                 fa_fwd_tile_schedule, fa_fwd_workgroup_tile, fa_status_string, flash_attn_fwd,
+                 library_path)
 
 __all__ = [
     "FA_DTYPE_BF16", "FA_DTYPE_FP16", "FA_DTYPE_FP32", "FaError", "fa_fwd", "fa_fwd_check_args",
-    "fa_fwd_tile_schedule", "fa_status_string", "flash_attn_fwd", "library_path",
+    "fa_fwd_tile_schedule", "fa_fwd_workgroup_tile", "fa_status_string", "flash_attn_fwd",
+    "library_path",
 ]

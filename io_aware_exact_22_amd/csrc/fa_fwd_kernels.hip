@@ -41,7 +41,8 @@
 //    tiles inside it for every row of the workgroup run a loop body that has
 //    no mask code at all; the few boundary tiles apply the mask.
 //  * Workgroup ids are remapped so each XCD holds whole (batch, head) groups
-//    (L2 reuse of K/V), and causal Q tiles run heaviest first.
+//    (L2 reuse of K/V); for causal masks each XCD runs the heaviest Q tiles of
+//    all its heads first, so the light tiles fill the end of the launch.
 //  * Probabilities are rounded to the input dtype (RNE, v_cvt_pk_*) for the
 //    P V MFMA.  The row sum adds the fp32 weights for bf16 and the fp16-rounded
 //    weights two at a time (v_dot2c with ones) for fp16.  Max, exp and the
@@ -220,13 +221,11 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(
     const int hh = lane >> 5;   // wave half
     const int ql = lane & 31;   // query row of this lane within the wave
 
-    // ---- workgroup -> (b, h, q tile)
-    const int64_t n_wg = (int64_t)B * H * n_qt;
-    const int64_t logical = xcd_remap(blockIdx.x, n_wg);
-    const int64_t bh = logical / n_qt;
-    int qt = (int)(logical % n_qt);
-    if (causal) qt = n_qt - 1 - qt;  // heaviest Q tiles first
-    const int bb = (int)(bh / H), h = (int)(bh % H);
+    // ---- workgroup -> (b, h, q tile); causal: heaviest Q tiles first per XCD
+    uint32_t bh, qt32;
+    workgroup_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt, causal != 0, &bh, &qt32);
+    const int qt = (int)qt32;
+    const int bb = (int)(bh / (uint32_t)H), h = (int)(bh % (uint32_t)H);
 
     // ---- K/V tiles of this Q tile: [kt0, kt1); mask-free ones: [ki0, ki1)
     const MaskSpec ms{S, causal, wl, wr};
@@ -600,12 +599,10 @@ __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hh = lane >> 5, ql = lane & 31;
-    const int64_t n_wg = (int64_t)B * H * n_qt;
-    const int64_t logical = xcd_remap(blockIdx.x, n_wg);
-    const int64_t bh = logical / n_qt;
-    int qt = (int)(logical % n_qt);
-    if (causal) qt = n_qt - 1 - qt;
-    const int bb = (int)(bh / H), h = (int)(bh % H);
+    uint32_t bh, qt32;
+    workgroup_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt, causal != 0, &bh, &qt32);
+    const int qt = (int)qt32;
+    const int bb = (int)(bh / (uint32_t)H), h = (int)(bh % (uint32_t)H);
     const MaskSpec ms{S, causal, wl, wr};
     int64_t kt0, kt1;
     q_tile_kv_range(ms, qt, kBM32, BN, &kt0, &kt1);

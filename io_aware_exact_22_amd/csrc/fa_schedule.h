@@ -101,15 +101,70 @@ __host__ __device__ inline void q_tile_interior_range(const MaskSpec& m, int64_t
     *ki1 = b;
 }
 
-// Workgroup id -> logical tile id.  Consecutive workgroup ids are dispatched
-// round-robin over the 8 XCDs of the MI355X; this gives each XCD a contiguous
-// block of logical ids, so the Q tiles of one (batch, head) -- which stream
-// the same K/V -- share that XCD's L2.
-__host__ __device__ inline int64_t xcd_remap(int64_t w, int64_t n) {
-    constexpr int64_t kXcds = 8;
-    const int64_t xcd = w % kXcds, idx = w / kXcds;
-    const int64_t per = n / kXcds, rem = n % kXcds;
-    return xcd * per + (xcd < rem ? xcd : rem) + idx;
+// Workgroup id -> (b * H + h, Q tile).  Consecutive workgroup ids are
+// dispatched round-robin over the 8 XCDs of the MI355X, so workgroup w runs on
+// XCD w % 8 and is that XCD's (w / 8)-th workgroup.  Each XCD gets a
+// contiguous block of the (head-major, Q-tile-minor) list of all tiles: the Q
+// tiles of one (batch, head), which stream the same K/V, share that XCD's L2.
+//
+// by_weight (causal launches, where Q tile t visits about t + 1 K/V tiles):
+// within its block an XCD runs the heaviest tiles of all its heads first --
+// the block is walked column by column over weight ranks (rank 0 = last Q
+// tile), head by head inside a column -- so that the light tiles, not the
+// heavy tiles of the block's last head, fill the end of the launch.
+// Otherwise the block is walked in list order.  Either way the map is a
+// bijection of [0, n_bh * n_qt).
+// All counts are 32-bit (the host bounds the grid well below 2^32 workgroups),
+// which keeps the per-workgroup index arithmetic short.
+__host__ __device__ inline void workgroup_tile(uint32_t w, uint32_t n_bh, uint32_t n_qt,
+                                               bool by_weight, uint32_t* bh, uint32_t* qt) {
+    constexpr uint32_t kXcds = 8;
+    const uint32_t n = n_bh * n_qt;
+    const uint32_t xcd = w % kXcds, idx = w / kXcds;
+    const uint32_t per = n / kXcds, rem = n % kXcds;
+    const uint32_t s = xcd * per + (xcd < rem ? xcd : rem);  // block start in the list
+    if (!by_weight) {
+        *bh = (s + idx) / n_qt;
+        *qt = (s + idx) % n_qt;
+        return;
+    }
+    // list position p = row * n_qt + rank; the block [s, e] covers row r0 from
+    // rank a0 on, rows r0+1 .. r1-1 whole, and row r1 up to rank b1
+    const uint32_t e = s + per + (xcd < rem ? 1 : 0) - 1;
+    const uint32_t r0 = s / n_qt, a0 = s - r0 * n_qt, r1 = e / n_qt, b1 = e - r1 * n_qt;
+    uint32_t row, rank;
+    if (r0 == r1) {
+        row = r0;
+        rank = a0 + idx;
+    } else {
+        const uint32_t full = r1 - r0 - 1;
+        // block entries with rank < c
+        auto before = [&](uint32_t c) {
+            return c * full + (c > a0 ? c - a0 : 0) + (c < b1 + 1 ? c : b1 + 1);
+        };
+        uint32_t lo = 0, hi = n_qt - 1;  // the largest c with before(c) <= idx
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi + 1) / 2;
+            if (before(mid) <= idx)
+                lo = mid;
+            else
+                hi = mid - 1;
+        }
+        rank = lo;
+        uint32_t k = idx - before(lo);  // position inside column `rank`
+        bool done = false;
+        if (rank >= a0) {
+            if (k == 0) {
+                row = r0;
+                done = true;
+            } else {
+                --k;
+            }
+        }
+        if (!done) row = k < full ? r0 + 1 + k : r1;
+    }
+    *bh = row;
+    *qt = n_qt - 1 - rank;
 }
 
 }  // namespace fa

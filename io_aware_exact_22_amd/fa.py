@@ -1,7 +1,7 @@
 """ctypes binding of libfa_mi355x (declared in include/fa_mi355x.h).
 
 Same names as the C ABI: ``fa_fwd``, ``fa_fwd_check_args``,
-``fa_status_string``, ``fa_fwd_tile_schedule``; plus ``flash_attn_fwd``, the
+``fa_status_string``, ``fa_fwd_tile_schedule``, ``fa_fwd_workgroup_tile``; plus ``flash_attn_fwd``, the
 tensor-level call that mirrors the pages' ``flash_attention(q, k, v,
 softmax_scale=None, causal=..., window_size=(-1, -1))`` argument list
 ("FlashAttention技术解析：加速GPT训练的核心优化", section 2.2).  This module only
@@ -63,6 +63,9 @@ def _load():
         lib.fa_fwd_tile_schedule.argtypes = [i64, i64, cint, cint, i64, i64, i64, p64, p64, p64,
                                              p64, p64, vp, i64]
         lib.fa_fwd_tile_schedule.restype = cint
+        lib.fa_fwd_workgroup_tile.argtypes = [i64, i64, i64, i64, cint, cint, i64, i64, i64, p64,
+                                              p64]
+        lib.fa_fwd_workgroup_tile.restype = cint
         _lib = lib
         return lib
 
@@ -104,6 +107,17 @@ def fa_fwd_tile_schedule(S: int, D: int, dtype: int, causal: int, window_left: i
         raise FaError(rc, "fa_fwd_tile_schedule")
     return {"bm": bm, "bn": bn, "n_q_tiles": nq, "kt_begin": t0, "kt_end": t1,
             "needs_mask": [int(mask[i]) for i in range(t1 - t0)]}
+
+
+def fa_fwd_workgroup_tile(B: int, H: int, S: int, D: int, dtype: int, causal: int,
+                          window_left: int, window_right: int, wg: int) -> tuple[int, int]:
+    """Host view of the launch order: (b * H + h, Q tile) of workgroup ``wg``."""
+    bh, qt = ctypes.c_int64(), ctypes.c_int64()
+    rc = _load().fa_fwd_workgroup_tile(B, H, S, D, dtype, causal, window_left, window_right, wg,
+                                       ctypes.byref(bh), ctypes.byref(qt))
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_workgroup_tile")
+    return bh.value, qt.value
 
 
 # ------------------------------------------------------------------ tensor call

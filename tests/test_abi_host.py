@@ -24,7 +24,8 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert set(names) == {"fa_fwd", "fa_fwd_check_args", "fa_status_string", "fa_fwd_tile_schedule"}
+    assert set(names) == {"fa_fwd", "fa_fwd_check_args", "fa_status_string", "fa_fwd_tile_schedule",
+                          "fa_fwd_workgroup_tile"}
     lib = ctypes.CDLL(fa.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -131,6 +132,35 @@ def test_tile_schedule_counts_causal_16k():
         tot += s["kt_end"] - s["kt_begin"]
         masked += sum(s["needs_mask"])
     assert tot == 16512 and masked == 256
+
+
+@pytest.mark.parametrize("B,H,S", [(1, 16, 16384), (2, 16, 2048), (1, 3, 1000), (1, 5, 16384),
+                                   (3, 7, 300), (1, 1, 128), (2, 1, 129), (1, 12, 4096)])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_workgroup_order(B, H, S, causal):
+    """The launch order is a bijection onto the (batch-head, Q tile) pairs; XCD
+    x (workgroups x, x + 8, ...) holds one contiguous block of the head-major
+    tile list; with the causal mask it visits that block heaviest Q tile first
+    (non-increasing visited K/V tile count)."""
+    dt = fa.FA_DTYPE_BF16
+    nq = fa.fa_fwd_tile_schedule(S, 128, dt, causal, -1, -1, 0)["n_q_tiles"]
+    n = B * H * nq
+    visits = [fa.fa_fwd_tile_schedule(S, 128, dt, causal, -1, -1, t) for t in range(nq)]
+    visits = [x["kt_end"] - x["kt_begin"] for x in visits]
+    tiles = [fa.fa_fwd_workgroup_tile(B, H, S, 128, dt, causal, -1, -1, w) for w in range(n)]
+    assert sorted(tiles) == [(bh, qt) for bh in range(B * H) for qt in range(nq)]
+    for x in range(8):
+        seq = tiles[x::8]
+        # list position of each tile: head-major, heaviest-first rank when causal
+        pos = sorted(bh * nq + (nq - 1 - qt if causal else qt) for bh, qt in seq)
+        assert pos == list(range(pos[0], pos[0] + len(pos))) if pos else True
+        if causal:
+            w = [visits[qt] for _, qt in seq]
+            assert all(a >= b for a, b in zip(w, w[1:])), (x, w[:20])
+        else:
+            assert [bh * nq + qt for bh, qt in seq] == pos
+    with pytest.raises(fa.FaError):
+        fa.fa_fwd_workgroup_tile(B, H, S, 128, dt, causal, -1, -1, n)
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
