@@ -195,7 +195,7 @@ __device__ inline void dma_matrix(__amdgpu_buffer_rsrc_t r, unsigned char* wave_
 }
 
 template <typename T, int D, int NW, int BN_>
-__global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(
+__global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ out,
     float* __restrict__ lse, int B, int H, int S, float c, int causal, int wl, int wr, int n_qt) {
     typedef Tile<D, NW, BN_> L;
@@ -555,21 +555,43 @@ __global__ __launch_bounds__(NW * 64, 1) void fa_fwd_mfma_kernel(
     // l == 0 only for a row with no allowed key; a NaN l (NaN scores) propagates
     const float l_tot = halves_sum(l_run);
     const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
-    if (qrow < S) {
-        T* op = out + head_base + (int64_t)qrow * row_stride + 4 * hh;
+    if (qrow < S && hh == 0) {
+        const float m_fin = (m_run == kNegInf) ? 0.f : m_run;
+        const float lse_v =
+            (l_tot == 0.f) ? kNegInf : 0.69314718055994531f * (m_fin + __log2f(l_tot));
+        lse[((int64_t)bb * H + h) * S + qrow] = lse_v;
+    }
+    // O leaves through LDS so that the global stores run along whole rows: a
+    // lane holds one row's columns 32d + 8g + 4*hh .. +3, so it writes them
+    // into the wave's 32 x D staging tile (16-byte chunk c of row r stored at
+    // chunk c ^ (r % NC): the column-wise writes spread over the banks), and
+    // then each lane reads and stores 16 contiguous bytes of a row.  The K
+    // stages are free here: no wave reads K in the last step.
+    constexpr int NC = RB / 16;                 // 16-byte chunks per row
+    constexpr int WAVE_BYTES = kWaveRows * RB;  // one wave's staging tile
+    constexpr int ROWS_PER_READ = 1024 / RB;    // rows one 16-byte-per-lane read covers
+    static_assert(2 * L::MAT >= NW * WAVE_BYTES, "the K stages hold the output tile");
+    unsigned char* const stg = wave * WAVE_BYTES < L::MAT
+                                   ? lds_k0 + wave * WAVE_BYTES
+                                   : lds_k1 + (wave * WAVE_BYTES - L::MAT);
 #pragma unroll
-        for (int d = 0; d < DB; ++d)
+    for (int d = 0; d < DB; ++d)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                u32x2 w = {Mfma<T>::pack2(o[d][4 * g] * inv, o[d][4 * g + 1] * inv),
-                           Mfma<T>::pack2(o[d][4 * g + 2] * inv, o[d][4 * g + 3] * inv)};
-                *reinterpret_cast<u32x2*>(op + 32 * d + 8 * g) = w;
-            }
-        if (hh == 0) {
-            const float m_fin = (m_run == kNegInf) ? 0.f : m_run;
-            const float lse_v =
-                (l_tot == 0.f) ? kNegInf : 0.69314718055994531f * (m_fin + __log2f(l_tot));
-            lse[((int64_t)bb * H + h) * S + qrow] = lse_v;
+        for (int g = 0; g < 4; ++g) {
+            const u32x2 w = {Mfma<T>::pack2(o[d][4 * g] * inv, o[d][4 * g + 1] * inv),
+                             Mfma<T>::pack2(o[d][4 * g + 2] * inv, o[d][4 * g + 3] * inv)};
+            const int chunk = (4 * d + g) ^ (ql & (NC - 1));
+            *reinterpret_cast<u32x2*>(stg + ql * RB + 16 * chunk + 8 * hh) = w;
+        }
+    {
+        const int rl = lane / NC, cl = lane % NC;
+        T* const orow = out + head_base + 8 * cl;
+#pragma unroll
+        for (int i = 0; i < kWaveRows / ROWS_PER_READ; ++i) {
+            const int r = i * ROWS_PER_READ + rl;
+            const u32x4 x =
+                *reinterpret_cast<const u32x4*>(stg + r * RB + 16 * (cl ^ (r & (NC - 1))));
+            if (qw0 + r < S) *reinterpret_cast<u32x4*>(orow + (int64_t)(qw0 + r) * row_stride) = x;
         }
     }
 }
