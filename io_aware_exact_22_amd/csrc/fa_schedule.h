@@ -108,14 +108,17 @@ __host__ __device__ inline void q_tile_interior_range(const MaskSpec& m, int64_t
 // tiles of one (batch, head), which stream the same K/V, share that XCD's L2.
 //
 // by_weight (causal launches, where Q tile t visits about t + 1 K/V tiles):
-// within its block an XCD runs the heaviest tiles of all its heads first --
-// the block is walked column by column over weight ranks (rank 0 = last Q
-// tile), head by head inside a column -- so that the light tiles, not the
-// heavy tiles of the block's last head, fill the end of the launch.
+// rank r of a head's tiles is Q tile n_qt - 1 - r (rank 0 = heaviest).  The
+// XCD first runs the heavy ranks [0, R) head by head, heaviest first (one
+// head's K/V in its L2 at a time), then the light ranks [R, n_qt) of all its
+// heads rank by rank, so that the launch ends on the lightest tiles of every
+// head and the workgroups still running at the end have little work left.
 // Otherwise the block is walked in list order.  Either way the map is a
-// bijection of [0, n_bh * n_qt).
-// All counts are 32-bit (the host bounds the grid well below 2^32 workgroups),
-// which keeps the per-workgroup index arithmetic short.
+// bijection of [0, n_bh * n_qt).  All counts are 32-bit (the host bounds the
+// grid well below 2^32 workgroups), which keeps the index arithmetic short.
+#ifndef FA_LIGHT_DIV
+#define FA_LIGHT_DIV 4  // the lightest 1/FA_LIGHT_DIV of each head's Q tiles close the launch
+#endif
 __host__ __device__ inline void workgroup_tile(uint32_t w, uint32_t n_bh, uint32_t n_qt,
                                                bool by_weight, uint32_t* bh, uint32_t* qt) {
     constexpr uint32_t kXcds = 8;
@@ -129,20 +132,37 @@ __host__ __device__ inline void workgroup_tile(uint32_t w, uint32_t n_bh, uint32
         return;
     }
     // list position p = row * n_qt + rank; the block [s, e] covers row r0 from
-    // rank a0 on, rows r0+1 .. r1-1 whole, and row r1 up to rank b1
+    // rank a0 on, rows r0+1 .. r1-1 whole (`full` of them), and row r1 up to
+    // rank b1 (r0 == r1: ranks a0 .. b1 of one row)
     const uint32_t e = s + per + (xcd < rem ? 1 : 0) - 1;
     const uint32_t r0 = s / n_qt, a0 = s - r0 * n_qt, r1 = e / n_qt, b1 = e - r1 * n_qt;
+    const uint32_t full = r1 > r0 ? r1 - r0 - 1 : 0;
     uint32_t row, rank;
-    if (r0 == r1) {
-        row = r0;
-        rank = a0 + idx;
-    } else {
-        const uint32_t full = r1 - r0 - 1;
-        // block entries with rank < c
-        auto before = [&](uint32_t c) {
-            return c * full + (c > a0 ? c - a0 : 0) + (c < b1 + 1 ? c : b1 + 1);
-        };
-        uint32_t lo = 0, hi = n_qt - 1;  // the largest c with before(c) <= idx
+    if (r0 == r1) {  // one row: rank order is heaviest first already
+        *bh = r0;
+        *qt = n_qt - 1 - (a0 + idx);
+        return;
+    }
+    // block entries with rank < c
+    auto before = [&](uint32_t c) {
+        return c * full + (c > a0 ? c - a0 : 0) + (c < b1 + 1 ? c : b1 + 1);
+    };
+    const uint32_t R = n_qt - n_qt / FA_LIGHT_DIV;  // heavy ranks [0, R)
+    const uint32_t n_heavy = before(R);
+    if (idx < n_heavy) {  // heavy part, row by row
+        const uint32_t c0 = R > a0 ? R - a0 : 0;  // heavy entries of row r0
+        if (idx < c0) {
+            row = r0;
+            rank = a0 + idx;
+        } else if (idx - c0 < full * R) {
+            row = r0 + 1 + (idx - c0) / R;
+            rank = (idx - c0) % R;
+        } else {
+            row = r1;
+            rank = idx - c0 - full * R;
+        }
+    } else {  // light part, rank by rank
+        uint32_t lo = R, hi = n_qt - 1;  // the largest c >= R with before(c) <= idx
         while (lo < hi) {
             const uint32_t mid = (lo + hi + 1) / 2;
             if (before(mid) <= idx)

@@ -140,8 +140,10 @@ def test_tile_schedule_counts_causal_16k():
 def test_workgroup_order(B, H, S, causal):
     """The launch order is a bijection onto the (batch-head, Q tile) pairs; XCD
     x (workgroups x, x + 8, ...) holds one contiguous block of the head-major
-    tile list; with the causal mask it visits that block heaviest Q tile first
-    (non-increasing visited K/V tile count)."""
+    tile list.  With the causal mask the XCD runs the heavy three quarters of
+    each head's Q tiles head by head, heaviest first, and then the lightest
+    quarter of all its heads in non-increasing visited K/V tile count, after
+    every heavier tile."""
     dt = fa.FA_DTYPE_BF16
     nq = fa.fa_fwd_tile_schedule(S, 128, dt, causal, -1, -1, 0)["n_q_tiles"]
     n = B * H * nq
@@ -155,7 +157,12 @@ def test_workgroup_order(B, H, S, causal):
         pos = sorted(bh * nq + (nq - 1 - qt if causal else qt) for bh, qt in seq)
         assert pos == list(range(pos[0], pos[0] + len(pos))) if pos else True
         if causal:
-            w = [visits[qt] for _, qt in seq]
+            light = nq // 4  # Q tiles qt < light close the launch
+            heavy = [(bh, qt) for bh, qt in seq if qt >= light]
+            tail = [(bh, qt) for bh, qt in seq if qt < light]
+            assert seq == heavy + tail
+            assert heavy == sorted(heavy, key=lambda t: (t[0], -t[1]))
+            w = [visits[qt] for _, qt in tail]
             assert all(a >= b for a, b in zip(w, w[1:])), (x, w[:20])
         else:
             assert [bh * nq + qt for bh, qt in seq] == pos
