@@ -458,10 +458,28 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
     load_v(kt0, lds_v0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    qk(sc, lds_k0);
-    if (kt0 < ki0 || kt0 >= ki1) apply_mask(sc, kt0 * BN);
-    update_max(sc);
-    moved = false;  // O and l are still zero
+    // K/V tiles this wave computes: [kw0, kw1), the tiles of [kt0, kt1) that
+    // hold an allowed key for one of its own 32 rows (a window or the causal
+    // diagonal leaves some tiles of the workgroup empty for some of its
+    // waves).  The loads and barriers still run over the workgroup's
+    // [kt0, kt1), so every wave passes the same barriers.  Padding rows past
+    // S take the workgroup's range.
+    int kw0 = kt0, kw1 = kt1;
+    if (qw0 < S) {
+        int64_t lo, hi;
+        key_range(ms, qw0, qw0 + kWaveRows - 1 < S - 1 ? qw0 + kWaveRows - 1 : S - 1, &lo, &hi);
+        kw0 = (int)(lo / BN) > kt0 ? (int)(lo / BN) : kt0;
+        kw1 = (int)(hi / BN) + 1 < kt1 ? (int)(hi / BN) + 1 : kt1;
+    }
+    kw0 = __builtin_amdgcn_readfirstlane(kw0);
+    kw1 = __builtin_amdgcn_readfirstlane(kw1);
+    auto first_scores = [&](int kt, unsigned char* kst) __attribute__((always_inline)) {
+        qk(sc, kst);
+        if (kt < ki0 || kt >= ki1) apply_mask(sc, kt * BN);
+        update_max(sc);
+        moved = false;  // O and l are still zero
+    };
+    if (kw0 == kt0) first_scores(kt0, lds_k0);
 
     // ---- one pipelined step for tile j: S_{j+1} = K_{j+1} Q^T and the weights
     // of tile j, then O += P_j V_j and the row max of tile j+1.  STAGE = (j -
@@ -481,6 +499,9 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
         if (!LAST) {
             if (j + 2 < kt1) load_k(j + 2, k_this);
             load_v(j + 1, v_next);
+        } else {  // this wave's last tile; the workgroup may go on
+            if (j + 2 < kt1) load_k(j + 2, k_this);
+            if (j + 1 < kt1) load_v(j + 1, v_next);
         }
         rescale_if_moved();
         u32x4 p[NCH];
@@ -537,19 +558,34 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
         }
         if (j < j1) step(j, IntTag<0>{}, mask_next_tag, BoolTag<false>{});
     };
+    // a step of the workgroup's loads and barrier only (outside [kw0, kw1))
+    auto idle_step = [&](int j) __attribute__((always_inline)) {
+        const bool st = ((j - kt0) & 1) != 0;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (j + 2 < kt1) load_k(j + 2, st ? lds_k1 : lds_k0);
+        if (j + 1 < kt1) load_v(j + 1, st ? lds_v0 : lds_v1);
+    };
+    for (int j = kt0; j + 1 < kw0; ++j) idle_step(j);
+    if (kw0 > kt0) {  // the step before the wave's first tile: its scores
+        const int j = kw0 - 1;
+        idle_step(j);
+        first_scores(kw0, ((j - kt0) & 1) ? lds_k0 : lds_k1);
+    }
     // iteration j has a mask-free next tile iff ki0 <= j + 1 < ki1
-    const int jl = kt1 - 1;
-    int ja = ki0 - 1 > kt0 ? ki0 - 1 : kt0;
+    const int jl = kw1 - 1;
+    int ja = ki0 - 1 > kw0 ? ki0 - 1 : kw0;
     if (ja > jl) ja = jl;
     int jb = ki1 - 1 < jl ? ki1 - 1 : jl;
     if (jb < ja) jb = ja;
-    run(kt0, ja, BoolTag<true>{});
+    run(kw0, ja, BoolTag<true>{});
     run(ja, jb, BoolTag<false>{});
     run(jb, jl, BoolTag<true>{});
     if ((jl - kt0) & 1)
         step(jl, IntTag<1>{}, BoolTag<false>{}, BoolTag<true>{});
     else
         step(jl, IntTag<0>{}, BoolTag<false>{}, BoolTag<true>{});
+    for (int j = kw1; j < kt1; ++j) idle_step(j);
 
     // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
     // l == 0 only for a row with no allowed key; a NaN l (NaN scores) propagates

@@ -98,6 +98,29 @@ def test_parity_windows(window, causal):
     check_full(1, 700, 2, 128, torch.bfloat16, causal, window, seed=17)
 
 
+@pytest.mark.parametrize("B,H,S", [(2, 10, 1000), (1, 20, 1024)])
+def test_parity_launch_order_blocks(B, H, S):
+    """Causal, with B * H not a multiple of 8: the XCD blocks of the launch
+    order start and end inside heads and hold whole heads between; every
+    element against the oracle."""
+    check_full(B, S, H, 128, torch.bfloat16, True, (-1, -1), seed=1000 * B + H)
+
+
+def test_parity_launch_order_many_workgroups():
+    """5 heads of 16384 causal rows: 640 workgroups, more than the device holds
+    at once, with XCD blocks that split heads; sampled rows of every head."""
+    from types import SimpleNamespace
+
+    w = SimpleNamespace(name="causal_16k_h5", B=1, H=5, S=16384, D=128, dtype=torch.bfloat16,
+                        causal=True, window=(-1, -1), scale=1.0 / math.sqrt(128))
+    q, k, v = make_qkv(w.B, w.S, w.H, w.D, w.dtype, 55)
+    print("run causal 16384 x 5 heads", flush=True)
+    out, lse = gpu_fwd(q, k, v, w.scale, w.causal, w.window)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    rows = [0, 127, 128, 4095, 4096, 8191, 12288, 16255, 16256, 16383]
+    check_sampled_rows(w, q, k, v, out, lse, [(0, h) for h in range(w.H)], rows)
+
+
 @pytest.mark.parametrize("name", ["tiny_fp32", "gpt_causal_2k", "full_4k_d64"])
 @pytest.mark.parametrize("seed", [None, 101, 102])
 def test_parity_named_small_workloads(name, seed):
