@@ -110,6 +110,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--splitkv", type=int, default=-1,
+                    help="time fa_fwd_splitkv with this many K/V parts per Q tile (0 = the "
+                         "library's choice for the device) instead of fa_fwd")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the benchmark, run --steps plain device copies of this many "
                          "MiB (the reference kernel for scaling HBM byte counters)")
@@ -148,9 +151,23 @@ def main() -> int:
     lse = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        fa.flash_attn_fwd(qd, kd, vd, softmax_scale=w.scale, causal=w.causal,
-                          window_size=w.window, out=out, lse=lse, stream=stream)
+    n_splits = None
+    if args.splitkv >= 0:
+        dcode = {torch.float32: fa.FA_DTYPE_FP32, torch.float16: fa.FA_DTYPE_FP16,
+                 torch.bfloat16: fa.FA_DTYPE_BF16}[w.dtype]
+        n_splits = args.splitkv or fa.fa_fwd_splitkv_auto_splits(
+            w.B, w.H, w.S, w.D, int(w.causal), w.window[0], w.window[1], dcode)
+        need = fa.fa_fwd_splitkv_workspace_size(w.B, w.H, w.S, w.D, dcode, n_splits)
+        ws = torch.empty(max(1, (need + 3) // 4), dtype=torch.float32, device=dev)
+
+        def step():
+            fa.flash_attn_fwd_splitkv(qd, kd, vd, softmax_scale=w.scale, causal=w.causal,
+                                      window_size=w.window, n_splits=n_splits, out=out, lse=lse,
+                                      workspace=ws, stream=stream)
+    else:
+        def step():
+            fa.flash_attn_fwd(qd, kd, vd, softmax_scale=w.scale, causal=w.causal,
+                              window_size=w.window, out=out, lse=lse, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -213,7 +230,9 @@ def main() -> int:
         "pct_of_peak": 100.0 * tflops / peak,
         "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
                    "causal": w.causal, "window": list(w.window), "S_eff": s_eff,
-                   "flops_per_step": flops, "parallelism": "single GPU"},
+                   "flops_per_step": flops, "parallelism": "single GPU",
+                   "entry": "fa_fwd" if n_splits is None else "fa_fwd_splitkv",
+                   **({} if n_splits is None else {"n_splits": n_splits})},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

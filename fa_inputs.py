@@ -53,6 +53,9 @@ WORKLOADS = {
     "window_8k": Workload("window_8k", 2, 16, 8192, 128, torch.bfloat16, False, (128, 128), 4),
     "causal_16k": Workload("causal_16k", 1, 16, 16384, 128, torch.bfloat16, True, (-1, -1), 5),
     "causal_32k": Workload("causal_32k", 1, 16, 32768, 128, torch.bfloat16, True, (-1, -1), 6),
+    # one GPU's share of causal_16k split by heads over 8 GPUs (2 of 16 heads):
+    # a grid of one workgroup per compute unit, the case split-KV is for
+    "causal_16k_h2": Workload("causal_16k_h2", 1, 2, 16384, 128, torch.bfloat16, True, (-1, -1), 7),
 }
 
 

@@ -51,8 +51,14 @@ typedef enum {
     FA_ERR_SCALE = -6,    /* scale NaN, infinite or negative */
     FA_ERR_ALIGN = -7,    /* q, k, v or out not 16-byte aligned, or lse not 4-byte aligned */
     FA_ERR_ALIAS = -8,    /* out or lse overlaps an input, or out overlaps lse */
-    FA_ERR_HIP = -9       /* the kernel launch failed (hipGetLastError) */
+    FA_ERR_HIP = -9,      /* the kernel launch failed (hipGetLastError) */
+    FA_ERR_WORKSPACE = -10, /* fa_fwd_splitkv: workspace NULL, too small, not 16-byte
+                               aligned, or overlapping an input or output */
+    FA_ERR_SPLITS = -11   /* fa_fwd_splitkv: n_splits outside [1, FA_MAX_SPLITS] */
 } fa_status_t;
+
+/* The most K/V parts per Q tile fa_fwd_splitkv takes. */
+#define FA_MAX_SPLITS 16
 
 /*
  * fa_fwd -- one fused attention forward over all (b, h).
@@ -132,6 +138,62 @@ int fa_fwd_tile_schedule(int64_t S, int64_t D, int dtype, int causal, int64_t wi
 int fa_fwd_workgroup_tile(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int causal,
                           int64_t window_left, int64_t window_right, int64_t wg, int64_t* bh,
                           int64_t* q_tile);
+
+/*
+ * fa_fwd_splitkv -- fa_fwd with the K/V tiles of every Q tile cut into
+ * n_splits contiguous parts that separate workgroups process at the same
+ * time.  Each workgroup writes the partial (O, LSE) of its part, in fp32, to
+ * `workspace`; a second kernel then merges a row's parts with the log-domain
+ * rule of the online softmax ([FA] section 1 item 3; [V2] section 二.1 step 2):
+ * LSE = log-sum-exp of the parts' LSEs, O = the parts' O weighted by
+ * exp(LSE_p - LSE).  The result equals fa_fwd's up to rounding.  It pays off
+ * when fa_fwd's grid cannot fill the device or one Q tile's long row of K/V
+ * tiles sets the time (short sequences, few heads, causal masks): the longest
+ * chain of K/V tiles one workgroup walks shrinks by n_splits.
+ *
+ * Arguments and results as fa_fwd, plus:
+ * n_splits         parts per Q tile, 1 .. FA_MAX_SPLITS.  1 runs fa_fwd itself.
+ *                  A Q tile with fewer K/V tiles than parts leaves some parts
+ *                  empty (they add nothing).  fp32 inputs always run in one
+ *                  part.
+ * workspace        device buffer of at least fa_fwd_splitkv_workspace_size
+ *                  bytes, 16-byte aligned, not overlapping q, k, v, out or lse;
+ *                  owned by the caller, its contents on return unspecified.
+ *                  May be NULL when that size is 0.
+ * workspace_bytes  its size in bytes.
+ * Validation happens before any HIP call, as for fa_fwd.  Enqueues two
+ * kernels on `stream` (one when no split is used) and returns without
+ * synchronising.  Returns FA_OK or a negative fa_status_t.
+ */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
+                   int64_t H, int64_t S, int64_t D, float scale, int causal, int64_t window_left,
+                   int64_t window_right, int dtype, int64_t n_splits, void* workspace,
+                   int64_t workspace_bytes, void* stream);
+
+/*
+ * fa_fwd_splitkv_workspace_size -- the workspace fa_fwd_splitkv needs, in
+ * *bytes: n_splits * B * H * S * (D + 1) * 4 (the fp32 partial O and LSE of
+ * every part), or 0 when n_splits is 1 or dtype is FA_DTYPE_FP32.  Pure
+ * function, no HIP call.  Returns FA_OK, FA_ERR_NULL, FA_ERR_SPLITS, or the
+ * status fa_fwd_check_args gives for the shape, head dimension and dtype.
+ */
+int fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t S, int64_t D, int dtype,
+                                  int64_t n_splits, int64_t* bytes);
+
+/*
+ * fa_fwd_splitkv_auto_splits -- a part count for this problem on the current
+ * device: 1 when fa_fwd's own grid has at least two workgroups per compute
+ * unit (then the fp32 partials and the merge cost about what the split saves),
+ * else enough parts for four workgroups per unit, at most 8 and at most the
+ * K/V tile count of the longest Q tile; 1 for fp32 inputs or when the device
+ * cannot be queried.
+ * Queries the device (HIP calls) but launches nothing.  Returns FA_OK or the
+ * status fa_fwd_check_args gives for the problem arguments (pointers are not
+ * needed).
+ */
+int fa_fwd_splitkv_auto_splits(int64_t B, int64_t H, int64_t S, int64_t D, int causal,
+                               int64_t window_left, int64_t window_right, int dtype,
+                               int64_t* n_splits);
 
 #ifdef __cplusplus
 }

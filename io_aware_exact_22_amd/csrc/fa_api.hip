@@ -68,6 +68,10 @@ FA_API const char* fa_status_string(int status) {
     case FA_ERR_ALIGN: return "q, k, v, out must be 16-byte aligned and lse 4-byte aligned";
     case FA_ERR_ALIAS: return "out and lse must not overlap the inputs or each other";
     case FA_ERR_HIP: return "the HIP kernel launch failed";
+    case FA_ERR_WORKSPACE:
+        return "the split-KV workspace is NULL, too small, not 16-byte aligned or overlaps an "
+               "input or output";
+    case FA_ERR_SPLITS: return "n_splits must be in [1, FA_MAX_SPLITS]";
     default: return "unknown status";
     }
 }
@@ -92,12 +96,12 @@ FA_API int fa_fwd_check_args(const void* q, const void* k, const void* v, const 
     return FA_OK;
 }
 
-FA_API int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
-                  int64_t H, int64_t S, int64_t D, float scale, int causal, int64_t window_left,
-                  int64_t window_right, int dtype, void* stream) {
-    const int rc = fa_fwd_check_args(q, k, v, out, lse, B, H, S, D, scale, causal, window_left,
-                                     window_right, dtype);
-    if (rc != FA_OK) return rc;
+namespace {
+
+// Launch arguments of a validated problem (pointers may be NULL for queries).
+fa::LaunchArgs make_args(const void* q, const void* k, const void* v, void* out, float* lse,
+                         int64_t B, int64_t H, int64_t S, int64_t D, float scale, int causal,
+                         int64_t window_left, int64_t window_right, int dtype, void* stream) {
     fa::LaunchArgs a;
     a.q = q;
     a.k = k;
@@ -120,6 +124,92 @@ FA_API int fa_fwd(const void* q, const void* k, const void* v, void* out, float*
     a.wr = window_right >= S ? -1 : window_right;
     a.dtype = dtype;
     a.stream = (hipStream_t)stream;
+    return a;
+}
+
+// Bytes of fp32 partial O and LSE for n_splits parts (0 when nothing is split).
+int64_t split_workspace_bytes(int64_t B, int64_t H, int64_t S, int64_t D, int dtype,
+                              int64_t n_splits) {
+    if (n_splits <= 1 || dtype == FA_DTYPE_FP32) return 0;
+    return n_splits * B * H * S * (D + 1) * 4;
+}
+
+}  // namespace
+
+FA_API int fa_fwd(const void* q, const void* k, const void* v, void* out, float* lse, int64_t B,
+                  int64_t H, int64_t S, int64_t D, float scale, int causal, int64_t window_left,
+                  int64_t window_right, int dtype, void* stream) {
+    const int rc = fa_fwd_check_args(q, k, v, out, lse, B, H, S, D, scale, causal, window_left,
+                                     window_right, dtype);
+    if (rc != FA_OK) return rc;
+    const fa::LaunchArgs a = make_args(q, k, v, out, lse, B, H, S, D, scale, causal, window_left,
+                                       window_right, dtype, stream);
+    const hipError_t e = fa::launch_fwd(a);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+FA_API int fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t S, int64_t D, int dtype,
+                                         int64_t n_splits, int64_t* bytes) {
+    if (!bytes) return FA_ERR_NULL;
+    int64_t nbytes, lbytes;
+    const int rc = check_problem(B, H, S, D, 0, -1, -1, dtype, &nbytes, &lbytes);
+    if (rc != FA_OK) return rc;
+    if (n_splits < 1 || n_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
+    // n_splits * (B*H*S) * (D + 1) * 4 fits: B*H*S*D*e is checked to fit int64, and
+    // n_splits * 4 * (D + 1) / e <= 16 * 4 * 129 / 2
+    int64_t rows, t, r;
+    if (!mul_ok(B, H, &t) || !mul_ok(t, S, &rows) || !mul_ok(rows, n_splits * (D + 1) * 4, &r))
+        return FA_ERR_SHAPE;
+    *bytes = split_workspace_bytes(B, H, S, D, dtype, n_splits);
+    return FA_OK;
+}
+
+FA_API int fa_fwd_splitkv_auto_splits(int64_t B, int64_t H, int64_t S, int64_t D, int causal,
+                                      int64_t window_left, int64_t window_right, int dtype,
+                                      int64_t* n_splits) {
+    if (!n_splits) return FA_ERR_NULL;
+    int64_t nbytes, lbytes;
+    const int rc = check_problem(B, H, S, D, causal, window_left, window_right, dtype, &nbytes,
+                                 &lbytes);
+    if (rc != FA_OK) return rc;
+    const fa::LaunchArgs a = make_args(nullptr, nullptr, nullptr, nullptr, nullptr, B, H, S, D, 1.f,
+                                       causal, window_left, window_right, dtype, nullptr);
+    *n_splits = fa::auto_splits(a);
+    return FA_OK;
+}
+
+FA_API int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* out, float* lse,
+                          int64_t B, int64_t H, int64_t S, int64_t D, float scale, int causal,
+                          int64_t window_left, int64_t window_right, int dtype, int64_t n_splits,
+                          void* workspace, int64_t workspace_bytes, void* stream) {
+    int rc = fa_fwd_check_args(q, k, v, out, lse, B, H, S, D, scale, causal, window_left,
+                               window_right, dtype);
+    if (rc != FA_OK) return rc;
+    int64_t need = 0;
+    rc = fa_fwd_splitkv_workspace_size(B, H, S, D, dtype, n_splits, &need);
+    if (rc != FA_OK) return rc;
+    fa::LaunchArgs a = make_args(q, k, v, out, lse, B, H, S, D, scale, causal, window_left,
+                                 window_right, dtype, stream);
+    if (need > 0) {
+        // the split grid: Q tiles x parts workgroups of 256 threads
+        const int64_t bm = fa::q_tile_rows(dtype, D, S, a.wl, a.wr);
+        int64_t n_wg;
+        if (!mul_ok(B * H, (S + bm - 1) / bm, &n_wg) || !mul_ok(n_wg, n_splits, &n_wg) ||
+            n_wg > (int64_t)(UINT32_MAX / 256))
+            return FA_ERR_SHAPE;
+        if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15u))
+            return FA_ERR_WORKSPACE;
+        int64_t nbytes = 0, lbytes = 0;
+        (void)check_problem(B, H, S, D, causal, window_left, window_right, dtype, &nbytes, &lbytes);
+        const void* others[5] = {q, k, v, out, lse};
+        const int64_t sizes[5] = {nbytes, nbytes, nbytes, nbytes, lbytes};
+        for (int i = 0; i < 5; ++i)
+            if (overlaps(workspace, need, others[i], sizes[i])) return FA_ERR_WORKSPACE;
+        const int64_t rows = B * H * S;
+        a.n_splits = (int)n_splits;
+        a.part_o = (float*)workspace;
+        a.part_lse = (float*)workspace + n_splits * rows * D;
+    }
     const hipError_t e = fa::launch_fwd(a);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

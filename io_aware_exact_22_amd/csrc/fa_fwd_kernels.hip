@@ -194,10 +194,16 @@ __device__ inline void dma_matrix(__amdgpu_buffer_rsrc_t r, unsigned char* wave_
     if (N > 3) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, l, 16, voff[N > 3 ? 3 : 0], 0, 3072, 0);
 }
 
-template <typename T, int D, int NW, int BN_>
+// SPLIT: the K/V tiles of each Q tile are cut into n_splits contiguous parts,
+// one workgroup per (Q tile, part); each writes the partial (O, LSE) of its
+// part, in fp32, to part_o [n_splits, B, H, S, D] and part_lse
+// [n_splits, B, H, S], for the merge kernel below (the log-domain merge of the
+// online softmax, applied once across parts).
+template <typename T, int D, int NW, int BN_, bool SPLIT>
 __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ out,
-    float* __restrict__ lse, int B, int H, int S, float c, int causal, int wl, int wr, int n_qt) {
+    float* __restrict__ lse, int B, int H, int S, float c, int causal, int wl, int wr, int n_qt,
+    int n_splits, float* __restrict__ part_o, float* __restrict__ part_lse) {
     typedef Tile<D, NW, BN_> L;
     constexpr int BN = L::BN;
     constexpr int BM = L::BM;
@@ -221,9 +227,14 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
     const int hh = lane >> 5;   // wave half
     const int ql = lane & 31;   // query row of this lane within the wave
 
-    // ---- workgroup -> (b, h, q tile); causal: heaviest Q tiles first per XCD
-    uint32_t bh, qt32;
-    workgroup_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt, causal != 0, &bh, &qt32);
+    // ---- workgroup -> (b, h, q tile[, part]); causal: heaviest Q tiles first per XCD
+    uint32_t bh, qt32, wg = blockIdx.x;
+    int sp = 0;  // K/V part (SPLIT)
+    if (SPLIT) {
+        sp = (int)(wg % (uint32_t)n_splits);
+        wg /= (uint32_t)n_splits;
+    }
+    workgroup_tile(wg, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt, causal != 0, &bh, &qt32);
     const int qt = (int)qt32;
     const int bb = (int)(bh / (uint32_t)H), h = (int)(bh % (uint32_t)H);
 
@@ -233,6 +244,12 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
     {
         int64_t a0, a1, b0, b1;
         q_tile_kv_range(ms, qt, BM, BN, &a0, &a1);
+        if (SPLIT) {  // part sp of [a0, a1): near-equal tile counts, possibly empty
+            const int64_t len = a1 - a0;
+            const int64_t p0 = a0 + len * sp / n_splits, p1 = a0 + len * (sp + 1) / n_splits;
+            a0 = p0;
+            a1 = p1;
+        }
         q_tile_interior_range(ms, (int64_t)qt * BM, BM, BN, a0, a1, &b0, &b1);
         kt0 = (int)a0;
         kt1 = (int)a1;
@@ -245,6 +262,20 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
     const int q0 = qt * BM;
     const int qw0 = q0 + wave * kWaveRows;  // first row of this wave
     const int qrow = qw0 + ql;              // this lane's query row
+    // SPLIT: this part's partial output rows
+    const int64_t part_row = ((int64_t)sp * B * H + bh) * S + qrow;
+    if (SPLIT && kt0 == kt1) {  // an empty part (fewer tiles than parts): no keys
+        if (qrow < S) {
+            if (hh == 0) part_lse[part_row] = kNegInf;
+#pragma unroll
+            for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<f32x4*>(part_o + part_row * D + 32 * d + 8 * g + 4 * hh) =
+                        f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        return;
+    }
 
     // allowed keys of this lane's row: [key_lo, key_lo + key_w] (rows past S
     // are padding: any finite range will do, their results are not stored)
@@ -471,6 +502,10 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
         kw0 = (int)(lo / BN) > kt0 ? (int)(lo / BN) : kt0;
         kw1 = (int)(hi / BN) + 1 < kt1 ? (int)(hi / BN) + 1 : kt1;
     }
+    if (SPLIT && kw0 >= kw1) {  // no allowed key of these rows in this part:
+        kw0 = kt0;              // run it all, fully masked (l = 0, O = 0)
+        kw1 = kt1;
+    }
     kw0 = __builtin_amdgcn_readfirstlane(kw0);
     kw1 = __builtin_amdgcn_readfirstlane(kw1);
     auto first_scores = [&](int kt, unsigned char* kst) __attribute__((always_inline)) {
@@ -591,12 +626,22 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
     // l == 0 only for a row with no allowed key; a NaN l (NaN scores) propagates
     const float l_tot = halves_sum(l_run);
     const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
-    if (qrow < S && hh == 0) {
-        const float m_fin = (m_run == kNegInf) ? 0.f : m_run;
-        const float lse_v =
-            (l_tot == 0.f) ? kNegInf : 0.69314718055994531f * (m_fin + __log2f(l_tot));
-        lse[((int64_t)bb * H + h) * S + qrow] = lse_v;
+    const float m_fin = (m_run == kNegInf) ? 0.f : m_run;
+    const float lse_v = (l_tot == 0.f) ? kNegInf : 0.69314718055994531f * (m_fin + __log2f(l_tot));
+    if (SPLIT) {  // the part's normalised O and its LSE, in fp32
+        if (qrow < S) {
+            if (hh == 0) part_lse[part_row] = lse_v;
+#pragma unroll
+            for (int d = 0; d < DB; ++d)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    *reinterpret_cast<f32x4*>(part_o + part_row * D + 32 * d + 8 * g + 4 * hh) =
+                        f32x4{o[d][4 * g] * inv, o[d][4 * g + 1] * inv, o[d][4 * g + 2] * inv,
+                              o[d][4 * g + 3] * inv};
+        }
+        return;
     }
+    if (qrow < S && hh == 0) lse[((int64_t)bb * H + h) * S + qrow] = lse_v;
     // O leaves through LDS so that the global stores run along whole rows: a
     // lane holds one row's columns 32d + 8g + 4*hh .. +3, so it writes them
     // into the wave's 32 x D staging tile (16-byte chunk c of row r stored at
@@ -630,6 +675,68 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
             if (qw0 + r < S) *reinterpret_cast<u32x4*>(orow + (int64_t)(qw0 + r) * row_stride) = x;
         }
     }
+}
+
+// ---------------------------------------------------------------- part merge
+// A row's O and LSE from the partial (O_p, LSE_p) of its K/V parts: with
+// M = max_p LSE_p and w_p = exp(LSE_p - M), LSE = M + ln(sum_p w_p) and
+// O = sum_p w_p O_p / sum_p w_p -- the online softmax's rescale-and-add
+// ([FA] section 1 item 3; [V2] section 二.1 step 2), applied once across the
+// parts.  A part with no allowed key has LSE_p = -inf and weight 0.  A NaN LSE
+// in any part makes the row NaN, as it would be without the split.
+template <typename T> __device__ inline void store4(T* p, f32x4 x);
+template <> __device__ inline void store4<float>(float* p, f32x4 x) {
+    *reinterpret_cast<f32x4*>(p) = x;
+}
+template <> __device__ inline void store4<__bf16>(__bf16* p, f32x4 x) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{Mfma<__bf16>::pack2(x[0], x[1]), Mfma<__bf16>::pack2(x[2], x[3])};
+}
+template <> __device__ inline void store4<_Float16>(_Float16* p, f32x4 x) {
+    *reinterpret_cast<u32x2*>(p) =
+        u32x2{Mfma<_Float16>::pack2(x[0], x[1]), Mfma<_Float16>::pack2(x[2], x[3])};
+}
+
+constexpr int kMergeThreads = 256;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kMergeThreads) void fa_merge_parts_kernel(
+    const float* __restrict__ part_o, const float* __restrict__ part_lse, T* __restrict__ out,
+    float* __restrict__ lse, int B, int H, int S, int n_splits) {
+    constexpr int TPR = D / 4;                  // threads per row, 4 columns each
+    constexpr int RPB = kMergeThreads / TPR;    // rows per workgroup
+    const int64_t R = (int64_t)B * H * S;       // rows, ordered (b * H + h) * S + s
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+    const int c4 = threadIdx.x % TPR;
+    if (row >= R) return;
+    float m = kNegInf;
+    bool nan = false;
+    for (int p = 0; p < n_splits; ++p) {
+        const float l = part_lse[p * R + row];
+        nan |= l != l;
+        m = fmaxf(m, l);
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (m != kNegInf) {
+        for (int p = 0; p < n_splits; ++p) {
+            const float l = part_lse[p * R + row];
+            const float w = (l == kNegInf) ? 0.f : expf(l - m);
+            const f32x4 x = *reinterpret_cast<const f32x4*>(part_o + (p * R + row) * D + 4 * c4);
+            acc += w * x;
+            wsum += w;
+        }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    f32x4 o = acc * inv;
+    float lv = (m == kNegInf) ? kNegInf : m + logf(wsum);
+    if (nan) {
+        o = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+        lv = __builtin_nanf("");
+    }
+    const int64_t bh = row / S, srow = row - bh * S;
+    const int64_t b = bh / H, h = bh - b * H;
+    store4<T>(out + ((b * S + srow) * H + h) * D + 4 * c4, o);
+    if (c4 == 0) lse[row] = lv;
 }
 
 // ---------------------------------------------------------------- fp32
@@ -774,11 +881,28 @@ static hipError_t launch_mfma_cfg(const LaunchArgs& a) {
     constexpr int BM = Tile<D, NW, BN>::BM;
     const int n_qt = (int)((a.S + BM - 1) / BM);
     const int64_t n_wg = a.B * a.H * n_qt;
-    hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN>), dim3((unsigned)n_wg), dim3(NW * 64), 0,
-                       a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse,
-                       (int)a.B, (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt);
+    if (a.n_splits <= 1) {
+        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false>), dim3((unsigned)n_wg),
+                           dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
+                           (T*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl,
+                           (int)a.wr, n_qt, 1, nullptr, nullptr);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, true>), dim3((unsigned)(n_wg * a.n_splits)),
+                       dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
+                       (T*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl,
+                       (int)a.wr, n_qt, a.n_splits, a.part_o, a.part_lse);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr int RPB = kMergeThreads / (D / 4);
+    const int64_t rows = a.B * a.H * a.S;
+    hipLaunchKernelGGL((fa_merge_parts_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)),
+                       dim3(kMergeThreads), 0, a.stream, (const float*)a.part_o,
+                       (const float*)a.part_lse, (T*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S,
+                       a.n_splits);
     return hipGetLastError();
 }
+
 
 // bf16 / fp16: 4 waves, 128-row Q tiles, 64-key K/V tiles
 constexpr int kMfmaWaves = 4, kMfmaKeys = 64;
@@ -788,6 +912,8 @@ static hipError_t launch_mfma(const LaunchArgs& a) {
     return launch_mfma_cfg<T, D, kMfmaWaves, kMfmaKeys>(a);
 }
 
+// fp32 inputs always run in one part (n_splits is ignored): the fp32 kernel
+// has no split path.
 template <int D>
 static hipError_t launch_fp32(const LaunchArgs& a) {
     const int n_qt = (int)((a.S + kBM32 - 1) / kBM32);
@@ -803,6 +929,50 @@ hipError_t launch_fwd(const LaunchArgs& a) {
     case kDtypeBf16: return a.D == 64 ? launch_mfma<__bf16, 64>(a) : launch_mfma<__bf16, 128>(a);
     case kDtypeFp16: return a.D == 64 ? launch_mfma<_Float16, 64>(a) : launch_mfma<_Float16, 128>(a);
     default: return a.D == 64 ? launch_fp32<64>(a) : launch_fp32<128>(a);
+    }
+}
+
+// K/V parts per Q tile for the split launch.  Splitting pays only when the
+// unsplit grid leaves compute units short of work: the fp32 partials and the
+// merge pass cost about as much as a 2-workgroups-per-CU grid gains from
+// shorter chains (measured: the 2K causal workload, 512 workgroups on 256
+// CUs, is slower split; 16K causal rows of 2 heads, 256 workgroups, are 20%
+// faster in 4 parts).  So: 1 when the grid has at least two workgroups per
+// compute unit, else enough parts for four per unit, at most kMaxAutoSplits
+// and at most the K/V tile count of the longest Q tile; 1 when the device
+// cannot be queried.
+constexpr int kMaxAutoSplits = 8;
+
+template <typename T, int D>
+static int auto_splits_cfg(const LaunchArgs& a) {
+    constexpr int BM = Tile<D, kMfmaWaves, kMfmaKeys>::BM;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 1;
+    }
+    const int64_t n_qt = (a.S + BM - 1) / BM, tiles = a.B * a.H * n_qt;
+    const MaskSpec m{a.S, a.causal, a.wl, a.wr};
+    int64_t longest = 1;
+    for (int64_t t = 0; t < n_qt; ++t) {
+        int64_t t0, t1;
+        q_tile_kv_range(m, t, BM, kMfmaKeys, &t0, &t1);
+        if (t1 - t0 > longest) longest = t1 - t0;
+    }
+    if (tiles >= 2 * (int64_t)cus) return 1;
+    int64_t ns = (4 * (int64_t)cus + tiles - 1) / tiles;
+    if (ns > kMaxAutoSplits) ns = kMaxAutoSplits;
+    if (ns > longest) ns = longest;
+    return ns < 1 ? 1 : (int)ns;
+}
+
+int auto_splits(const LaunchArgs& a) {
+    switch (a.dtype) {
+    case kDtypeBf16: return a.D == 64 ? auto_splits_cfg<__bf16, 64>(a) : auto_splits_cfg<__bf16, 128>(a);
+    case kDtypeFp16:
+        return a.D == 64 ? auto_splits_cfg<_Float16, 64>(a) : auto_splits_cfg<_Float16, 128>(a);
+    default: return 1;  // fp32 inputs run in one part
     }
 }
 

@@ -23,10 +23,20 @@ struct LaunchArgs {
     int64_t wl, wr;  // already clamped to [-1, S]
     int dtype;
     hipStream_t stream;
+    // split launch (bf16 / fp16 only): > 1 = K/V parts per Q tile, partial
+    // results in part_o [n_splits, B, H, S, D] and part_lse [n_splits, B, H, S]
+    // (fp32), merged into out / lse by a second kernel
+    int n_splits = 1;
+    float* part_o = nullptr;
+    float* part_lse = nullptr;
 };
 
-// Enqueues the forward kernel for validated arguments.
+// Enqueues the forward kernel (and, for a split launch, the merge kernel) for
+// validated arguments.
 hipError_t launch_fwd(const LaunchArgs& a);
+// K/V parts per Q tile that fill the current device for this problem (1 for
+// fp32 inputs, or when the device cannot be queried).
+int auto_splits(const LaunchArgs& a);
 // Tile shape the kernels use: Q rows per workgroup (it depends on the
 // configuration the launcher picks for S and the window; wl, wr already
 // clamped to [-1, S)), keys per K/V tile.

@@ -1,7 +1,9 @@
 """ctypes binding of libfa_mi355x (declared in include/fa_mi355x.h).
 
 Same names as the C ABI: ``fa_fwd``, ``fa_fwd_check_args``,
-``fa_status_string``, ``fa_fwd_tile_schedule``, ``fa_fwd_workgroup_tile``; plus ``flash_attn_fwd``, the
+``fa_status_string``, ``fa_fwd_tile_schedule``, ``fa_fwd_workgroup_tile``, ``fa_fwd_splitkv``,
+``fa_fwd_splitkv_workspace_size``, ``fa_fwd_splitkv_auto_splits``; plus ``flash_attn_fwd`` (and
+``flash_attn_fwd_splitkv``), the
 tensor-level call that mirrors the pages' ``flash_attention(q, k, v,
 softmax_scale=None, causal=..., window_size=(-1, -1))`` argument list
 ("FlashAttention技术解析：加速GPT训练的核心优化", section 2.2).  This module only
@@ -17,6 +19,7 @@ import threading
 FA_DTYPE_FP32 = 0
 FA_DTYPE_FP16 = 1
 FA_DTYPE_BF16 = 2
+FA_MAX_SPLITS = 16
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libfa_mi355x.so")
@@ -66,6 +69,13 @@ def _load():
         lib.fa_fwd_workgroup_tile.argtypes = [i64, i64, i64, i64, cint, cint, i64, i64, i64, p64,
                                               p64]
         lib.fa_fwd_workgroup_tile.restype = cint
+        lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, cint,
+                                       i64, i64, cint, i64, vp, i64, vp]
+        lib.fa_fwd_splitkv.restype = cint
+        lib.fa_fwd_splitkv_workspace_size.argtypes = [i64, i64, i64, i64, cint, i64, p64]
+        lib.fa_fwd_splitkv_workspace_size.restype = cint
+        lib.fa_fwd_splitkv_auto_splits.argtypes = [i64, i64, i64, i64, cint, i64, i64, cint, p64]
+        lib.fa_fwd_splitkv_auto_splits.restype = cint
         _lib = lib
         return lib
 
@@ -120,6 +130,34 @@ def fa_fwd_workgroup_tile(B: int, H: int, S: int, D: int, dtype: int, causal: in
     return bh.value, qt.value
 
 
+def fa_fwd_splitkv(q: int, k: int, v: int, out: int, lse: int, B: int, H: int, S: int, D: int,
+                   scale: float, causal: int, window_left: int, window_right: int, dtype: int,
+                   n_splits: int, workspace: int, workspace_bytes: int, stream: int | None) -> int:
+    """The split-KV C entry point with raw device pointers (ints); returns the status."""
+    return _load().fa_fwd_splitkv(q, k, v, out, lse, B, H, S, D, scale, causal, window_left,
+                                  window_right, dtype, n_splits, workspace, workspace_bytes,
+                                  stream)
+
+
+def fa_fwd_splitkv_workspace_size(B: int, H: int, S: int, D: int, dtype: int,
+                                  n_splits: int) -> int:
+    n = ctypes.c_int64()
+    rc = _load().fa_fwd_splitkv_workspace_size(B, H, S, D, dtype, n_splits, ctypes.byref(n))
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_splitkv_workspace_size")
+    return n.value
+
+
+def fa_fwd_splitkv_auto_splits(B: int, H: int, S: int, D: int, causal: int, window_left: int,
+                               window_right: int, dtype: int) -> int:
+    n = ctypes.c_int64()
+    rc = _load().fa_fwd_splitkv_auto_splits(B, H, S, D, causal, window_left, window_right, dtype,
+                                            ctypes.byref(n))
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_splitkv_auto_splits")
+    return n.value
+
+
 # ------------------------------------------------------------------ tensor call
 def _dtype_code(t) -> int:
     import torch
@@ -172,4 +210,51 @@ def flash_attn_fwd(q, k, v, softmax_scale: float | None = None, causal: bool = F
                     S, D, scale, int(bool(causal)), wl, wr, dtype, st.cuda_stream)
     if rc != 0:
         raise FaError(rc, "fa_fwd")
+    return out, lse
+
+
+def flash_attn_fwd_splitkv(q, k, v, softmax_scale: float | None = None, causal: bool = False,
+                           window_size=(-1, -1), n_splits: int = 0, out=None, lse=None,
+                           workspace=None, stream=None):
+    """flash_attn_fwd with the K/V tiles of each Q tile split into ``n_splits``
+    parts (0 = the library's choice for the current device) and merged.  The
+    fp32 workspace is a torch tensor of at least the size
+    fa_fwd_splitkv_workspace_size reports (allocated here when None).
+    Returns (out, lse) like flash_attn_fwd."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise TypeError(f"{name} must be a GPU tensor")
+        if t.dim() != 4 or t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must share shape [B, S, H, D], dtype and device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, S, H, D]")
+    B, S, H, D = q.shape
+    dtype = _dtype_code(q)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    wl, wr = (int(x) for x in window_size)
+    with torch.cuda.device(q.device):
+        if n_splits == 0:
+            n_splits = fa_fwd_splitkv_auto_splits(B, H, S, D, int(bool(causal)), wl, wr, dtype)
+        need = fa_fwd_splitkv_workspace_size(B, H, S, D, dtype, n_splits)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 tensor [B, H, S]")
+    if workspace is None and need > 0:
+        workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        rc = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), B, H, S, D, scale, int(bool(causal)), wl, wr, dtype,
+                            n_splits, ws_ptr or None, ws_bytes, st.cuda_stream)
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_splitkv")
     return out, lse

@@ -25,7 +25,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_check_args", "fa_status_string", "fa_fwd_tile_schedule",
-                          "fa_fwd_workgroup_tile"}
+                          "fa_fwd_workgroup_tile", "fa_fwd_splitkv",
+                          "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv_auto_splits"}
     lib = ctypes.CDLL(fa.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in range(0, -10, -1):
+    for st in range(0, -12, -1):
         s = fa.fa_status_string(st)
         assert s and s != "unknown status"
     assert fa.fa_status_string(-99) == "unknown status"
@@ -83,6 +84,44 @@ def test_fa_fwd_rejects_before_any_hip_call():
     assert rc == -3
     rc = fa.fa_fwd(0, K, V, OUT, LSE, 1, 1, 128, 64, 0.1, 0, -1, -1, fa.FA_DTYPE_BF16, None)
     assert rc == -1
+
+
+@pytest.mark.parametrize("B,H,S,D,dtype,ns", [(2, 16, 2048, 64, fa.FA_DTYPE_BF16, 3),
+                                                (1, 2, 16384, 128, fa.FA_DTYPE_BF16, 4),
+                                                (3, 5, 389, 128, fa.FA_DTYPE_FP16, 16)])
+def test_splitkv_workspace_size(B, H, S, D, dtype, ns):
+    """fp32 partial O and LSE of every part: ns * B * H * S * (D + 1) * 4 bytes;
+    nothing for one part or fp32 inputs."""
+    assert fa.fa_fwd_splitkv_workspace_size(B, H, S, D, dtype, ns) == ns * B * H * S * (D + 1) * 4
+    assert fa.fa_fwd_splitkv_workspace_size(B, H, S, D, dtype, 1) == 0
+    assert fa.fa_fwd_splitkv_workspace_size(B, H, S, D, fa.FA_DTYPE_FP32, ns) == 0
+    for bad in (0, -1, fa.FA_MAX_SPLITS + 1):
+        with pytest.raises(fa.FaError) as e:
+            fa.fa_fwd_splitkv_workspace_size(B, H, S, D, dtype, bad)
+        assert e.value.status == -11
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_fwd_splitkv_workspace_size(B, H, S, 96, dtype, ns)
+    assert e.value.status == -3
+
+
+WS = 6 << 32  # a fake, aligned workspace address disjoint from the tensors above
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"ns": 2, "ws": 0}, -10), ({"ns": 2, "wsb": 100}, -10), ({"ns": 2, "ws": WS + 8}, -10),
+    ({"ns": 2, "ws": Q}, -10), ({"ns": 2, "ws": LSE - 64}, -10),
+    ({"ns": 0}, -11), ({"ns": 17}, -11), ({"ns": -3}, -11),
+    ({"ns": 2, "D": 96}, -3), ({"ns": 2, "q": 0}, -1), ({"ns": 2, "out": Q}, -8),
+    ({"ns": 2, "dtype": 7}, -5),
+])
+def test_splitkv_rejects_before_any_hip_call(kw, status):
+    """Invalid arguments return their status without touching the GPU."""
+    a = dict(GOOD, ns=2, ws=WS, wsb=1 << 40)
+    a.update(kw)
+    rc = fa.fa_fwd_splitkv(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["S"],
+                           a["D"], a["scale"], a["causal"], a["window_left"], a["window_right"],
+                           a["dtype"], a["ns"], a["ws"] or None, a["wsb"], None)
+    assert rc == status
 
 
 def allowed(i, j, causal, wl, wr):

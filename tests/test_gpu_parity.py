@@ -287,3 +287,102 @@ def test_raw_c_abi_call():
     assert rc == -6
     torch.cuda.synchronize()
     assert (out == 1.0).all()
+
+
+# ---------------------------------------------------------------- split-KV
+def gpu_fwd_splitkv(q, k, v, scale, causal, window, n_splits):
+    import io_aware_exact_22_amd as fa
+
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    out, lse = fa.flash_attn_fwd_splitkv(qd, kd, vd, softmax_scale=scale, causal=causal,
+                                         window_size=window, n_splits=n_splits)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (False, (128, 128)),
+                                           (True, (100, -1)), (False, (33, 7))])
+@pytest.mark.parametrize("n_splits", [2, 3])
+def test_splitkv_parity(dtype, D, causal, window, n_splits):
+    """fa_fwd_splitkv against the oracle, every element: ragged S, several
+    heads and batches, each mask mode."""
+    q, k, v = make_qkv(2, 389, 3, D, dtype, 29)
+    scale = 1.0 / math.sqrt(D)
+    what = f"splitkv x{n_splits} D{D} {dtype} causal={causal} window={window}"
+    print("run", what, flush=True)
+    out, lse = gpu_fwd_splitkv(q, k, v, scale, causal, window, n_splits)
+    ref_out, ref_lse = oracle.fwd(q, k, v, scale, causal, window)
+    assert_close(out, lse, ref_out, ref_lse, dtype, what)
+
+
+@pytest.mark.parametrize("S,n_splits", [(100, 4), (130, 16), (1, 2), (4097, 5), (2048, 16)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_splitkv_more_parts_than_tiles(S, n_splits, causal):
+    """More parts than a Q tile has K/V tiles (empty parts), and long rows cut
+    into many parts."""
+    q, k, v = make_qkv(1, S, 2, 128, torch.bfloat16, S + n_splits)
+    print(f"run splitkv S{S} x{n_splits} causal={causal}", flush=True)
+    out, lse = gpu_fwd_splitkv(q, k, v, 0.0883883, causal, (-1, -1), n_splits)
+    ref_out, ref_lse = oracle.fwd(q, k, v, 0.0883883, causal, (-1, -1))
+    assert_close(out, lse, ref_out, ref_lse, torch.bfloat16, f"S{S} x{n_splits}")
+
+
+@pytest.mark.parametrize("n_splits", [0, 2])
+def test_splitkv_gpt_causal_2k(n_splits):
+    """The 2K causal workload at full size, every element, in 2 parts and in
+    the library's part count (1 here: 512 workgroups fill 256 CUs twice)."""
+    import io_aware_exact_22_amd as fa
+
+    w = WORKLOADS["gpt_causal_2k"]
+    ns = fa.fa_fwd_splitkv_auto_splits(w.B, w.H, w.S, w.D, 1, -1, -1, fa.FA_DTYPE_BF16)
+    print("auto splits", ns, flush=True)
+    assert 1 <= ns <= 8
+    q, k, v = workload_qkv(w)
+    out, lse = gpu_fwd_splitkv(q, k, v, w.scale, w.causal, w.window, n_splits)
+    ref_out, ref_lse = oracle.fwd(q, k, v, w.scale, w.causal, w.window)
+    assert_close(out, lse, ref_out, ref_lse, w.dtype, f"gpt_causal_2k x{n_splits or ns}")
+
+
+@pytest.mark.parametrize("n_splits", [0, 4])
+def test_splitkv_head_sharded_16k_sampled(n_splits):
+    """One GPU's share of the 16K causal workload under head sharding (2 of
+    16 heads) in the library's part count and in 4 parts: sampled rows of both
+    heads."""
+    w = WORKLOADS["causal_16k_h2"]
+    q, k, v = workload_qkv(w)
+    out, lse = gpu_fwd_splitkv(q, k, v, w.scale, w.causal, w.window, n_splits)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    rows = [0, 1, 127, 128, 255, 4096, 8191, 12345, 16255, 16383]
+    check_sampled_rows(w, q, k, v, out, lse, [(0, 0), (0, 1)], rows)
+
+
+def test_splitkv_nan_rows_propagate_like_the_oracle():
+    q, k, v = make_qkv(1, 257, 1, 64, torch.bfloat16, 11)
+    q[0, 100, 0, 3] = float("nan")
+    k[0, 200, 0, 7] = float("nan")
+    out, lse = gpu_fwd_splitkv(q, k, v, 0.125, True, (-1, -1), 3)
+    ref_o, ref_l = oracle.fwd(q, k, v, 0.125, True, (-1, -1))
+    nan_rows = np.isnan(ref_l[0, 0])
+    assert np.array_equal(torch.isnan(lse[0, 0]).numpy(), nan_rows)
+    assert np.array_equal(torch.isnan(out[0, :, 0]).all(-1).numpy(), nan_rows)
+    ok = ~nan_rows
+    assert_close(out[:, ok], lse[:, :, ok], ref_o[:, ok], ref_l[:, :, ok], torch.bfloat16, "nan")
+
+
+def test_splitkv_workspace_guard_bands():
+    """The split writes only its workspace, out and lse: memory around a
+    caller's workspace is untouched, and a second run is bitwise identical."""
+    import io_aware_exact_22_amd as fa
+
+    q, k, v = (t.cuda() for t in make_qkv(2, 300, 3, 64, torch.float16, 5))
+    need = fa.fa_fwd_splitkv_workspace_size(2, 3, 300, 64, fa.FA_DTYPE_FP16, 3)
+    pad = 4096
+    buf = torch.full(((need + 2 * pad) // 4,), 7.0, dtype=torch.float32, device="cuda")
+    ws = buf[pad // 4: (pad + need) // 4]
+    o1, l1 = fa.flash_attn_fwd_splitkv(q, k, v, causal=True, n_splits=3, workspace=ws)
+    o2, l2 = fa.flash_attn_fwd_splitkv(q, k, v, causal=True, n_splits=3, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert bool((buf[: pad // 4] == 7.0).all()) and bool((buf[(pad + need) // 4:] == 7.0).all())
