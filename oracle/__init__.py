@@ -1,4 +1,4 @@
-"""CPU oracle for exact attention (forward): plain, slow, fp64.
+"""CPU oracle for exact attention (forward and backward): plain, slow, fp64.
 
 TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``, ``__graft_entry__.smoke()``
 and the ``cpu_baseline`` leg of ``bench.py`` may import this package.  It shares
@@ -67,6 +67,9 @@ def _load():
         lib.fa_oracle_allowed_pairs.restype = i64
         lib.fa_oracle_decode.argtypes = [vp, ctypes.c_int, i64, vp]
         lib.fa_oracle_decode.restype = ctypes.c_int
+        lib.fa_oracle_bwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, dp,
+                                      ctypes.c_int, i64, i64, vp, vp, vp, ctypes.c_int]
+        lib.fa_oracle_bwd.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -132,6 +135,27 @@ def fwd_rows(q, k, v, scale: float, causal: bool, window_size, b: int, h: int, i
     if rc != 0:
         raise ValueError(f"oracle: fa_oracle_fwd_rows failed ({rc})")
     return out, lse
+
+
+def bwd(q, k, v, dout, scale: float, causal: bool = False, window_size=(-1, -1),
+        nthreads: int = 0):
+    """Gradients of exact attention for the output gradient ``dout``: the chain
+    rule through the forward definition, fp64 ("大模型加速新突破：Flash Attention
+    V2核心网络算子解析" section 二.1 step 3 names this backward pass).  q, k, v,
+    dout: CPU tensors [B, S, H, D] of one dtype.  Returns (dq, dk, dv), each
+    [B, S, H, D] fp64 numpy."""
+    _check_inputs(q, k, v)
+    _check_inputs(q, dout, dout)
+    lib = _load()
+    B, S, H, D = q.shape
+    wl, wr = _window(window_size)
+    dq, dk, dv = (np.empty((B, S, H, D), dtype=np.float64) for _ in range(3))
+    rc = lib.fa_oracle_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                           _dtype_code(q), B, H, S, D, float(scale), int(bool(causal)), wl, wr,
+                           dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle: fa_oracle_bwd failed ({rc})")
+    return dq, dk, dv
 
 
 def allowed_pairs(S: int, causal: bool, window_size=(-1, -1)) -> int:

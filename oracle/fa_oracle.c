@@ -1,5 +1,6 @@
 /*
- * fa_oracle.c -- the CPU oracle for exact attention (forward).
+ * fa_oracle.c -- the CPU oracle for exact attention (forward, and the backward
+ * gradients at the end of the file).
  *
  * TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the tests, the smoke check and
  * the CPU-baseline leg of the benchmark may load this library.  It shares no
@@ -236,5 +237,118 @@ int fa_oracle_fwd(const void* q, const void* k, const void* v, int dtype, int64_
                 memcpy(out + ((b * S + i) * H + h) * D, rows + i * D, sizeof(double) * (size_t)D);
         }
     free(rows);
+    return 0;
+}
+
+/*
+ * fa_oracle_bwd -- gradients of exact attention with respect to q, k and v for
+ * an output gradient dout, in fp64, with the full probability and score-
+ * gradient matrices of each (b, h) materialised.  It is the chain rule through
+ * the forward definition above, written out (the V2 page, section 二.1, step 3
+ * names the backward pass that reuses what the forward saved):
+ *
+ *   p_ij  = exp(s_ij - m_i) / sum_j' exp(s_ij' - m_i)    (0 where j is not allowed)
+ *   dV_j  = sum_i p_ij dO_i
+ *   dP_ij = dO_i . v_j
+ *   D_i   = sum_j p_ij dP_ij
+ *   dS_ij = p_ij (dP_ij - D_i)
+ *   dQ_i  = scale * sum_j dS_ij k_j
+ *   dK_j  = scale * sum_i dS_ij q_i
+ *
+ * dout has the inputs' dtype and layout.  dq, dk, dv are [B, S, H, D] fp64.  A
+ * row with no allowed key contributes nothing.  NaN propagates.
+ */
+int fa_oracle_bwd(const void* q, const void* k, const void* v, const void* dout, int dtype,
+                  int64_t B, int64_t H, int64_t S, int64_t D, double scale, int causal,
+                  int64_t wl, int64_t wr, double* dq, double* dk, double* dv, int nthreads) {
+    if (orc_check(dtype, B, H, S, D, wl, wr)) return -1;
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+    const size_t sd = (size_t)(S * D), ss = (size_t)(S * S);
+    double* Q = (double*)malloc(sizeof(double) * sd);
+    double* K = (double*)malloc(sizeof(double) * sd);
+    double* V = (double*)malloc(sizeof(double) * sd);
+    double* dO = (double*)malloc(sizeof(double) * sd);
+    double* P = (double*)malloc(sizeof(double) * ss);  /* probabilities */
+    double* dS = (double*)malloc(sizeof(double) * ss); /* dP, then dS */
+    if (!Q || !K || !V || !dO || !P || !dS) {
+        free(Q); free(K); free(V); free(dO); free(P); free(dS);
+        return -2;
+    }
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < H; ++h) {
+#define ORC_BIDX(s_, d_) (((b * S + (s_)) * H + h) * D + (d_))
+            for (int64_t s = 0; s < S; ++s)
+                for (int64_t d = 0; d < D; ++d) {
+                    Q[s * D + d] = orc_load(q, dtype, ORC_BIDX(s, d));
+                    K[s * D + d] = orc_load(k, dtype, ORC_BIDX(s, d));
+                    V[s * D + d] = orc_load(v, dtype, ORC_BIDX(s, d));
+                    dO[s * D + d] = orc_load(dout, dtype, ORC_BIDX(s, d));
+                }
+            /* rows: probabilities, dP, D_i, dS, dQ */
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads)
+            for (int64_t i = 0; i < S; ++i) {
+                double* prow = P + i * S;
+                double* grow = dS + i * S;
+                double m = -INFINITY;
+                for (int64_t j = 0; j < S; ++j) {
+                    if (!orc_allowed(i, j, causal, wl, wr)) {
+                        prow[j] = -INFINITY;
+                        continue;
+                    }
+                    double dot = 0.0;
+                    for (int64_t d = 0; d < D; ++d) dot += Q[i * D + d] * K[j * D + d];
+                    prow[j] = dot * scale;
+                    if (isnan(prow[j]) || isnan(m)) m = NAN;
+                    else if (prow[j] > m) m = prow[j];
+                }
+                double* dqrow = dq + ORC_BIDX(i, 0);
+                if (m == -INFINITY) { /* no allowed key */
+                    for (int64_t j = 0; j < S; ++j) prow[j] = grow[j] = 0.0;
+                    for (int64_t d = 0; d < D; ++d) dqrow[d] = 0.0;
+                    continue;
+                }
+                double l = 0.0;
+                for (int64_t j = 0; j < S; ++j) {
+                    prow[j] = exp(prow[j] - m) /* 0 for a masked key */;
+                    l += prow[j];
+                }
+                for (int64_t j = 0; j < S; ++j) prow[j] = prow[j] / l;
+                double Di = 0.0;
+                for (int64_t j = 0; j < S; ++j) {
+                    grow[j] = 0.0;
+                    if (!orc_allowed(i, j, causal, wl, wr)) continue;
+                    double dot = 0.0;
+                    for (int64_t d = 0; d < D; ++d) dot += dO[i * D + d] * V[j * D + d];
+                    grow[j] = dot; /* dP_ij */
+                    Di += prow[j] * dot;
+                }
+                for (int64_t j = 0; j < S; ++j)
+                    if (orc_allowed(i, j, causal, wl, wr)) grow[j] = prow[j] * (grow[j] - Di);
+                for (int64_t d = 0; d < D; ++d) {
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < S; ++j)
+                        if (orc_allowed(i, j, causal, wl, wr)) acc += grow[j] * K[j * D + d];
+                    dqrow[d] = scale * acc;
+                }
+            }
+            /* columns: dK, dV */
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads)
+            for (int64_t j = 0; j < S; ++j) {
+                double* dkrow = dk + ORC_BIDX(j, 0);
+                double* dvrow = dv + ORC_BIDX(j, 0);
+                for (int64_t d = 0; d < D; ++d) {
+                    double ak = 0.0, av = 0.0;
+                    for (int64_t i = 0; i < S; ++i) {
+                        if (!orc_allowed(i, j, causal, wl, wr)) continue;
+                        ak += dS[i * S + j] * Q[i * D + d];
+                        av += P[i * S + j] * dO[i * D + d];
+                    }
+                    dkrow[d] = scale * ak;
+                    dvrow[d] = av;
+                }
+            }
+#undef ORC_BIDX
+        }
+    free(Q); free(K); free(V); free(dO); free(P); free(dS);
     return 0;
 }

@@ -1,5 +1,6 @@
 """Plants plausible mistakes in copies of the CPU oracle (on the CPU only) and
-checks that the pins in test_oracle_pins.py catch every one of them."""
+checks that the pins in test_oracle_pins.py and test_oracle_bwd_pins.py catch
+every one of them."""
 import os
 import subprocess
 import sys
@@ -23,6 +24,14 @@ MUTANTS = {
     "fp16_bias_off": ("mag = ldexp(1024.0 + (double)f, e - 25);", "mag = ldexp(1024.0 + (double)f, e - 24);"),
     "bf16_subnormal_off": ("mag = ldexp((double)f, -133);", "mag = ldexp((double)f, -134);"),
     "max_ignores_nan": ("if (isnan(prow[j])) {", "if (0) {"),
+    # backward
+    "bwd_no_row_term": ("grow[j] = prow[j] * (grow[j] - Di);", "grow[j] = prow[j] * grow[j];"),
+    "bwd_dk_from_p": ("ak += dS[i * S + j] * Q[i * D + d];", "ak += P[i * S + j] * Q[i * D + d];"),
+    "bwd_dq_unscaled": ("dqrow[d] = scale * acc;", "dqrow[d] = acc;"),
+    "bwd_dv_from_v": ("av += P[i * S + j] * dO[i * D + d];", "av += P[i * S + j] * V[i * D + d];"),
+    "bwd_dp_transposed": ("for (int64_t d = 0; d < D; ++d) dot += dO[i * D + d] * V[j * D + d];",
+                          "for (int64_t d = 0; d < D; ++d) dot += dO[j * D + d] * V[i * D + d];"),
+    "bwd_dk_unscaled": ("dkrow[d] = scale * ak;", "dkrow[d] = ak;"),
 }
 
 
@@ -38,6 +47,7 @@ def test_pins_catch_mutant(name, tmp_path):
                     str(lib), "-lm"], check=True)
     env = dict(os.environ, FA_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_bwd_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
