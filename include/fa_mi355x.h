@@ -195,6 +195,39 @@ int fa_fwd_splitkv_auto_splits(int64_t B, int64_t H, int64_t S, int64_t D, int c
                                int64_t window_left, int64_t window_right, int dtype,
                                int64_t* n_splits);
 
+/*
+ * fa_bwd -- gradients of fa_fwd's output with respect to q, k and v for an
+ * output gradient dout, recomputed tile by tile from the saved LSE instead of
+ * a stored S x S matrix ([V2] section 二.1, step 3: the backward pass reuses
+ * what the forward saved).  With P = exp(scale q.k - LSE) over the allowed
+ * keys, D_i = dout_i . out_i and dS = P (dout v^T - D):
+ *   dq = scale dS k,   dk = scale dS^T q,   dv = P^T dout.
+ *
+ * q, k, v, out, lse  the forward's inputs and results (out and lse exactly as
+ *          fa_fwd wrote them for these q, k, v and arguments).
+ * dout     the output gradient, [B, S, H, D] of `dtype`.
+ * dq, dk, dv  outputs, [B, S, H, D] of `dtype` (fp32 accumulation, RNE).
+ * workspace  device buffer of at least fa_bwd_workspace_size bytes (fp32
+ *          D_i), 16-byte aligned; owned by the caller, contents on return
+ *          unspecified.
+ * dtype    FA_DTYPE_BF16 or FA_DTYPE_FP16 (fp32 is not supported here:
+ *          FA_ERR_DTYPE).  Other arguments as fa_fwd.
+ * Pointers as in fa_fwd: 16-byte aligned tensors, lse 4-byte aligned; the
+ * outputs and the workspace must not overlap the inputs or each other
+ * (FA_ERR_ALIAS, FA_ERR_WORKSPACE).  Validation happens before any HIP call.
+ * Enqueues three kernels on `stream` and returns without synchronising.
+ * Returns FA_OK or a negative fa_status_t.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t S,
+           int64_t D, float scale, int causal, int64_t window_left, int64_t window_right,
+           int dtype, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* fa_bwd_workspace_size -- the workspace fa_bwd needs in *bytes: B * H * S * 4.
+ * Pure function.  Returns FA_OK, FA_ERR_NULL or the shape / head-dimension /
+ * dtype status of fa_fwd_check_args (fp32: FA_ERR_DTYPE). */
+int fa_bwd_workspace_size(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int64_t* bytes);
+
 #ifdef __cplusplus
 }
 #endif

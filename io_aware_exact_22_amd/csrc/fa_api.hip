@@ -270,3 +270,71 @@ FA_API int fa_fwd_tile_schedule(int64_t S, int64_t D, int dtype, int causal, int
     }
     return FA_OK;
 }
+
+FA_API int fa_bwd_workspace_size(int64_t B, int64_t H, int64_t S, int64_t D, int dtype,
+                                 int64_t* bytes) {
+    if (!bytes) return FA_ERR_NULL;
+    int64_t nbytes, lbytes;
+    const int rc = check_problem(B, H, S, D, 0, -1, -1, dtype, &nbytes, &lbytes);
+    if (rc != FA_OK) return rc;
+    if (dtype == FA_DTYPE_FP32) return FA_ERR_DTYPE;
+    *bytes = lbytes;  // fp32 [B, H, S], the size of lse
+    return FA_OK;
+}
+
+FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                  const void* dout, void* dq, void* dk, void* dv, int64_t B, int64_t H, int64_t S,
+                  int64_t D, float scale, int causal, int64_t window_left, int64_t window_right,
+                  int dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+    int64_t nbytes = 0, lbytes = 0;
+    int rc = check_problem(B, H, S, D, causal, window_left, window_right, dtype, &nbytes, &lbytes);
+    if (rc != FA_OK) return rc;
+    if (dtype == FA_DTYPE_FP32) return FA_ERR_DTYPE;
+    if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
+    const void* tens[8] = {q, k, v, out, dout, dq, dk, dv};
+    for (const void* t : tens)
+        if ((uintptr_t)t & 15u) return FA_ERR_ALIGN;
+    if ((uintptr_t)lse & 3u) return FA_ERR_ALIGN;
+    const void* ins[6] = {q, k, v, out, dout, lse};
+    const int64_t in_bytes[6] = {nbytes, nbytes, nbytes, nbytes, nbytes, lbytes};
+    void* outs[3] = {dq, dk, dv};
+    for (int o = 0; o < 3; ++o) {
+        for (int i = 0; i < 6; ++i)
+            if (overlaps(outs[o], nbytes, ins[i], in_bytes[i])) return FA_ERR_ALIAS;
+        for (int p = o + 1; p < 3; ++p)
+            if (overlaps(outs[o], nbytes, outs[p], nbytes)) return FA_ERR_ALIAS;
+    }
+    if (!workspace || workspace_bytes < lbytes || ((uintptr_t)workspace & 15u))
+        return FA_ERR_WORKSPACE;
+    for (int i = 0; i < 6; ++i)
+        if (overlaps(workspace, lbytes, ins[i], in_bytes[i])) return FA_ERR_WORKSPACE;
+    for (int o = 0; o < 3; ++o)
+        if (overlaps(workspace, lbytes, outs[o], nbytes)) return FA_ERR_WORKSPACE;
+    const fa::LaunchArgs f = make_args(q, k, v, nullptr, nullptr, B, H, S, D, scale, causal,
+                                       window_left, window_right, dtype, stream);
+    fa::BwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.lse = lse;
+    a.dout = dout;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.di = (float*)workspace;
+    a.B = B;
+    a.H = H;
+    a.S = S;
+    a.D = D;
+    a.c = f.c;
+    a.scale = scale;
+    a.causal = causal;
+    a.wl = f.wl;
+    a.wr = f.wr;
+    a.dtype = dtype;
+    a.stream = (hipStream_t)stream;
+    const hipError_t e = fa::launch_bwd(a);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}

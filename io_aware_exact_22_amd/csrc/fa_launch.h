@@ -31,6 +31,29 @@ struct LaunchArgs {
     float* part_lse = nullptr;
 };
 
+// The backward pass: gradients for an output gradient dout (bf16 / fp16).
+struct BwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* out;
+    const float* lse;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* di;  // workspace: D_i = dO_i . O_i, fp32 [B, H, S]
+    int64_t B, H, S, D;
+    float c;      // as in LaunchArgs
+    float scale;  // softmax scale
+    int causal;
+    int64_t wl, wr;
+    int dtype;
+    hipStream_t stream;
+};
+// Enqueues the three backward kernels for validated arguments.
+hipError_t launch_bwd(const BwdArgs& a);
+
 // Enqueues the forward kernel (and, for a split launch, the merge kernel) for
 // validated arguments.
 hipError_t launch_fwd(const LaunchArgs& a);

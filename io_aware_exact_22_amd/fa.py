@@ -2,8 +2,9 @@
 
 Same names as the C ABI: ``fa_fwd``, ``fa_fwd_check_args``,
 ``fa_status_string``, ``fa_fwd_tile_schedule``, ``fa_fwd_workgroup_tile``, ``fa_fwd_splitkv``,
-``fa_fwd_splitkv_workspace_size``, ``fa_fwd_splitkv_auto_splits``; plus ``flash_attn_fwd`` (and
-``flash_attn_fwd_splitkv``), the
+``fa_fwd_splitkv_workspace_size``, ``fa_fwd_splitkv_auto_splits``, ``fa_bwd``,
+``fa_bwd_workspace_size``; plus ``flash_attn_fwd`` (and ``flash_attn_fwd_splitkv``,
+``flash_attn_bwd``), the
 tensor-level call that mirrors the pages' ``flash_attention(q, k, v,
 softmax_scale=None, causal=..., window_size=(-1, -1))`` argument list
 ("FlashAttention技术解析：加速GPT训练的核心优化", section 2.2).  This module only
@@ -76,6 +77,11 @@ def _load():
         lib.fa_fwd_splitkv_workspace_size.restype = cint
         lib.fa_fwd_splitkv_auto_splits.argtypes = [i64, i64, i64, i64, cint, i64, i64, cint, p64]
         lib.fa_fwd_splitkv_auto_splits.restype = cint
+        lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                               ctypes.c_float, cint, i64, i64, cint, vp, i64, vp]
+        lib.fa_bwd.restype = cint
+        lib.fa_bwd_workspace_size.argtypes = [i64, i64, i64, i64, cint, p64]
+        lib.fa_bwd_workspace_size.restype = cint
         _lib = lib
         return lib
 
@@ -155,6 +161,23 @@ def fa_fwd_splitkv_auto_splits(B: int, H: int, S: int, D: int, causal: int, wind
                                             ctypes.byref(n))
     if rc != 0:
         raise FaError(rc, "fa_fwd_splitkv_auto_splits")
+    return n.value
+
+
+def fa_bwd(q: int, k: int, v: int, out: int, lse: int, dout: int, dq: int, dk: int, dv: int,
+           B: int, H: int, S: int, D: int, scale: float, causal: int, window_left: int,
+           window_right: int, dtype: int, workspace: int, workspace_bytes: int,
+           stream: int | None) -> int:
+    """The backward C entry point with raw device pointers (ints); returns the status."""
+    return _load().fa_bwd(q, k, v, out, lse, dout, dq, dk, dv, B, H, S, D, scale, causal,
+                          window_left, window_right, dtype, workspace, workspace_bytes, stream)
+
+
+def fa_bwd_workspace_size(B: int, H: int, S: int, D: int, dtype: int) -> int:
+    n = ctypes.c_int64()
+    rc = _load().fa_bwd_workspace_size(B, H, S, D, dtype, ctypes.byref(n))
+    if rc != 0:
+        raise FaError(rc, "fa_bwd_workspace_size")
     return n.value
 
 
@@ -258,3 +281,39 @@ def flash_attn_fwd_splitkv(q, k, v, softmax_scale: float | None = None, causal: 
     if rc != 0:
         raise FaError(rc, "fa_fwd_splitkv")
     return out, lse
+
+
+def flash_attn_bwd(dout, q, k, v, out, lse, softmax_scale: float | None = None,
+                   causal: bool = False, window_size=(-1, -1), workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of flash_attn_fwd's output for the output
+    gradient ``dout``, given the forward's q, k, v and its out and lse.
+    bf16 / fp16 tensors [B, S, H, D]; the fp32 workspace (B * H * S floats)
+    is allocated here when None."""
+    import torch
+
+    ts = (("dout", dout), ("q", q), ("k", k), ("v", v), ("out", out))
+    for name, t in ts:
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise TypeError(f"{name} must be a GPU tensor")
+        if t.dim() != 4 or t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("dout, q, k, v, out must share shape [B, S, H, D], dtype and device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, S, H, D]")
+    B, S, H, D = q.shape
+    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be the forward's contiguous fp32 [B, H, S]")
+    dtype = _dtype_code(q)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    wl, wr = (int(x) for x in window_size)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if workspace is None:
+        workspace = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                    dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, S, D,
+                    scale, int(bool(causal)), wl, wr, dtype, workspace.data_ptr(),
+                    workspace.numel() * workspace.element_size(), st.cuda_stream)
+    if rc != 0:
+        raise FaError(rc, "fa_bwd")
+    return dq, dk, dv

@@ -26,7 +26,8 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_check_args", "fa_status_string", "fa_fwd_tile_schedule",
                           "fa_fwd_workgroup_tile", "fa_fwd_splitkv",
-                          "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv_auto_splits"}
+                          "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv_auto_splits",
+                          "fa_bwd", "fa_bwd_workspace_size"}
     lib = ctypes.CDLL(fa.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -121,6 +122,34 @@ def test_splitkv_rejects_before_any_hip_call(kw, status):
     rc = fa.fa_fwd_splitkv(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["S"],
                            a["D"], a["scale"], a["causal"], a["window_left"], a["window_right"],
                            a["dtype"], a["ns"], a["ws"] or None, a["wsb"], None)
+    assert rc == status
+
+
+def test_bwd_workspace_size():
+    assert fa.fa_bwd_workspace_size(2, 16, 2048, 64, fa.FA_DTYPE_BF16) == 2 * 16 * 2048 * 4
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_bwd_workspace_size(2, 16, 2048, 64, fa.FA_DTYPE_FP32)
+    assert e.value.status == -5
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_bwd_workspace_size(2, 16, 2048, 80, fa.FA_DTYPE_BF16)
+    assert e.value.status == -3
+
+
+DO, DQ, DK, DV = 7 << 32, 8 << 32, 9 << 32, 10 << 32
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"dq": 0}, -1), ({"dout": 0}, -1), ({"dtype": fa.FA_DTYPE_FP32}, -5), ({"D": 96}, -3),
+    ({"dq": Q}, -8), ({"dk": DV}, -8), ({"dv": LSE}, -8), ({"dq": DQ + 8}, -7), ({"lse": LSE + 2}, -7),
+    ({"ws": 0}, -10), ({"wsb": 100}, -10), ({"ws": DQ}, -10), ({"ws": WS + 4}, -10),
+    ({"scale": -1.0}, -6), ({"window_left": -3}, -4),
+])
+def test_bwd_rejects_before_any_hip_call(kw, status):
+    a = dict(GOOD, dout=DO, dq=DQ, dk=DK, dv=DV, ws=WS, wsb=1 << 30)
+    a.update(kw)
+    rc = fa.fa_bwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"],
+                   a["B"], a["H"], a["S"], a["D"], a["scale"], a["causal"], a["window_left"],
+                   a["window_right"], a["dtype"], a["ws"] or None, a["wsb"], None)
     assert rc == status
 
 

@@ -386,3 +386,56 @@ def test_splitkv_workspace_guard_bands():
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     assert bool((buf[: pad // 4] == 7.0).all()) and bool((buf[(pad + need) // 4:] == 7.0).all())
+
+
+# ---------------------------------------------------------------- backward
+TOL_GRAD = {torch.float16: 4e-3, torch.bfloat16: 2e-2}
+
+
+def gpu_bwd(q, k, v, do, scale, causal, window):
+    import io_aware_exact_22_amd as fa
+
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    out, lse = fa.flash_attn_fwd(qd, kd, vd, softmax_scale=scale, causal=causal, window_size=window)
+    dq, dk, dv = fa.flash_attn_bwd(dod, qd, kd, vd, out, lse, softmax_scale=scale, causal=causal,
+                                   window_size=window)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def check_bwd(B, S, H, D, dtype, causal, window, seed, scale=None):
+    """dq, dk, dv against the oracle's fp64 gradients: max-abs error within
+    TOL_GRAD[dtype] x max(1, max |reference|), per gradient."""
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    q, k, v = make_qkv(B, S, H, D, dtype, seed)
+    do = make_qkv(B, S, H, D, dtype, seed + 1)[0]
+    what = f"bwd B{B} S{S} H{H} D{D} {dtype} causal={causal} window={window}"
+    print("run", what, flush=True)
+    got = gpu_bwd(q, k, v, do, scale, causal, window)
+    ref = oracle.bwd(q, k, v, do, scale, causal, window)
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref):
+        g = g.double().numpy()
+        assert np.all(np.isfinite(g)), f"{what}: non-finite {name}"
+        bound = TOL_GRAD[dtype] * max(1.0, float(np.max(np.abs(r))))
+        err = float(np.max(np.abs(g - r)))
+        print(f"{what}: {name} max err {err:.3e} (bound {bound:.3e})", flush=True)
+        assert err <= bound, f"{what}: {name} error {err} > {bound}"
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (False, (128, 128)),
+                                           (True, (100, -1)), (False, (33, 7))])
+def test_bwd_parity(dtype, D, causal, window):
+    check_bwd(2, 389, 3, D, dtype, causal, window, seed=71)
+
+
+@pytest.mark.parametrize("S", [1, 63, 64, 65, 128, 129, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_lengths(S, causal):
+    check_bwd(1, S, 2, 128, torch.bfloat16, causal, (-1, -1), seed=S + 3)
+
+
+def test_bwd_gpt_causal_2k():
+    """The 2K causal workload's shape (B2 H16 S2048 D64 bf16), every element."""
+    check_bwd(2, 2048, 16, 64, torch.bfloat16, True, (-1, -1), seed=81)
