@@ -29,6 +29,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "attention fwd TFLOPS (4·B·H·S·S_eff·D/t) and % of MI355X bf16 MFMA peak"
+METRIC_BWD = "attention bwd TFLOPS (10·B·H·S·S_eff·D/t: five products) and % of MI355X bf16 MFMA peak"
 PEAK_MFMA_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp32": 157.3}  # MI355X dense, 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "causal_16k"
@@ -110,6 +111,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time fa_bwd (the gradients of the forward) instead of fa_fwd; "
+                         "bf16 / fp16 workloads")
     ap.add_argument("--splitkv", type=int, default=-1,
                     help="time fa_fwd_splitkv with this many K/V parts per Q tile (0 = the "
                          "library's choice for the device) instead of fa_fwd")
@@ -152,7 +156,20 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
 
     n_splits = None
-    if args.splitkv >= 0:
+    if args.backward:
+        out, lse = fa.flash_attn_fwd(qd, kd, vd, softmax_scale=w.scale, causal=w.causal,
+                                     window_size=w.window, stream=stream)
+        g = torch.Generator(device="cpu")
+        g.manual_seed(w.seed + 1000)
+        dod = torch.randn(qd.shape, generator=g, dtype=torch.float32).to(w.dtype).to(dev)
+        ws_b = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+
+        def step():
+            fa.flash_attn_bwd(dod, qd, kd, vd, out, lse, softmax_scale=w.scale, causal=w.causal,
+                              window_size=w.window, workspace=ws_b, dq=dq, dk=dk, dv=dv,
+                              stream=stream)
+    elif args.splitkv >= 0:
         dcode = {torch.float32: fa.FA_DTYPE_FP32, torch.float16: fa.FA_DTYPE_FP16,
                  torch.bfloat16: fa.FA_DTYPE_BF16}[w.dtype]
         n_splits = args.splitkv or fa.fa_fwd_splitkv_auto_splits(
@@ -186,13 +203,17 @@ def main() -> int:
 
     pairs = allowed_pairs(w.S, w.causal, w.window)
     s_eff = pairs / w.S
-    flops = 4.0 * w.B * w.H * pairs * w.D
+    # the backward's five products (S, dP, dV, dK, dQ) against the forward's two
+    flops = (10.0 if args.backward else 4.0) * w.B * w.H * pairs * w.D
     ms_per_step = wall * 1e3 / args.steps
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     avg_launch_ms = float(np.mean(launch_ms))
     kern_tflops = flops / (avg_launch_ms * 1e-3) / 1e12
     esz = 4 if dt_name == "fp32" else 2
-    alg_bytes = 4 * w.B * w.S * w.H * w.D * esz + 4 * w.B * w.H * w.S
+    if args.backward:  # read q, k, v, out, dO and LSE; write dQ, dK, dV; D out and back in
+        alg_bytes = 8 * w.B * w.S * w.H * w.D * esz + 12 * w.B * w.H * w.S
+    else:
+        alg_bytes = 4 * w.B * w.S * w.H * w.D * esz + 4 * w.B * w.H * w.S
     ai = flops / alg_bytes
     peak = PEAK_MFMA_TFLOPS[dt_name]
     hbm_bound = ai < peak * 1e12 / (PEAK_HBM_GBS * 1e9)
@@ -203,19 +224,21 @@ def main() -> int:
     else:
         roof = {"bound": "mfma", "achieved": kern_tflops, "peak": peak, "unit": "TFLOP/s",
                 "frac": kern_tflops / peak}
-    roof["traffic"] = measured_traffic(w.name)
+    # the recorded counters are those of fa_fwd on its default workload
+    roof["traffic"] = None if (args.backward or n_splits is not None) else measured_traffic(w.name)
     roof["kernel_ms"] = avg_launch_ms
     roof["algorithmic_flops_per_launch"] = flops
     roof["algorithmic_bytes_per_launch"] = alg_bytes
 
     # correctness of what was timed: sampled rows against the oracle are the
     # GPU tests' job; here only a finiteness check of the timed output
-    if not (torch.isfinite(out.float()).all() and torch.isfinite(lse).all()):
+    timed = (dq, dk, dv) if args.backward else (out, lse)
+    if not all(bool(torch.isfinite(t.float()).all()) for t in timed):
         print("bench.py: non-finite output", file=sys.stderr)
         return 1
 
     rec = {
-        "metric": METRIC,
+        "metric": METRIC_BWD if args.backward else METRIC,
         "value": tflops,
         "unit": "TFLOPS",
         "n_gpus": 1,
@@ -231,11 +254,12 @@ def main() -> int:
         "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
                    "causal": w.causal, "window": list(w.window), "S_eff": s_eff,
                    "flops_per_step": flops, "parallelism": "single GPU",
-                   "entry": "fa_fwd" if n_splits is None else "fa_fwd_splitkv",
+                   "entry": ("fa_bwd" if args.backward else
+                             "fa_fwd" if n_splits is None else "fa_fwd_splitkv"),
                    **({} if n_splits is None else {"n_splits": n_splits})},
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.backward and n_splits is None:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v)
     else:
         rec["cpu_baseline"] = None

@@ -284,11 +284,12 @@ def flash_attn_fwd_splitkv(q, k, v, softmax_scale: float | None = None, causal: 
 
 
 def flash_attn_bwd(dout, q, k, v, out, lse, softmax_scale: float | None = None,
-                   causal: bool = False, window_size=(-1, -1), workspace=None, stream=None):
+                   causal: bool = False, window_size=(-1, -1), workspace=None, dq=None, dk=None,
+                   dv=None, stream=None):
     """Gradients (dq, dk, dv) of flash_attn_fwd's output for the output
     gradient ``dout``, given the forward's q, k, v and its out and lse.
     bf16 / fp16 tensors [B, S, H, D]; the fp32 workspace (B * H * S floats)
-    is allocated here when None."""
+    and the gradients are allocated here when None."""
     import torch
 
     ts = (("dout", dout), ("q", q), ("k", k), ("v", v), ("out", out))
@@ -305,7 +306,12 @@ def flash_attn_bwd(dout, q, k, v, out, lse, softmax_scale: float | None = None,
     dtype = _dtype_code(q)
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     wl, wr = (int(x) for x in window_size)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor shaped and typed like q")
     if workspace is None:
         workspace = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
     st = stream if stream is not None else torch.cuda.current_stream(q.device)
