@@ -73,3 +73,30 @@ def make_qkv(B: int, S: int, H: int, D: int, dtype: torch.dtype, seed: int):
 
 def workload_qkv(w: Workload, seed: int | None = None):
     return make_qkv(w.B, w.S, w.H, w.D, w.dtype, w.seed if seed is None else seed)
+
+
+# ---------------------------------------------------------------- block masks
+# Which (query block, key block) pairs a block-sparse call keeps.  These only
+# choose bytes of 0 / 1; what a kept block means is the method's business.
+def random_block_mask(n_mask: int, n_qb: int, n_kb: int, density: float, seed: int) -> torch.Tensor:
+    """uint8 [n_mask, n_qb, n_kb]: each block on with probability ``density``,
+    from a torch CPU generator seeded with ``seed``."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    u = torch.rand((n_mask, n_qb, n_kb), generator=g, dtype=torch.float32)
+    return (u < density).to(torch.uint8).contiguous()
+
+
+def local_global_block_mask(n_qb: int, n_kb: int, block_m: int, block_n: int, local_keys: int,
+                            global_kb: int) -> torch.Tensor:
+    """uint8 [1, n_qb, n_kb], the long-context pattern of a local band plus a few
+    global key blocks: query block r keeps the first ``global_kb`` key blocks
+    and every key block that overlaps the ``local_keys`` keys ending at the
+    block's last query row (``local_keys`` >= 1)."""
+    m = torch.zeros((1, n_qb, n_kb), dtype=torch.uint8)
+    m[0, :, :global_kb] = 1
+    for r in range(n_qb):
+        last = (r + 1) * block_m - 1
+        first = max(0, last - local_keys + 1)
+        m[0, r, first // block_n: min(n_kb, last // block_n + 1)] = 1
+    return m.contiguous()

@@ -70,6 +70,15 @@ def _load():
         lib.fa_oracle_bwd.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, dp,
                                       ctypes.c_int, i64, i64, vp, vp, vp, ctypes.c_int]
         lib.fa_oracle_bwd.restype = ctypes.c_int
+        lib.fa_oracle_fwd_blocksparse.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, i64,
+                                                  dp, ctypes.c_int, i64, i64, vp, i64, i64, i64,
+                                                  vp, vp, ctypes.c_int]
+        lib.fa_oracle_fwd_blocksparse.restype = ctypes.c_int
+        lib.fa_oracle_fwd_rows_blocksparse.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64,
+                                                       i64, dp, ctypes.c_int, i64, i64, vp, i64,
+                                                       i64, i64, i64, i64, i64, i64, vp, vp,
+                                                       ctypes.c_int]
+        lib.fa_oracle_fwd_rows_blocksparse.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -134,6 +143,61 @@ def fwd_rows(q, k, v, scale: float, causal: bool, window_size, b: int, h: int, i
                                 out.ctypes.data, lse.ctypes.data, int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle: fa_oracle_fwd_rows failed ({rc})")
+    return out, lse
+
+
+def _check_mask(mask, B, H, S, block_m, block_n):
+    """The block mask as a contiguous uint8 numpy array [n_mask, n_qb, n_kb]."""
+    m = np.ascontiguousarray(np.asarray(mask), dtype=np.uint8)
+    n_qb, n_kb = -(-S // block_m), -(-S // block_n)
+    if m.ndim == 2:
+        m = m[None]
+    if m.ndim != 3 or m.shape[1:] != (n_qb, n_kb) or m.shape[0] not in (1, H, B * H):
+        raise ValueError(f"oracle: block mask must be [1|H|B*H, {n_qb}, {n_kb}], got {m.shape}")
+    return np.ascontiguousarray(m)
+
+
+def fwd_blocksparse(q, k, v, scale: float, mask, block_m: int, block_n: int,
+                    causal: bool = False, window_size=(-1, -1), nthreads: int = 0):
+    """Block-sparse exact attention: ``fwd`` with key j allowed for query i only
+    where mask[hm, i // block_m, j // block_n] != 0 ("FlashAttention技术解析：
+    加速GPT训练的核心优化" section 5 lists the block-sparse variant).  mask:
+    uint8/bool array [n_mask, ceil(S/block_m), ceil(S/block_n)] with n_mask in
+    {1, H, B*H} (a 2-D mask is taken as n_mask = 1).  Returns (out, lse) as fwd."""
+    _check_inputs(q, k, v)
+    lib = _load()
+    B, S, H, D = q.shape
+    m = _check_mask(mask, B, H, S, block_m, block_n)
+    wl, wr = _window(window_size)
+    out = np.empty((B, S, H, D), dtype=np.float64)
+    lse = np.empty((B, H, S), dtype=np.float64)
+    rc = lib.fa_oracle_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dtype_code(q),
+                                       B, H, S, D, float(scale), int(bool(causal)), wl, wr,
+                                       m.ctypes.data, m.shape[0], int(block_m), int(block_n),
+                                       out.ctypes.data, lse.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle: fa_oracle_fwd_blocksparse failed ({rc})")
+    return out, lse
+
+
+def fwd_rows_blocksparse(q, k, v, scale: float, mask, block_m: int, block_n: int, causal: bool,
+                         window_size, b: int, h: int, i0: int, i1: int, nthreads: int = 0):
+    """Block-sparse attention for query rows [i0, i1) of head (b, h); as fwd_rows."""
+    _check_inputs(q, k, v)
+    lib = _load()
+    B, S, H, D = q.shape
+    m = _check_mask(mask, B, H, S, block_m, block_n)
+    wl, wr = _window(window_size)
+    R = i1 - i0
+    out = np.empty((max(R, 0), D), dtype=np.float64)
+    lse = np.empty((max(R, 0),), dtype=np.float64)
+    rc = lib.fa_oracle_fwd_rows_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                            _dtype_code(q), B, H, S, D, float(scale),
+                                            int(bool(causal)), wl, wr, m.ctypes.data, m.shape[0],
+                                            int(block_m), int(block_n), b, h, i0, i1,
+                                            out.ctypes.data, lse.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle: fa_oracle_fwd_rows_blocksparse failed ({rc})")
     return out, lse
 
 

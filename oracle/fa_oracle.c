@@ -42,6 +42,21 @@
  *    NaN, so a NaN score makes the whole row NaN;
  *  - bf16/fp16/fp32 inputs are decoded exactly to fp64 (subnormals kept).
  *
+ * Block-sparse attention ("FlashAttention技术解析：加速GPT训练的核心优化",
+ * section 5, lists a block-sparse variant of the method that reaches very long
+ * contexts through a sparse pattern) is the same definition with one more
+ * factor in allowed(i, j): the block mask bit of the (query block, key block)
+ * pair,
+ *
+ *   allowed_bs(i,j) = allowed(i,j) && mask[i / block_m][j / block_n] != 0,
+ *
+ * with mask a row-major [ceil(S/block_m), ceil(S/block_n)] byte matrix per
+ * (b, h) -- shared by every head (n_mask = 1), by every batch (n_mask = H) or
+ * one per (b, h) (n_mask = B*H).  Reading: the pages name the variant and its
+ * purpose only; the plainest reading, a block-granular mask intersected with
+ * the causal and window masks, is the one taken.  A row whose blocks are all
+ * off has no allowed key: O = 0, LSE = -inf, as above.
+ *
  * Build: gcc -O2 -fopenmp -shared -fPIC fa_oracle.c -o libfa_oracle.so -lm
  * No -ffast-math: the oracle depends on IEEE inf/NaN semantics.
  */
@@ -109,6 +124,14 @@ static int orc_allowed(int64_t i, int64_t j, int causal, int64_t wl, int64_t wr)
     return 1;
 }
 
+/* The block mask factor of allowed_bs: mask is one (b, h)'s row-major
+ * [n_qb, n_kb] byte matrix, or NULL for no block mask. */
+static int orc_block_on(const uint8_t* mask, int64_t i, int64_t j, int64_t block_m,
+                        int64_t block_n, int64_t n_kb) {
+    if (!mask) return 1;
+    return mask[(i / block_m) * n_kb + j / block_n] != 0;
+}
+
 /* Decodes n elements of raw input bits to fp64, so the tests can check the
  * decoders against other implementations of the formats. */
 int fa_oracle_decode(const void* base, int dtype, int64_t n, double* out) {
@@ -134,18 +157,21 @@ static int orc_check(int dtype, int64_t B, int64_t H, int64_t S, int64_t D,
 }
 
 /*
- * Query rows [i0, i1) of one (b, h).  out_rows is [(i1 - i0), D] fp64,
- * lse_rows is [(i1 - i0)] fp64.  The (i1 - i0) x S score matrix of this head
- * is materialised in full; rows run in parallel over nthreads OpenMP threads
- * (0 = the OpenMP default).
+ * Query rows [i0, i1) of one (b, h), with an optional block mask (bmask: this
+ * (b, h)'s [ceil(S/block_m), ceil(S/block_n)] bytes, or NULL).  out_rows is
+ * [(i1 - i0), D] fp64, lse_rows is [(i1 - i0)] fp64.  The (i1 - i0) x S score
+ * matrix of this head is materialised in full; rows run in parallel over
+ * nthreads OpenMP threads (0 = the OpenMP default).
  */
-int fa_oracle_fwd_rows(const void* q, const void* k, const void* v, int dtype,
-                       int64_t B, int64_t H, int64_t S, int64_t D, double scale,
-                       int causal, int64_t wl, int64_t wr, int64_t b, int64_t h,
-                       int64_t i0, int64_t i1, double* out_rows, double* lse_rows,
-                       int nthreads) {
+static int orc_fwd_rows(const void* q, const void* k, const void* v, int dtype, int64_t B,
+                        int64_t H, int64_t S, int64_t D, double scale, int causal, int64_t wl,
+                        int64_t wr, const uint8_t* bmask, int64_t block_m, int64_t block_n,
+                        int64_t b, int64_t h, int64_t i0, int64_t i1, double* out_rows,
+                        double* lse_rows, int nthreads) {
     if (orc_check(dtype, B, H, S, D, wl, wr)) return -1;
     if (b < 0 || b >= B || h < 0 || h >= H || i0 < 0 || i1 > S || i0 > i1) return -1;
+    if (bmask && (block_m < 1 || block_n < 1)) return -1;
+    const int64_t n_kb = bmask ? (S + block_n - 1) / block_n : 0;
     const int64_t R = i1 - i0;
     if (R == 0) return 0;
     /* element (b, s, h, d) of a [B, S, H, D] tensor */
@@ -173,7 +199,8 @@ int fa_oracle_fwd_rows(const void* q, const void* k, const void* v, int dtype,
         double* prow = P + r * S;
         /* 1. scores of the allowed keys; -inf elsewhere */
         for (int64_t j = 0; j < S; ++j) {
-            if (!orc_allowed(i, j, causal, wl, wr)) {
+            if (!orc_allowed(i, j, causal, wl, wr) ||
+                !orc_block_on(bmask, i, j, block_m, block_n, n_kb)) {
                 prow[j] = -INFINITY;
                 continue;
             }
@@ -206,7 +233,9 @@ int fa_oracle_fwd_rows(const void* q, const void* k, const void* v, int dtype,
         /* 4. O = P V */
         for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
         for (int64_t j = 0; j < S; ++j) {
-            if (!orc_allowed(i, j, causal, wl, wr)) continue; /* p = 0 exactly */
+            if (!orc_allowed(i, j, causal, wl, wr) ||
+                !orc_block_on(bmask, i, j, block_m, block_n, n_kb))
+                continue; /* p = 0 exactly */
             const double p = prow[j];
             for (int64_t d = 0; d < D; ++d) orow[d] += p * V[j * D + d];
         }
@@ -214,6 +243,49 @@ int fa_oracle_fwd_rows(const void* q, const void* k, const void* v, int dtype,
     }
     free(Q); free(K); free(V); free(P);
     return 0;
+}
+
+/* Query rows [i0, i1) of one (b, h), no block mask. */
+int fa_oracle_fwd_rows(const void* q, const void* k, const void* v, int dtype,
+                       int64_t B, int64_t H, int64_t S, int64_t D, double scale,
+                       int causal, int64_t wl, int64_t wr, int64_t b, int64_t h,
+                       int64_t i0, int64_t i1, double* out_rows, double* lse_rows,
+                       int nthreads) {
+    return orc_fwd_rows(q, k, v, dtype, B, H, S, D, scale, causal, wl, wr, NULL, 0, 0, b, h,
+                        i0, i1, out_rows, lse_rows, nthreads);
+}
+
+/* The (b, h) block mask of a [n_mask, n_qb, n_kb] mask: one shared matrix
+ * (n_mask = 1), one per head (n_mask = H) or one per (b, h) (n_mask = B*H);
+ * NULL for any other n_mask.  Where H = 1 or B = 1 two readings coincide. */
+static const uint8_t* orc_head_mask(const uint8_t* mask, int64_t n_mask, int64_t B, int64_t H,
+                                    int64_t S, int64_t block_m, int64_t block_n, int64_t b,
+                                    int64_t h) {
+    const int64_t per = ((S + block_m - 1) / block_m) * ((S + block_n - 1) / block_n);
+    int64_t hm;
+    if (n_mask == 1)
+        hm = 0;
+    else if (n_mask == H)
+        hm = h;
+    else if (n_mask == B * H)
+        hm = b * H + h;
+    else
+        return NULL;
+    return mask + hm * per;
+}
+
+/* Block-sparse rows [i0, i1) of one (b, h): mask is [n_mask, n_qb, n_kb]. */
+int fa_oracle_fwd_rows_blocksparse(const void* q, const void* k, const void* v, int dtype,
+                                   int64_t B, int64_t H, int64_t S, int64_t D, double scale,
+                                   int causal, int64_t wl, int64_t wr, const uint8_t* mask,
+                                   int64_t n_mask, int64_t block_m, int64_t block_n, int64_t b,
+                                   int64_t h, int64_t i0, int64_t i1, double* out_rows,
+                                   double* lse_rows, int nthreads) {
+    if (!mask || block_m < 1 || block_n < 1 || b < 0 || b >= B || h < 0 || h >= H) return -1;
+    const uint8_t* hmask = orc_head_mask(mask, n_mask, B, H, S, block_m, block_n, b, h);
+    if (!hmask) return -1;
+    return orc_fwd_rows(q, k, v, dtype, B, H, S, D, scale, causal, wl, wr, hmask, block_m,
+                        block_n, b, h, i0, i1, out_rows, lse_rows, nthreads);
 }
 
 /*
@@ -229,6 +301,36 @@ int fa_oracle_fwd(const void* q, const void* k, const void* v, int dtype, int64_
         for (int64_t h = 0; h < H; ++h) {
             int rc = fa_oracle_fwd_rows(q, k, v, dtype, B, H, S, D, scale, causal, wl, wr, b,
                                         h, 0, S, rows, lse + (b * H + h) * S, nthreads);
+            if (rc) {
+                free(rows);
+                return rc;
+            }
+            for (int64_t i = 0; i < S; ++i)
+                memcpy(out + ((b * S + i) * H + h) * D, rows + i * D, sizeof(double) * (size_t)D);
+        }
+    free(rows);
+    return 0;
+}
+
+/*
+ * Block-sparse attention over every (b, h), all rows: fa_oracle_fwd with the
+ * block mask factor (mask [n_mask, ceil(S/block_m), ceil(S/block_n)] bytes).
+ */
+int fa_oracle_fwd_blocksparse(const void* q, const void* k, const void* v, int dtype,
+                              int64_t B, int64_t H, int64_t S, int64_t D, double scale,
+                              int causal, int64_t wl, int64_t wr, const uint8_t* mask,
+                              int64_t n_mask, int64_t block_m, int64_t block_n, double* out,
+                              double* lse, int nthreads) {
+    if (orc_check(dtype, B, H, S, D, wl, wr)) return -1;
+    if (!mask || block_m < 1 || block_n < 1) return -1;
+    double* rows = (double*)malloc(sizeof(double) * (size_t)(S * D));
+    if (!rows) return -2;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < H; ++h) {
+            int rc = fa_oracle_fwd_rows_blocksparse(q, k, v, dtype, B, H, S, D, scale, causal,
+                                                    wl, wr, mask, n_mask, block_m, block_n, b,
+                                                    h, 0, S, rows, lse + (b * H + h) * S,
+                                                    nthreads);
             if (rc) {
                 free(rows);
                 return rc;

@@ -1,6 +1,6 @@
 """Plants plausible mistakes in copies of the CPU oracle (on the CPU only) and
-checks that the pins in test_oracle_pins.py and test_oracle_bwd_pins.py catch
-every one of them."""
+checks that the pins in test_oracle_pins.py, test_oracle_bwd_pins.py and
+test_oracle_blocksparse_pins.py catch every one of them."""
 import os
 import subprocess
 import sys
@@ -32,6 +32,16 @@ MUTANTS = {
     "bwd_dp_transposed": ("for (int64_t d = 0; d < D; ++d) dot += dO[i * D + d] * V[j * D + d];",
                           "for (int64_t d = 0; d < D; ++d) dot += dO[j * D + d] * V[i * D + d];"),
     "bwd_dk_unscaled": ("dkrow[d] = scale * ak;", "dkrow[d] = ak;"),
+    # block-sparse factor
+    "bs_mask_ignored": ("if (!mask) return 1;", "if (1) return 1;"),
+    "bs_key_block_divisor": ("return mask[(i / block_m) * n_kb + j / block_n] != 0;",
+                             "return mask[(i / block_m) * n_kb + j / block_m] != 0;"),
+    "bs_row_stride": ("return mask[(i / block_m) * n_kb + j / block_n] != 0;",
+                      "return mask[(i / block_m) * (n_kb - 1) + j / block_n] != 0;"),
+    "bs_head_index": ("hm = b * H + h;", "hm = h * B + b;"),
+    "bs_per_head_ignored": ("hm = h;", "hm = 0;"),
+    "bs_only_in_scores": ("!orc_block_on(bmask, i, j, block_m, block_n, n_kb))\n                continue;",
+                          "0)\n                continue;"),
 }
 
 
@@ -48,6 +58,7 @@ def test_pins_catch_mutant(name, tmp_path):
     env = dict(os.environ, FA_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_bwd_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_bwd_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_blocksparse_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
