@@ -52,9 +52,12 @@ typedef enum {
     FA_ERR_ALIGN = -7,    /* q, k, v or out not 16-byte aligned, or lse not 4-byte aligned */
     FA_ERR_ALIAS = -8,    /* out or lse overlaps an input, or out overlaps lse */
     FA_ERR_HIP = -9,      /* the kernel launch failed (hipGetLastError) */
-    FA_ERR_WORKSPACE = -10, /* fa_fwd_splitkv: workspace NULL, too small, not 16-byte
+    FA_ERR_WORKSPACE = -10, /* a workspace argument is NULL, too small, not 16-byte
                                aligned, or overlapping an input or output */
-    FA_ERR_SPLITS = -11   /* fa_fwd_splitkv: n_splits outside [1, FA_MAX_SPLITS] */
+    FA_ERR_SPLITS = -11,  /* fa_fwd_splitkv: n_splits outside [1, FA_MAX_SPLITS] */
+    FA_ERR_BLOCKMASK = -12 /* fa_fwd_blocksparse: block_m not a positive multiple of 128,
+                              block_n not a positive multiple of 64, or n_mask not 1, H
+                              or B*H */
 } fa_status_t;
 
 /* The most K/V parts per Q tile fa_fwd_splitkv takes. */
@@ -227,6 +230,50 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
  * Pure function.  Returns FA_OK, FA_ERR_NULL or the shape / head-dimension /
  * dtype status of fa_fwd_check_args (fp32: FA_ERR_DTYPE). */
 int fa_bwd_workspace_size(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int64_t* bytes);
+
+/*
+ * fa_fwd_blocksparse -- fa_fwd restricted to the blocks a block mask keeps
+ * (block-sparse attention: [FA] section 5 lists it as the variant of the
+ * method that reaches very long contexts through a sparse pattern).  Key j is
+ * allowed for query i of head (b, h) when fa_fwd allows it and
+ *   block_mask[hm][i / block_m][j / block_n] != 0,
+ * hm = 0 (n_mask = 1: one mask for every head), h (n_mask = H) or b * H + h
+ * (n_mask = B * H).  Dropped blocks are never read: the work and the K/V
+ * traffic scale with the kept blocks.  A row with no allowed key gets O = 0
+ * and LSE = -inf.
+ *
+ * Arguments and results as fa_fwd, plus:
+ * block_mask  device pointer, contiguous uint8 [n_mask, ceil(S / block_m),
+ *             ceil(S / block_n)], nonzero = kept; read only, any alignment.
+ * n_mask      1, H or B * H.
+ * block_m     query rows per mask block: a positive multiple of 128.
+ * block_n     keys per mask block: a positive multiple of 64.
+ * workspace   device buffer of at least fa_fwd_blocksparse_workspace_size
+ *             bytes, 16-byte aligned, not overlapping q, k, v, out, lse or the
+ *             mask; owned by the caller, contents on return unspecified (the
+ *             compacted list of kept tiles).  May be NULL when that size is 0.
+ * workspace_bytes  its size in bytes.
+ * Validation happens before any HIP call (FA_ERR_BLOCKMASK for bad block
+ * sizes or n_mask, FA_ERR_ALIAS when out or lse overlaps the mask).  Enqueues
+ * two kernels on `stream` (one for fp32, which reads the mask directly) and
+ * returns without synchronising.  Returns FA_OK or a negative fa_status_t.
+ */
+int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* out, float* lse,
+                       int64_t B, int64_t H, int64_t S, int64_t D, float scale, int causal,
+                       int64_t window_left, int64_t window_right, int dtype,
+                       const uint8_t* block_mask, int64_t n_mask, int64_t block_m,
+                       int64_t block_n, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * fa_fwd_blocksparse_workspace_size -- the workspace fa_fwd_blocksparse needs,
+ * in *bytes: n_mask * ceil(S / 128) * (4 + 4 * ceil(ceil(S / 64) / 4)) * 4 for
+ * bf16 / fp16 (one list of kept K/V tiles per mask head and Q tile), 0 for
+ * fp32.  Pure function, no HIP call.  Returns FA_OK, FA_ERR_NULL,
+ * FA_ERR_BLOCKMASK (n_mask not 1, H or B * H) or the status fa_fwd_check_args
+ * gives for the shape, head dimension and dtype.
+ */
+int fa_fwd_blocksparse_workspace_size(int64_t B, int64_t H, int64_t S, int64_t D, int dtype,
+                                      int64_t n_mask, int64_t* bytes);
 
 #ifdef __cplusplus
 }

@@ -72,6 +72,8 @@ FA_API const char* fa_status_string(int status) {
         return "the split-KV workspace is NULL, too small, not 16-byte aligned or overlaps an "
                "input or output";
     case FA_ERR_SPLITS: return "n_splits must be in [1, FA_MAX_SPLITS]";
+    case FA_ERR_BLOCKMASK:
+        return "block_m must be a positive multiple of 128, block_n of 64, and n_mask 1, H or B*H";
     default: return "unknown status";
     }
 }
@@ -336,5 +338,72 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* out, 
     a.dtype = dtype;
     a.stream = (hipStream_t)stream;
     const hipError_t e = fa::launch_bwd(a);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+namespace {
+
+// Bytes of a [n_mask, ceil(S / block_m), ceil(S / block_n)] block mask, or -1
+// for block sizes / head counts fa_fwd_blocksparse does not take.
+int64_t block_mask_bytes(int64_t B, int64_t H, int64_t S, int64_t n_mask, int64_t block_m,
+                         int64_t block_n) {
+    if (block_m < 128 || block_m % 128 != 0 || block_n < 64 || block_n % 64 != 0) return -1;
+    if (n_mask != 1 && n_mask != H && n_mask != B * H) return -1;
+    int64_t t, r;
+    if (!mul_ok(n_mask, (S + block_m - 1) / block_m, &t) ||
+        !mul_ok(t, (S + block_n - 1) / block_n, &r))
+        return -1;
+    return r;
+}
+
+}  // namespace
+
+FA_API int fa_fwd_blocksparse_workspace_size(int64_t B, int64_t H, int64_t S, int64_t D, int dtype,
+                                             int64_t n_mask, int64_t* bytes) {
+    if (!bytes) return FA_ERR_NULL;
+    int64_t nbytes, lbytes;
+    const int rc = check_problem(B, H, S, D, 0, -1, -1, dtype, &nbytes, &lbytes);
+    if (rc != FA_OK) return rc;
+    if (n_mask != 1 && n_mask != H && n_mask != B * H) return FA_ERR_BLOCKMASK;
+    // n_mask * ceil(S/128) rows of 4 + ceil(S/64) ints: below 2 * B*H*S*4 + small
+    *bytes = fa::blocksparse_lut_bytes(dtype, S, n_mask);
+    return FA_OK;
+}
+
+FA_API int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* out, float* lse,
+                              int64_t B, int64_t H, int64_t S, int64_t D, float scale, int causal,
+                              int64_t window_left, int64_t window_right, int dtype,
+                              const uint8_t* block_mask, int64_t n_mask, int64_t block_m,
+                              int64_t block_n, void* workspace, int64_t workspace_bytes,
+                              void* stream) {
+    int rc = fa_fwd_check_args(q, k, v, out, lse, B, H, S, D, scale, causal, window_left,
+                               window_right, dtype);
+    if (rc != FA_OK) return rc;
+    if (!block_mask) return FA_ERR_NULL;
+    const int64_t mbytes = block_mask_bytes(B, H, S, n_mask, block_m, block_n);
+    if (mbytes < 0) return FA_ERR_BLOCKMASK;
+    int64_t need = 0;
+    rc = fa_fwd_blocksparse_workspace_size(B, H, S, D, dtype, n_mask, &need);
+    if (rc != FA_OK) return rc;
+    int64_t nbytes = 0, lbytes = 0;
+    (void)check_problem(B, H, S, D, causal, window_left, window_right, dtype, &nbytes, &lbytes);
+    if (overlaps(out, nbytes, block_mask, mbytes) || overlaps(lse, lbytes, block_mask, mbytes))
+        return FA_ERR_ALIAS;
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15u))
+            return FA_ERR_WORKSPACE;
+        const void* others[6] = {q, k, v, out, lse, block_mask};
+        const int64_t sizes[6] = {nbytes, nbytes, nbytes, nbytes, lbytes, mbytes};
+        for (int i = 0; i < 6; ++i)
+            if (overlaps(workspace, need, others[i], sizes[i])) return FA_ERR_WORKSPACE;
+    }
+    fa::LaunchArgs a = make_args(q, k, v, out, lse, B, H, S, D, scale, causal, window_left,
+                                 window_right, dtype, stream);
+    a.bmask = block_mask;
+    a.n_mask = n_mask;
+    a.block_m = block_m;
+    a.block_n = block_n;
+    a.lut = (int*)workspace;
+    const hipError_t e = fa::launch_fwd(a);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -199,11 +199,13 @@ __device__ inline void dma_matrix(__amdgpu_buffer_rsrc_t r, unsigned char* wave_
 // part, in fp32, to part_o [n_splits, B, H, S, D] and part_lse
 // [n_splits, B, H, S], for the merge kernel below (the log-domain merge of the
 // online softmax, applied once across parts).
-template <typename T, int D, int NW, int BN_, bool SPLIT>
+template <typename T, int D, int NW, int BN_, bool SPLIT, bool SPARSE>
 __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ out,
     float* __restrict__ lse, int B, int H, int S, float c, int causal, int wl, int wr, int n_qt,
-    int n_splits, float* __restrict__ part_o, float* __restrict__ part_lse) {
+    int n_splits, float* __restrict__ part_o, float* __restrict__ part_lse,
+    const int* __restrict__ sp_lut, int sp_heads, int sp_stride) {
+    static_assert(!(SPLIT && SPARSE), "a block-sparse launch runs in one part");
     typedef Tile<D, NW, BN_> L;
     constexpr int BN = L::BN;
     constexpr int BM = L::BM;
@@ -255,6 +257,20 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
         kt1 = (int)a1;
         ki0 = (int)b0;
         ki1 = (int)b1;
+    }
+    // SPARSE: the workgroup walks only the kept K/V tiles of its Q tile, in
+    // ascending order: its row of sp_lut holds {kept count, kept tiles below
+    // ki0, kept tiles below ki1, 0, tile 0, tile 1, ...} (sparse_lut_kernel).
+    // From here on kt0, kt1, ki0 and ki1 count positions in that list; the
+    // pipeline steps over positions and maps each to its tile.
+    const int* sp_row = nullptr;
+    if (SPARSE) {
+        const int64_t hm = sp_heads == 1 ? 0 : (sp_heads == H ? (int64_t)h : (int64_t)bh);
+        sp_row = sp_lut + (hm * n_qt + qt) * (int64_t)sp_stride;
+        kt0 = 0;
+        kt1 = __builtin_amdgcn_readfirstlane(sp_row[0]);
+        ki0 = __builtin_amdgcn_readfirstlane(sp_row[1]);
+        ki1 = __builtin_amdgcn_readfirstlane(sp_row[2]);
     }
 
     const int64_t row_stride = (int64_t)H * D;                      // elements between rows
@@ -352,6 +368,14 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
     auto load_v = [&](int kt, unsigned char* buf) __attribute__((always_inline)) {
         dma_matrix<L::DMA_PER_WAVE>(tile_rsrc(v_head, kt), buf + wave * L::DMA_PER_WAVE * 1024,
                                     dma_voff);
+    };
+    // SPARSE: list entry p, read by a vector load (it lands with the step's
+    // K/V loads and is waited for with them; a scalar load would make every
+    // LDS wait of the step wait for it too).  Entries past the count read 0.
+    const __amdgpu_buffer_rsrc_t sp_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(SPARSE ? sp_row + 4 : sp_lut), (short)0, SPARSE ? kt1 * 4 : 0, kBufferFlags);
+    auto sp_entry = [&](int p) __attribute__((always_inline)) {
+        return (int)__builtin_amdgcn_raw_buffer_load_b32(sp_rsrc, 4 * p, 0, 0);
     };
 
     // ---- per-lane LDS operand addresses (bytes within a tile)
@@ -482,11 +506,25 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
         }
     };
 
+    // A block-sparse Q tile may keep no tile at all: its rows have no allowed
+    // key, and the epilogue writes O = 0, LSE = -inf.
+    if (!SPARSE || kt1 > kt0) {
     // ---- prologue: K of the first two tiles, V of the first, scores of the first
     f32x16 sc[KB];  // scores of the current tile (masked)
-    load_k(kt0, lds_k0);
-    if (kt0 + 1 < kt1) load_k(kt0 + 1, lds_k1);
-    load_v(kt0, lds_v0);
+    int tile_a = kt0, tile_b = kt0 + 1;  // tiles of positions kt0, kt0 + 1
+    int sp_t1 = 0;                       // SPARSE: tile of position j + 1 at step j
+    int sp_nx = 0;                       // SPARSE: entry j + 2, in flight from step j - 1
+    if (SPARSE) {
+        tile_a = __builtin_amdgcn_readfirstlane(sp_row[4]);
+        tile_b = kt1 > 1 ? __builtin_amdgcn_readfirstlane(sp_row[5]) : 0;
+    }
+    load_k(tile_a, lds_k0);
+    if (kt0 + 1 < kt1) load_k(tile_b, lds_k1);
+    load_v(tile_a, lds_v0);
+    if (SPARSE) {
+        sp_t1 = tile_b;
+        sp_nx = sp_entry(2);
+    }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     // K/V tiles this wave computes: [kw0, kw1), the tiles of [kt0, kt1) that
@@ -495,8 +533,10 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
     // waves).  The loads and barriers still run over the workgroup's
     // [kt0, kt1), so every wave passes the same barriers.  Padding rows past
     // S take the workgroup's range.
+    // (SPARSE: every wave walks every kept tile; a tile without an allowed key
+    // for some of a wave's rows gives those rows weight 0.)
     int kw0 = kt0, kw1 = kt1;
-    if (qw0 < S) {
+    if (!SPARSE && qw0 < S) {
         int64_t lo, hi;
         key_range(ms, qw0, qw0 + kWaveRows - 1 < S - 1 ? qw0 + kWaveRows - 1 : S - 1, &lo, &hi);
         kw0 = (int)(lo / BN) > kt0 ? (int)(lo / BN) : kt0;
@@ -508,13 +548,14 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
     }
     kw0 = __builtin_amdgcn_readfirstlane(kw0);
     kw1 = __builtin_amdgcn_readfirstlane(kw1);
-    auto first_scores = [&](int kt, unsigned char* kst) __attribute__((always_inline)) {
+    // scores of the tile at position pos (tile number `tile`)
+    auto first_scores = [&](int pos, int tile, unsigned char* kst) __attribute__((always_inline)) {
         qk(sc, kst);
-        if (kt < ki0 || kt >= ki1) apply_mask(sc, kt * BN);
+        if (pos < ki0 || pos >= ki1) apply_mask(sc, tile * BN);
         update_max(sc);
         moved = false;  // O and l are still zero
     };
-    if (kw0 == kt0) first_scores(kt0, lds_k0);
+    if (kw0 == kt0) first_scores(kt0, tile_a, lds_k0);
 
     // ---- one pipelined step for tile j: S_{j+1} = K_{j+1} Q^T and the weights
     // of tile j, then O += P_j V_j and the row max of tile j+1.  STAGE = (j -
@@ -531,12 +572,19 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
         unsigned char* const v_next = ST ? lds_v0 : lds_v1;  // V_{j+1}
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K_{j+1}, V_j have landed
         __syncthreads();  // ... for every wave; every wave is done with tile j-1
+        int tn1 = j + 1, tn2 = j + 2;  // tiles of positions j + 1 and j + 2
+        if (SPARSE) {
+            tn1 = sp_t1;
+            tn2 = __builtin_amdgcn_readfirstlane(sp_nx);
+            sp_t1 = tn2;
+            sp_nx = sp_entry(j + 3);
+        }
         if (!LAST) {
-            if (j + 2 < kt1) load_k(j + 2, k_this);
-            load_v(j + 1, v_next);
+            if (j + 2 < kt1) load_k(tn2, k_this);
+            load_v(tn1, v_next);
         } else {  // this wave's last tile; the workgroup may go on
-            if (j + 2 < kt1) load_k(j + 2, k_this);
-            if (j + 1 < kt1) load_v(j + 1, v_next);
+            if (j + 2 < kt1) load_k(tn2, k_this);
+            if (j + 1 < kt1) load_v(tn1, v_next);
         }
         rescale_if_moved();
         u32x4 p[NCH];
@@ -545,7 +593,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
             qk(sn, k_next);
             softmax(sc, p);
             pv(p, v_this);
-            if (MASK_NEXT) apply_mask(sn, (j + 1) * BN);
+            if (MASK_NEXT) apply_mask(sn, tn1 * BN);
             update_max(sn);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) sc[kb] = sn[kb];
@@ -601,11 +649,13 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
         if (j + 2 < kt1) load_k(j + 2, st ? lds_k1 : lds_k0);
         if (j + 1 < kt1) load_v(j + 1, st ? lds_v0 : lds_v1);
     };
-    for (int j = kt0; j + 1 < kw0; ++j) idle_step(j);
-    if (kw0 > kt0) {  // the step before the wave's first tile: its scores
-        const int j = kw0 - 1;
-        idle_step(j);
-        first_scores(kw0, ((j - kt0) & 1) ? lds_k0 : lds_k1);
+    if (!SPARSE) {
+        for (int j = kt0; j + 1 < kw0; ++j) idle_step(j);
+        if (kw0 > kt0) {  // the step before the wave's first tile: its scores
+            const int j = kw0 - 1;
+            idle_step(j);
+            first_scores(kw0, kw0, ((j - kt0) & 1) ? lds_k0 : lds_k1);
+        }
     }
     // iteration j has a mask-free next tile iff ki0 <= j + 1 < ki1
     const int jl = kw1 - 1;
@@ -620,7 +670,9 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
         step(jl, IntTag<1>{}, BoolTag<false>{}, BoolTag<true>{});
     else
         step(jl, IntTag<0>{}, BoolTag<false>{}, BoolTag<true>{});
-    for (int j = kw1; j < kt1; ++j) idle_step(j);
+    if (!SPARSE)
+        for (int j = kw1; j < kt1; ++j) idle_step(j);
+    }  // kt1 > kt0
 
     // ---- epilogue: O = O_acc / l, LSE = ln2 * (m + log2 l)
     // l == 0 only for a row with no allowed key; a NaN l (NaN scores) propagates
@@ -675,6 +727,54 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
             if (qw0 + r < S) *reinterpret_cast<u32x4*>(orow + (int64_t)(qw0 + r) * row_stride) = x;
         }
     }
+}
+
+// ================================================================ block-sparse
+// Block-sparse attention keeps key j for query i only where the mask byte of
+// (query block i / block_m, key block j / block_n) is nonzero, on top of the
+// causal / window mask ("FlashAttention技术解析：加速GPT训练的核心优化" section
+// 5 lists the block-sparse variant for very long contexts).  block_m is a
+// multiple of the Q tile and block_n of the K/V tile, so a kept block is a
+// set of whole tiles for every row of a Q tile: skipping a dropped tile needs
+// no per-element mask, and a kept one is masked exactly as in the dense case.
+//
+// sparse_lut_kernel compacts, for every (mask head, Q tile), the kept K/V
+// tiles of the tile range the dense kernel would walk into an ascending list:
+// row r = hm * n_qt + qt of lut, sp_stride ints, holds {count, kept tiles
+// below the mask-free range, kept tiles below its end, 0, tiles...}.  One
+// wave per row; lanes take 64 consecutive tiles at a time and place the kept
+// ones by the ballot's prefix count.
+__host__ __device__ constexpr int64_t sparse_lut_stride(int64_t n_kt) {
+    return 4 + (n_kt + 3) / 4 * 4;
+}
+
+template <int BM, int BN>
+__global__ __launch_bounds__(64) void sparse_lut_kernel(
+    const uint8_t* __restrict__ mask, int S, int causal, int wl, int wr, int n_qt, int n_kb,
+    int n_qb, int block_m, int block_n, int sp_stride, int* __restrict__ lut) {
+    const int lane = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const int64_t hm = row / n_qt;
+    const int qt = (int)(row - hm * n_qt);
+    const MaskSpec ms{S, causal, wl, wr};
+    int64_t a0, a1, b0, b1;
+    q_tile_kv_range(ms, qt, BM, BN, &a0, &a1);
+    q_tile_interior_range(ms, (int64_t)qt * BM, BM, BN, a0, a1, &b0, &b1);
+    const uint8_t* const mrow = mask + (hm * n_qb + (int64_t)qt * BM / block_m) * n_kb;
+    int* const out = lut + row * sp_stride;
+    int n = 0, r0 = 0, r1 = 0;
+    for (int64_t t0 = a0; t0 < a1; t0 += 64) {
+        const int64_t t = t0 + lane;
+        const bool kept = t < a1 && mrow[t * BN / block_n] != 0;
+        const uint64_t m = __ballot(kept);
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (kept) out[4 + n + below] = (int)t;
+        n += __popcll(m);
+        r0 += __popcll(m & __ballot(t < b0));
+        r1 += __popcll(m & __ballot(t < b1));
+    }
+    if (lane == 0) *reinterpret_cast<int4*>(out) = int4{n, r0, r1, 0};
 }
 
 // ================================================================ backward
@@ -1223,11 +1323,14 @@ template <int D> struct Lds32 {
     static constexpr int VS = D + 4;
 };
 
-template <int D>
+// SPARSE: K/V tiles whose mask byte is 0 are skipped (bmask [sp_heads, n_qb,
+// n_kb]; block_m a multiple of the Q tile, block_n of the K/V tile).
+template <int D, bool SPARSE>
 __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ out, float* __restrict__ lse, int B, int H, int S, float c, int causal,
-    int wl, int wr, int n_qt) {
+    int wl, int wr, int n_qt, const uint8_t* __restrict__ bmask, int sp_heads, int n_qb, int n_kb,
+    int block_m, int block_n) {
     typedef Lds32<D> L;
     constexpr int BN = L::BN;
     constexpr int DB = D / 32;
@@ -1247,6 +1350,11 @@ __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
     const int64_t head_base = ((int64_t)bb * S * H + h) * D;
     const int qw0 = qt * kBM32 + wave * kWaveRows;
     const int qrow = qw0 + ql;
+    const uint8_t* mrow = nullptr;  // SPARSE: the Q tile's row of the block mask
+    if (SPARSE) {
+        const int64_t hm = sp_heads == 1 ? 0 : (sp_heads == H ? (int64_t)h : (int64_t)bh);
+        mrow = bmask + (hm * n_qb + (int64_t)qt * kBM32 / block_m) * n_kb;
+    }
 
     // Q fragment: lane supplies d = 2*kk + hh of its row
     float qf[D / 2];
@@ -1263,6 +1371,7 @@ __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
 
     for (int64_t kt = kt0; kt < kt1; ++kt) {
         const int64_t k0 = kt * BN;
+        if (SPARSE && mrow[k0 / block_n] == 0) continue;  // the same for the whole workgroup
         __syncthreads();
         for (int id = tid; id < BN * (D / 4); id += kThreads32) {
             const int r = id / (D / 4), cc = id % (D / 4);
@@ -1353,17 +1462,35 @@ static hipError_t launch_mfma_cfg(const LaunchArgs& a) {
     constexpr int BM = Tile<D, NW, BN>::BM;
     const int n_qt = (int)((a.S + BM - 1) / BM);
     const int64_t n_wg = a.B * a.H * n_qt;
-    if (a.n_splits <= 1) {
-        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false>), dim3((unsigned)n_wg),
+    if (a.bmask) {  // block-sparse: compact the kept tiles, then walk them
+        const int n_kt = (int)((a.S + BN - 1) / BN);
+        const int stride = (int)sparse_lut_stride(n_kt);
+        hipLaunchKernelGGL((sparse_lut_kernel<BM, BN>), dim3((unsigned)(a.n_mask * n_qt)), dim3(64),
+                           0, a.stream, a.bmask, (int)a.S, a.causal, (int)a.wl, (int)a.wr, n_qt,
+                           (int)((a.S + a.block_n - 1) / a.block_n),
+                           (int)((a.S + a.block_m - 1) / a.block_m), (int)a.block_m,
+                           (int)a.block_n, stride, a.lut);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, true>), dim3((unsigned)n_wg),
                            dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
                            (T*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl,
-                           (int)a.wr, n_qt, 1, nullptr, nullptr);
+                           (int)a.wr, n_qt, 1, nullptr, nullptr, (const int*)a.lut, (int)a.n_mask,
+                           stride);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, true>), dim3((unsigned)(n_wg * a.n_splits)),
-                       dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
-                       (T*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl,
-                       (int)a.wr, n_qt, a.n_splits, a.part_o, a.part_lse);
+    if (a.n_splits <= 1) {
+        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, false>), dim3((unsigned)n_wg),
+                           dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
+                           (T*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl,
+                           (int)a.wr, n_qt, 1, nullptr, nullptr, nullptr, 0, 0);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, true, false>),
+                       dim3((unsigned)(n_wg * a.n_splits)), dim3(NW * 64), 0, a.stream,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B,
+                       (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, a.n_splits,
+                       a.part_o, a.part_lse, nullptr, 0, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int RPB = kMergeThreads / (D / 4);
@@ -1419,9 +1546,19 @@ template <int D>
 static hipError_t launch_fp32(const LaunchArgs& a) {
     const int n_qt = (int)((a.S + kBM32 - 1) / kBM32);
     const int64_t n_wg = a.B * a.H * n_qt;
-    hipLaunchKernelGGL((fa_fwd_fp32_kernel<D>), dim3((unsigned)n_wg), dim3(kThreads32), 0, a.stream,
-                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.out, a.lse,
-                       (int)a.B, (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt);
+    if (a.bmask) {
+        hipLaunchKernelGGL((fa_fwd_fp32_kernel<D, true>), dim3((unsigned)n_wg), dim3(kThreads32), 0,
+                           a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                           (float*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S, a.c, a.causal,
+                           (int)a.wl, (int)a.wr, n_qt, a.bmask, (int)a.n_mask,
+                           (int)((a.S + a.block_m - 1) / a.block_m),
+                           (int)((a.S + a.block_n - 1) / a.block_n), (int)a.block_m, (int)a.block_n);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((fa_fwd_fp32_kernel<D, false>), dim3((unsigned)n_wg), dim3(kThreads32), 0,
+                       a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
+                       (float*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl,
+                       (int)a.wr, n_qt, nullptr, 0, 0, 0, 1, 1);
     return hipGetLastError();
 }
 
@@ -1475,6 +1612,13 @@ int auto_splits(const LaunchArgs& a) {
         return a.D == 64 ? auto_splits_cfg<_Float16, 64>(a) : auto_splits_cfg<_Float16, 128>(a);
     default: return 1;  // fp32 inputs run in one part
     }
+}
+
+int64_t blocksparse_lut_bytes(int dtype, int64_t S, int64_t n_mask) {
+    if (dtype == kDtypeFp32) return 0;  // the fp32 kernel reads the mask itself
+    constexpr int BM = kMfmaWaves * kWaveRows;
+    const int64_t n_qt = (S + BM - 1) / BM, n_kt = (S + kMfmaKeys - 1) / kMfmaKeys;
+    return n_mask * n_qt * sparse_lut_stride(n_kt) * 4;
 }
 
 int64_t q_tile_rows(int dtype, int64_t, int64_t, int64_t, int64_t) {

@@ -29,6 +29,13 @@ struct LaunchArgs {
     int n_splits = 1;
     float* part_o = nullptr;
     float* part_lse = nullptr;
+    // block-sparse launch: one byte per (query block, key block) in bmask
+    // [n_mask, ceil(S / block_m), ceil(S / block_n)], nonzero = the block is
+    // kept.  bf16 / fp16 first compact every Q tile's kept K/V tiles into
+    // `lut` (blocksparse_lut_bytes); fp32 reads bmask directly.
+    const uint8_t* bmask = nullptr;
+    int64_t n_mask = 0, block_m = 0, block_n = 0;
+    int* lut = nullptr;
 };
 
 // The backward pass: gradients for an output gradient dout (bf16 / fp16).
@@ -57,6 +64,9 @@ hipError_t launch_bwd(const BwdArgs& a);
 // Enqueues the forward kernel (and, for a split launch, the merge kernel) for
 // validated arguments.
 hipError_t launch_fwd(const LaunchArgs& a);
+// Bytes of the compacted tile lists a block-sparse launch needs (0 for fp32).
+int64_t blocksparse_lut_bytes(int dtype, int64_t S, int64_t n_mask);
+
 // K/V parts per Q tile that fill the current device for this problem (1 for
 // fp32 inputs, or when the device cannot be queried).
 int auto_splits(const LaunchArgs& a);

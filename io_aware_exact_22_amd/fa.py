@@ -3,8 +3,9 @@
 Same names as the C ABI: ``fa_fwd``, ``fa_fwd_check_args``,
 ``fa_status_string``, ``fa_fwd_tile_schedule``, ``fa_fwd_workgroup_tile``, ``fa_fwd_splitkv``,
 ``fa_fwd_splitkv_workspace_size``, ``fa_fwd_splitkv_auto_splits``, ``fa_bwd``,
-``fa_bwd_workspace_size``; plus ``flash_attn_fwd`` (and ``flash_attn_fwd_splitkv``,
-``flash_attn_bwd``), the
+``fa_bwd_workspace_size``, ``fa_fwd_blocksparse``, ``fa_fwd_blocksparse_workspace_size``;
+plus ``flash_attn_fwd`` (and ``flash_attn_fwd_splitkv``, ``flash_attn_bwd``,
+``flash_attn_fwd_blocksparse``), the
 tensor-level call that mirrors the pages' ``flash_attention(q, k, v,
 softmax_scale=None, causal=..., window_size=(-1, -1))`` argument list
 ("FlashAttention技术解析：加速GPT训练的核心优化", section 2.2).  This module only
@@ -80,6 +81,11 @@ def _load():
         lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                ctypes.c_float, cint, i64, i64, cint, vp, i64, vp]
         lib.fa_bwd.restype = cint
+        lib.fa_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float,
+                                           cint, i64, i64, cint, vp, i64, i64, i64, vp, i64, vp]
+        lib.fa_fwd_blocksparse.restype = cint
+        lib.fa_fwd_blocksparse_workspace_size.argtypes = [i64, i64, i64, i64, cint, i64, p64]
+        lib.fa_fwd_blocksparse_workspace_size.restype = cint
         lib.fa_bwd_workspace_size.argtypes = [i64, i64, i64, i64, cint, p64]
         lib.fa_bwd_workspace_size.restype = cint
         _lib = lib
@@ -178,6 +184,25 @@ def fa_bwd_workspace_size(B: int, H: int, S: int, D: int, dtype: int) -> int:
     rc = _load().fa_bwd_workspace_size(B, H, S, D, dtype, ctypes.byref(n))
     if rc != 0:
         raise FaError(rc, "fa_bwd_workspace_size")
+    return n.value
+
+
+def fa_fwd_blocksparse(q: int, k: int, v: int, out: int, lse: int, B: int, H: int, S: int, D: int,
+                       scale: float, causal: int, window_left: int, window_right: int, dtype: int,
+                       block_mask: int, n_mask: int, block_m: int, block_n: int, workspace: int,
+                       workspace_bytes: int, stream: int | None) -> int:
+    """The block-sparse C entry point with raw device pointers (ints); returns the status."""
+    return _load().fa_fwd_blocksparse(q, k, v, out, lse, B, H, S, D, scale, causal, window_left,
+                                      window_right, dtype, block_mask, n_mask, block_m, block_n,
+                                      workspace, workspace_bytes, stream)
+
+
+def fa_fwd_blocksparse_workspace_size(B: int, H: int, S: int, D: int, dtype: int,
+                                      n_mask: int) -> int:
+    n = ctypes.c_int64()
+    rc = _load().fa_fwd_blocksparse_workspace_size(B, H, S, D, dtype, n_mask, ctypes.byref(n))
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_blocksparse_workspace_size")
     return n.value
 
 
@@ -280,6 +305,68 @@ def flash_attn_fwd_splitkv(q, k, v, softmax_scale: float | None = None, causal: 
                             n_splits, ws_ptr or None, ws_bytes, st.cuda_stream)
     if rc != 0:
         raise FaError(rc, "fa_fwd_splitkv")
+    return out, lse
+
+
+def flash_attn_fwd_blocksparse(q, k, v, block_mask, block_m: int, block_n: int,
+                               softmax_scale: float | None = None, causal: bool = False,
+                               window_size=(-1, -1), out=None, lse=None, workspace=None,
+                               stream=None):
+    """flash_attn_fwd restricted to the blocks ``block_mask`` keeps: key j is
+    allowed for query i of head (b, h) only where
+    block_mask[hm, i // block_m, j // block_n] != 0 (hm = 0, h or b * H + h
+    for a mask of 1, H or B * H matrices).  block_mask: a contiguous uint8 or
+    bool GPU tensor [n_mask, ceil(S / block_m), ceil(S / block_n)] (2-D means
+    n_mask = 1); block_m a multiple of 128, block_n of 64.  The workspace (the
+    list of kept tiles) is a GPU tensor of at least
+    fa_fwd_blocksparse_workspace_size bytes, allocated here when None.
+    Returns (out, lse) like flash_attn_fwd."""
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise TypeError(f"{name} must be a GPU tensor")
+        if t.dim() != 4 or t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must share shape [B, S, H, D], dtype and device")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [B, S, H, D]")
+    if not isinstance(block_mask, torch.Tensor) or block_mask.device != q.device:
+        raise TypeError("block_mask must be a tensor on q's device")
+    if block_mask.dtype not in (torch.uint8, torch.bool) or not block_mask.is_contiguous():
+        raise ValueError("block_mask must be a contiguous uint8 or bool tensor")
+    mask = block_mask.view(torch.uint8) if block_mask.dtype == torch.bool else block_mask
+    if mask.dim() == 2:
+        mask = mask.unsqueeze(0)
+    B, S, H, D = q.shape
+    n_qb, n_kb = -(-S // int(block_m)), -(-S // int(block_n))
+    if mask.dim() != 3 or tuple(mask.shape[1:]) != (n_qb, n_kb):
+        raise ValueError(f"block_mask must be [n_mask, {n_qb}, {n_kb}] for S={S}, "
+                         f"block_m={block_m}, block_n={block_n}")
+    n_mask = mask.shape[0]
+    dtype = _dtype_code(q)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    wl, wr = (int(x) for x in window_size)
+    need = fa_fwd_blocksparse_workspace_size(B, H, S, D, dtype, n_mask)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 tensor [B, H, S]")
+    if workspace is None and need > 0:
+        workspace = torch.empty((need + 3) // 4, dtype=torch.int32, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        rc = fa_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), B, H, S, D, scale, int(bool(causal)), wl, wr,
+                                dtype, mask.data_ptr(), n_mask, int(block_m), int(block_n),
+                                ws_ptr or None, ws_bytes, st.cuda_stream)
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_blocksparse")
     return out, lse
 
 

@@ -27,7 +27,8 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == {"fa_fwd", "fa_fwd_check_args", "fa_status_string", "fa_fwd_tile_schedule",
                           "fa_fwd_workgroup_tile", "fa_fwd_splitkv",
                           "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv_auto_splits",
-                          "fa_bwd", "fa_bwd_workspace_size"}
+                          "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_blocksparse",
+                          "fa_fwd_blocksparse_workspace_size"}
     lib = ctypes.CDLL(fa.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in range(0, -12, -1):
+    for st in range(0, -13, -1):
         s = fa.fa_status_string(st)
         assert s and s != "unknown status"
     assert fa.fa_status_string(-99) == "unknown status"
@@ -150,6 +151,42 @@ def test_bwd_rejects_before_any_hip_call(kw, status):
     rc = fa.fa_bwd(a["q"], a["k"], a["v"], a["out"], a["lse"], a["dout"], a["dq"], a["dk"], a["dv"],
                    a["B"], a["H"], a["S"], a["D"], a["scale"], a["causal"], a["window_left"],
                    a["window_right"], a["dtype"], a["ws"] or None, a["wsb"], None)
+    assert rc == status
+
+
+@pytest.mark.parametrize("B,H,S,nm,dtype", [(1, 16, 16384, 1, fa.FA_DTYPE_BF16),
+                                             (2, 4, 300, 8, fa.FA_DTYPE_FP16),
+                                             (2, 4, 300, 4, fa.FA_DTYPE_BF16),
+                                             (2, 4, 300, 1, fa.FA_DTYPE_FP32)])
+def test_blocksparse_workspace_size(B, H, S, nm, dtype):
+    """One list row per (mask head, 128-row Q tile): a 4-int header and the
+    64-key tile count rounded up to 4 ints; nothing for fp32."""
+    got = fa.fa_fwd_blocksparse_workspace_size(B, H, S, 128, dtype, nm)
+    n_qt, n_kt = -(-S // 128), -(-S // 64)
+    want = 0 if dtype == fa.FA_DTYPE_FP32 else nm * n_qt * (4 + -(-n_kt // 4) * 4) * 4
+    assert got == want
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_fwd_blocksparse_workspace_size(B, H, S, 128, dtype, 3)
+    assert e.value.status == -12
+
+
+MASK = 11 << 32  # a fake block-mask address disjoint from everything above
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"mask": 0}, -1), ({"bm": 64}, -12), ({"bm": 192}, -12), ({"bm": 0}, -12), ({"bn": 32}, -12),
+    ({"bn": 96}, -12), ({"nm": 3}, -12), ({"nm": 0}, -12), ({"ws": 0}, -10), ({"wsb": 16}, -10),
+    ({"ws": WS + 8}, -10), ({"ws": Q}, -10), ({"ws": MASK}, -10), ({"out": MASK}, -8),
+    ({"lse": MASK}, -8), ({"D": 80}, -3), ({"scale": float("nan")}, -6), ({"q": 0}, -1),
+])
+def test_blocksparse_rejects_before_any_hip_call(kw, status):
+    """Invalid arguments return their status without touching the GPU."""
+    a = dict(GOOD, mask=MASK, nm=4, bm=128, bn=64, ws=WS, wsb=1 << 30)
+    a.update(kw)
+    rc = fa.fa_fwd_blocksparse(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["H"], a["S"],
+                               a["D"], a["scale"], a["causal"], a["window_left"],
+                               a["window_right"], a["dtype"], a["mask"] or None, a["nm"], a["bm"],
+                               a["bn"], a["ws"] or None, a["wsb"], None)
     assert rc == status
 
 
