@@ -30,6 +30,8 @@ if ROOT not in sys.path:
 
 METRIC = "attention fwd TFLOPS (4·B·H·S·S_eff·D/t) and % of MI355X bf16 MFMA peak"
 METRIC_BWD = "attention bwd TFLOPS (10·B·H·S·S_eff·D/t: five products) and % of MI355X bf16 MFMA peak"
+METRIC_BS = ("attention fwd TFLOPS over the pairs a block mask keeps (4·B·H·pairs·D/t) and % of "
+             "MI355X bf16 MFMA peak")
 PEAK_MFMA_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp32": 157.3}  # MI355X dense, 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "causal_16k"
@@ -49,6 +51,30 @@ def allowed_pairs(S: int, causal: bool, window) -> int:
     if causal:
         hi = np.minimum(hi, i)
     return int(np.maximum(0, hi - lo + 1).sum())
+
+
+def blocksparse_pairs(S: int, causal: bool, window, mask, bm: int, bn: int, r0: int = 0,
+                      r1: int | None = None) -> int:
+    """Allowed (query, key) pairs of rows [r0, r1) under one head's block mask
+    [n_qb, n_kb]: per row, the overlap of each kept key block with the row's
+    window interval."""
+    import numpy as np
+
+    r1 = S if r1 is None else r1
+    wl, wr = window
+    mask = np.asarray(mask)
+    total = 0
+    for qb in range(r0 // bm, (r1 + bm - 1) // bm):
+        i = np.arange(max(r0, qb * bm), min(r1, (qb + 1) * bm), dtype=np.int64)
+        lo = np.zeros_like(i) if wl < 0 else np.maximum(0, i - wl)
+        hi = np.full_like(i, S - 1) if wr < 0 else np.minimum(S - 1, i + wr)
+        if causal:
+            hi = np.minimum(hi, i)
+        c0 = np.nonzero(mask[qb])[0].astype(np.int64) * bn
+        c1 = np.minimum(S, c0 + bn)
+        cnt = np.minimum(c1[None, :] - 1, hi[:, None]) - np.maximum(c0[None, :], lo[:, None]) + 1
+        total += int(np.maximum(cnt, 0).sum())
+    return total
 
 
 def kernel_hash() -> str:
@@ -104,6 +130,40 @@ def cpu_baseline(w, q, k, v, target_s: float = 15.0):
     }
 
 
+def cpu_baseline_blocksparse(w, q, k, v, mask, bm, bn, target_s: float = 15.0):
+    """Time the CPU oracle's block-sparse rows: chunks of 512 rows of batch 0,
+    from the middle of head 0 on through the following rows and heads, until
+    about target_s seconds have run; report the rate on the metric's FLOP count
+    for the rows done."""
+    import oracle
+
+    threads = min(16, len(os.sched_getaffinity(0)))
+    CH = 512
+    chunks = [(h, r) for h in range(w.H) for r in range(0, w.S, CH)]
+    first = (w.S // 2) // CH
+    chunks = chunks[first:] + chunks[:first]
+    fl, dt, rows = 0.0, 0.0, 0
+    for h, r0 in chunks:
+        r1 = min(w.S, r0 + CH)
+        t0 = time.perf_counter()
+        oracle.fwd_rows_blocksparse(q, k, v, w.scale, mask, bm, bn, w.causal, w.window, 0, h, r0,
+                                    r1, nthreads=threads)
+        dt += time.perf_counter() - t0
+        fl += 4.0 * blocksparse_pairs(w.S, w.causal, w.window, mask[0], bm, bn, r0, r1) * w.D
+        rows += r1 - r0
+        if dt >= target_s:
+            break
+    return {
+        "value": fl / dt / 1e12,
+        "unit": "TFLOPS",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{w.name} under the block mask: {rows} rows of batch 0 in chunks of {CH} from "
+                   f"row {first * CH} of head 0 on, fp64 oracle materialising those rows' scores; "
+                   f"{fl / 1e9:.2f} GFLOP (metric count) in {dt:.1f} s on {threads} threads"),
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +177,11 @@ def main() -> int:
     ap.add_argument("--splitkv", type=int, default=-1,
                     help="time fa_fwd_splitkv with this many K/V parts per Q tile (0 = the "
                          "library's choice for the device) instead of fa_fwd")
+    ap.add_argument("--blocksparse", default="",
+                    help="time fa_fwd_blocksparse under a local + global block mask on 128 x 64 "
+                         "blocks: 'local:KEYS[:GLOBAL]' keeps, for each 128-row block, the KEYS "
+                         "keys ending at its last row and the first GLOBAL 64-key blocks "
+                         "(default 1)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the benchmark, run --steps plain device copies of this many "
                          "MiB (the reference kernel for scaling HBM byte counters)")
@@ -156,7 +221,32 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
 
     n_splits = None
-    if args.backward:
+    bs = None  # block-sparse: (mask [1, n_qb, n_kb] on the CPU, description)
+    if args.blocksparse:
+        from fa_inputs import local_global_block_mask
+
+        parts = args.blocksparse.split(":")
+        if parts[0] != "local" or len(parts) not in (2, 3):
+            print("bench.py: --blocksparse takes local:KEYS[:GLOBAL]", file=sys.stderr)
+            return 2
+        local_keys, glob = int(parts[1]), int(parts[2]) if len(parts) == 3 else 1
+        bm, bn = 128, 64
+        mask = local_global_block_mask(-(-w.S // bm), -(-w.S // bn), bm, bn, local_keys, glob)
+        dcode = {torch.float32: fa.FA_DTYPE_FP32, torch.float16: fa.FA_DTYPE_FP16,
+                 torch.bfloat16: fa.FA_DTYPE_BF16}[w.dtype]
+        need = fa.fa_fwd_blocksparse_workspace_size(w.B, w.H, w.S, w.D, dcode, 1)
+        ws = torch.empty(max(1, need // 4), dtype=torch.int32, device=dev)
+        md = mask.to(dev)
+        bs = (mask, {"pattern": "local+global", "local_keys": local_keys,
+                     "global_key_blocks": glob, "block_m": bm, "block_n": bn,
+                     "kept_blocks": int(mask.sum()),
+                     "block_density": float(mask.float().mean())})
+
+        def step():
+            fa.flash_attn_fwd_blocksparse(qd, kd, vd, md, bm, bn, softmax_scale=w.scale,
+                                          causal=w.causal, window_size=w.window, out=out, lse=lse,
+                                          workspace=ws, stream=stream)
+    elif args.backward:
         out, lse = fa.flash_attn_fwd(qd, kd, vd, softmax_scale=w.scale, causal=w.causal,
                                      window_size=w.window, stream=stream)
         g = torch.Generator(device="cpu")
@@ -201,7 +291,10 @@ def main() -> int:
     wall = time.perf_counter() - t0
     launch_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
 
-    pairs = allowed_pairs(w.S, w.causal, w.window)
+    if bs is not None:
+        pairs = blocksparse_pairs(w.S, w.causal, w.window, bs[0][0], 128, 64)
+    else:
+        pairs = allowed_pairs(w.S, w.causal, w.window)
     s_eff = pairs / w.S
     # the backward's five products (S, dP, dV, dK, dQ) against the forward's two
     flops = (10.0 if args.backward else 4.0) * w.B * w.H * pairs * w.D
@@ -225,7 +318,8 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": kern_tflops, "peak": peak, "unit": "TFLOP/s",
                 "frac": kern_tflops / peak}
     # the recorded counters are those of fa_fwd on its default workload
-    roof["traffic"] = None if (args.backward or n_splits is not None) else measured_traffic(w.name)
+    roof["traffic"] = (None if (args.backward or n_splits is not None or bs is not None)
+                       else measured_traffic(w.name))
     roof["kernel_ms"] = avg_launch_ms
     roof["algorithmic_flops_per_launch"] = flops
     roof["algorithmic_bytes_per_launch"] = alg_bytes
@@ -238,7 +332,7 @@ def main() -> int:
         return 1
 
     rec = {
-        "metric": METRIC_BWD if args.backward else METRIC,
+        "metric": METRIC_BWD if args.backward else METRIC_BS if bs is not None else METRIC,
         "value": tflops,
         "unit": "TFLOPS",
         "n_gpus": 1,
@@ -254,12 +348,15 @@ def main() -> int:
         "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
                    "causal": w.causal, "window": list(w.window), "S_eff": s_eff,
                    "flops_per_step": flops, "parallelism": "single GPU",
-                   "entry": ("fa_bwd" if args.backward else
+                   "entry": ("fa_bwd" if args.backward else "fa_fwd_blocksparse" if bs else
                              "fa_fwd" if n_splits is None else "fa_fwd_splitkv"),
-                   **({} if n_splits is None else {"n_splits": n_splits})},
+                   **({} if n_splits is None else {"n_splits": n_splits}),
+                   **({} if bs is None else {"block_mask": bs[1]})},
         "roofline": roof,
     }
-    if not args.no_cpu_baseline and not args.backward and n_splits is None:
+    if not args.no_cpu_baseline and bs is not None:
+        rec["cpu_baseline"] = cpu_baseline_blocksparse(w, q, k, v, bs[0].numpy(), 128, 64)
+    elif not args.no_cpu_baseline and not args.backward and n_splits is None:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v)
     else:
         rec["cpu_baseline"] = None

@@ -56,6 +56,10 @@ WORKLOADS = {
     # one GPU's share of causal_16k split by heads over 8 GPUs (2 of 16 heads):
     # a grid of one workgroup per compute unit, the case split-KV is for
     "causal_16k_h2": Workload("causal_16k_h2", 1, 2, 16384, 128, torch.bfloat16, True, (-1, -1), 7),
+    # a million-token causal sequence, the long-context case block-sparse
+    # attention is for (FlashAttention技术解析 page, section 5); only run under a
+    # block mask
+    "causal_1m_h8": Workload("causal_1m_h8", 1, 8, 1 << 20, 128, torch.bfloat16, True, (-1, -1), 8),
 }
 
 

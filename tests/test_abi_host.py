@@ -293,6 +293,28 @@ def test_bench_pair_count_matches_oracle(S, causal, window):
     assert bench.allowed_pairs(S, causal, window) == oracle.allowed_pairs(S, causal, window)
 
 
+@pytest.mark.parametrize("S,causal,window,bm,bn", [(1000, True, (-1, -1), 128, 64),
+                                                   (777, False, (100, 30), 256, 128),
+                                                   (640, True, (200, -1), 128, 192)])
+def test_bench_blocksparse_pair_count_brute_force(S, causal, window, bm, bn):
+    """bench.py's block-sparse pair count against a brute-force count of the
+    expanded element mask."""
+    import numpy as np
+
+    import bench
+    from fa_inputs import local_global_block_mask, random_block_mask
+
+    for mask in (random_block_mask(1, -(-S // bm), -(-S // bn), 0.4, S)[0].numpy(),
+                 local_global_block_mask(-(-S // bm), -(-S // bn), bm, bn, 300, 1)[0].numpy()):
+        el = np.repeat(np.repeat(mask.astype(bool), bm, 0), bn, 1)[:S, :S]
+        i, j = np.meshgrid(np.arange(S), np.arange(S), indexing="ij")
+        ok = el & ((not causal) | (j <= i)) & ((window[0] < 0) | (i - j <= window[0])) \
+            & ((window[1] < 0) | (j - i <= window[1]))
+        assert bench.blocksparse_pairs(S, causal, window, mask, bm, bn) == int(ok.sum())
+        assert bench.blocksparse_pairs(S, causal, window, mask, bm, bn, 130, 400) == \
+            int(ok[130:400].sum())
+
+
 def test_bench_refuses_several_gpus():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "8"],
                        capture_output=True, text=True, timeout=120)
