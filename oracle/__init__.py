@@ -79,6 +79,8 @@ def _load():
                                                        i64, i64, i64, i64, i64, i64, vp, vp,
                                                        ctypes.c_int]
         lib.fa_oracle_fwd_rows_blocksparse.restype = ctypes.c_int
+        lib.fa_oracle_gather_pages.argtypes = [vp, i64, i64, i64, vp, i64, i64, i64, i64, i64, vp]
+        lib.fa_oracle_gather_pages.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -199,6 +201,41 @@ def fwd_rows_blocksparse(q, k, v, scale: float, mask, block_m: int, block_n: int
     if rc != 0:
         raise ValueError(f"oracle: fa_oracle_fwd_rows_blocksparse failed ({rc})")
     return out, lse
+
+
+def gather_pages(pages, block_table, S: int):
+    """Contiguous [B, S, H, D] keys (or values) from a paged pool ``pages``
+    [num_pages, page_size, H, D] (CPU tensor) and ``block_table`` [B, n] int32:
+    row j of batch b is row j % page_size of page block_table[b, j // page_size]
+    ("突破大模型训练瓶颈：Flash-Attention编译优化与内存占用解决方案", section Paged KV
+    Cache支持, names the block table)."""
+    import torch
+
+    if not isinstance(pages, torch.Tensor) or pages.device.type != "cpu" or not pages.is_contiguous():
+        raise TypeError("oracle: pages must be a contiguous CPU tensor")
+    bt = np.ascontiguousarray(np.asarray(block_table), dtype=np.int32)
+    if pages.dim() != 4 or bt.ndim != 2:
+        raise ValueError("oracle: pages [num_pages, page_size, H, D], block_table [B, n]")
+    num_pages, page_size, H, D = pages.shape
+    B = bt.shape[0]
+    dense = torch.empty((B, S, H, D), dtype=pages.dtype)
+    rc = _load().fa_oracle_gather_pages(pages.data_ptr(), pages.element_size(), num_pages,
+                                        page_size, bt.ctypes.data, bt.shape[1], B, S, H, D,
+                                        dense.data_ptr())
+    if rc != 0:
+        raise ValueError("oracle: bad block table or page geometry")
+    return dense
+
+
+def fwd_paged(q, k_pages, v_pages, block_table, scale: float, causal: bool = False,
+              window_size=(-1, -1), nthreads: int = 0):
+    """Exact attention with keys and values in paged pools: the pools are
+    gathered by the block table (gather_pages), then ``fwd`` runs on them.
+    q: [B, S, H, D]; k_pages, v_pages: [num_pages, page_size, H, D]."""
+    S = q.shape[1]
+    k = gather_pages(k_pages, block_table, S)
+    v = gather_pages(v_pages, block_table, S)
+    return fwd(q, k, v, scale, causal, window_size, nthreads)
 
 
 def bwd(q, k, v, dout, scale: float, causal: bool = False, window_size=(-1, -1),

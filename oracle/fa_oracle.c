@@ -57,6 +57,16 @@
  * the causal and window masks, is the one taken.  A row whose blocks are all
  * off has no allowed key: O = 0, LSE = -inf, as above.
  *
+ * Paged K/V ("突破大模型训练瓶颈：Flash-Attention编译优化与内存占用解决方案",
+ * section Paged KV Cache支持: the K/V cache is kept in non-contiguous blocks, like
+ * memory pages of an operating system, found through a block table) changes
+ * where keys and values are read, not what is computed: key j of batch b is
+ * row j % page_size of page block_table[b][j / page_size] of the pools
+ * k_pages / v_pages [num_pages, page_size, H, D].  fa_oracle_fwd_paged gathers
+ * those rows into contiguous [B, S, H, D] tensors and runs the definition
+ * above on them.  Reading: the pages give the block table and nothing else;
+ * one S for queries and keys, as above.
+ *
  * Build: gcc -O2 -fopenmp -shared -fPIC fa_oracle.c -o libfa_oracle.so -lm
  * No -ffast-math: the oracle depends on IEEE inf/NaN semantics.
  */
@@ -339,6 +349,30 @@ int fa_oracle_fwd_blocksparse(const void* q, const void* k, const void* v, int d
                 memcpy(out + ((b * S + i) * H + h) * D, rows + i * D, sizeof(double) * (size_t)D);
         }
     free(rows);
+    return 0;
+}
+
+/*
+ * Gathers one paged pool [num_pages, page_size, H, D] (element size esize
+ * bytes) into a contiguous [B, S, H, D] tensor by the block table
+ * [B, table_stride]: row j of batch b comes from page block_table[b *
+ * table_stride + j / page_size], row j % page_size.  Returns -1 when a page
+ * index the sequence uses lies outside [0, num_pages).
+ */
+int fa_oracle_gather_pages(const void* pages, int64_t esize, int64_t num_pages,
+                           int64_t page_size, const int32_t* block_table, int64_t table_stride,
+                           int64_t B, int64_t S, int64_t H, int64_t D, void* dense) {
+    if (!pages || !block_table || !dense || esize < 1 || page_size < 1 || num_pages < 1) return -1;
+    if (table_stride < (S + page_size - 1) / page_size) return -1;
+    const int64_t row_bytes = H * D * esize;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t j = 0; j < S; ++j) {
+            const int64_t page = block_table[b * table_stride + j / page_size];
+            if (page < 0 || page >= num_pages) return -1;
+            const int64_t src_row = page * page_size + j % page_size;
+            memcpy((char*)dense + (b * S + j) * row_bytes, (const char*)pages + src_row * row_bytes,
+                   (size_t)row_bytes);
+        }
     return 0;
 }
 

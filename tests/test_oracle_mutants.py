@@ -1,6 +1,7 @@
 """Plants plausible mistakes in copies of the CPU oracle (on the CPU only) and
-checks that the pins in test_oracle_pins.py, test_oracle_bwd_pins.py and
-test_oracle_blocksparse_pins.py catch every one of them."""
+checks that the pins in test_oracle_pins.py, test_oracle_bwd_pins.py,
+test_oracle_blocksparse_pins.py and test_oracle_paged_pins.py catch every one of
+them."""
 import os
 import subprocess
 import sys
@@ -40,6 +41,13 @@ MUTANTS = {
                       "return mask[(i / block_m) * (n_kb - 1) + j / block_n] != 0;"),
     "bs_head_index": ("hm = b * H + h;", "hm = h * B + b;"),
     "bs_per_head_ignored": ("hm = h;", "hm = 0;"),
+    # paged gather
+    "paged_div_mod_swapped": ("const int64_t page = block_table[b * table_stride + j / page_size];",
+                              "const int64_t page = block_table[b * table_stride + j % page_size];"),
+    "paged_row_in_page": ("const int64_t src_row = page * page_size + j % page_size;",
+                          "const int64_t src_row = page * page_size + j / page_size;"),
+    "paged_table_stride": ("const int64_t page = block_table[b * table_stride + j / page_size];",
+                           "const int64_t page = block_table[b * (S + page_size - 1) / page_size + j / page_size];"),
     "bs_only_in_scores": ("!orc_block_on(bmask, i, j, block_m, block_n, n_kb))\n                continue;",
                           "0)\n                continue;"),
 }
@@ -59,6 +67,7 @@ def test_pins_catch_mutant(name, tmp_path):
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"),
                         os.path.join(ROOT, "tests", "test_oracle_bwd_pins.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_blocksparse_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_blocksparse_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_paged_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
