@@ -55,9 +55,12 @@ typedef enum {
     FA_ERR_WORKSPACE = -10, /* a workspace argument is NULL, too small, not 16-byte
                                aligned, or overlapping an input or output */
     FA_ERR_SPLITS = -11,  /* fa_fwd_splitkv: n_splits outside [1, FA_MAX_SPLITS] */
-    FA_ERR_BLOCKMASK = -12 /* fa_fwd_blocksparse: block_m not a positive multiple of 128,
-                              block_n not a positive multiple of 64, or n_mask not 1, H
-                              or B*H */
+    FA_ERR_BLOCKMASK = -12, /* fa_fwd_blocksparse: block_m not a positive multiple of 128,
+                               block_n not a positive multiple of 64, or n_mask not 1, H
+                               or B*H */
+    FA_ERR_PAGES = -13    /* fa_fwd_paged: page_size not a positive multiple of 64,
+                             num_pages < 1, table_stride < ceil(S / page_size), or a
+                             pool / table size outside the index ranges */
 } fa_status_t;
 
 /* The most K/V parts per Q tile fa_fwd_splitkv takes. */
@@ -274,6 +277,44 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* out, f
  */
 int fa_fwd_blocksparse_workspace_size(int64_t B, int64_t H, int64_t S, int64_t D, int dtype,
                                       int64_t n_mask, int64_t* bytes);
+
+/*
+ * fa_fwd_paged -- fa_fwd with keys and values kept in a paged cache: fixed-size
+ * pages in two pools, found through a block table, like the pages of an
+ * operating system's memory ([CG] section Paged KV Cache支持: non-contiguous
+ * blocks managed by a block table).  Key j of batch b is row j % page_size of
+ * page block_table[b * table_stride + j / page_size] of k_pages and v_pages.
+ * What is computed is fa_fwd's result on the gathered keys and values; pages
+ * may be shared between sequences and placed anywhere in the pools.
+ *
+ * q, out, lse  as fa_fwd.
+ * k_pages, v_pages  device pointers, contiguous [num_pages, page_size, H, D]
+ *             of `dtype`, 16-byte aligned; read only.  Rows of a page past S
+ *             are never read.
+ * block_table device pointer, int32 [B, table_stride], 4-byte aligned; read
+ *             only.  Entries 0 .. ceil(S / page_size) - 1 of each row are used;
+ *             each must lie in [0, num_pages) -- a page index outside the pool
+ *             is not an error the call can see (the table is device memory):
+ *             its keys and values read as zeros.
+ * num_pages   pages in each pool, >= 1.
+ * page_size   rows per page: a positive multiple of 64 (a K/V tile never
+ *             straddles pages).
+ * table_stride  int32 entries per table row, >= ceil(S / page_size).
+ * n_splits, workspace, workspace_bytes  as fa_fwd_splitkv (1 = one part; the
+ *             workspace is fa_fwd_splitkv_workspace_size bytes and may be
+ *             NULL when that is 0).  fp32 inputs run in one part.
+ * Other arguments as fa_fwd.  out and lse must not overlap q, the pools, the
+ * table or each other (FA_ERR_ALIAS); bad page geometry is FA_ERR_PAGES.
+ * Validation happens before any HIP call.  Enqueues one kernel on `stream`
+ * (two with a split) and returns without synchronising.  Returns FA_OK or a
+ * negative fa_status_t.
+ */
+int fa_fwd_paged(const void* q, const void* k_pages, const void* v_pages,
+                 const int32_t* block_table, void* out, float* lse, int64_t B, int64_t H,
+                 int64_t S, int64_t D, float scale, int causal, int64_t window_left,
+                 int64_t window_right, int dtype, int64_t num_pages, int64_t page_size,
+                 int64_t table_stride, int64_t n_splits, void* workspace,
+                 int64_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -74,6 +74,9 @@ FA_API const char* fa_status_string(int status) {
     case FA_ERR_SPLITS: return "n_splits must be in [1, FA_MAX_SPLITS]";
     case FA_ERR_BLOCKMASK:
         return "block_m must be a positive multiple of 128, block_n of 64, and n_mask 1, H or B*H";
+    case FA_ERR_PAGES:
+        return "page_size must be a positive multiple of 64, num_pages >= 1, the block table as "
+               "wide as ceil(S / page_size), and the pools must fit the index ranges";
     default: return "unknown status";
     }
 }
@@ -404,6 +407,66 @@ FA_API int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void*
     a.block_m = block_m;
     a.block_n = block_n;
     a.lut = (int*)workspace;
+    const hipError_t e = fa::launch_fwd(a);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+FA_API int fa_fwd_paged(const void* q, const void* k_pages, const void* v_pages,
+                        const int32_t* block_table, void* out, float* lse, int64_t B, int64_t H,
+                        int64_t S, int64_t D, float scale, int causal, int64_t window_left,
+                        int64_t window_right, int dtype, int64_t num_pages, int64_t page_size,
+                        int64_t table_stride, int64_t n_splits, void* workspace,
+                        int64_t workspace_bytes, void* stream) {
+    if (!q || !k_pages || !v_pages || !block_table || !out || !lse) return FA_ERR_NULL;
+    int64_t nbytes = 0, lbytes = 0;
+    int rc = check_problem(B, H, S, D, causal, window_left, window_right, dtype, &nbytes, &lbytes);
+    if (rc != FA_OK) return rc;
+    if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
+    // page geometry: a page holds whole 64-key tiles; the kernels index pages
+    // and rows with 32-bit values and pool rows with 64-bit offsets
+    if (page_size < 64 || page_size % 64 != 0 || page_size > INT32_MAX || num_pages < 1 ||
+        num_pages > INT32_MAX || table_stride < (S + page_size - 1) / page_size ||
+        table_stride > INT32_MAX)
+        return FA_ERR_PAGES;
+    int64_t t, pool_bytes, table_bytes;
+    if (!mul_ok(num_pages, page_size, &t) || !mul_ok(t, H * D * elem_size(dtype), &pool_bytes) ||
+        !mul_ok(B, table_stride, &t) || !mul_ok(t, 4, &table_bytes))
+        return FA_ERR_PAGES;
+    if (((uintptr_t)q | (uintptr_t)k_pages | (uintptr_t)v_pages | (uintptr_t)out) & 15u)
+        return FA_ERR_ALIGN;
+    if (((uintptr_t)lse | (uintptr_t)block_table) & 3u) return FA_ERR_ALIGN;
+    const void* ins[4] = {q, k_pages, v_pages, block_table};
+    const int64_t in_bytes[4] = {nbytes, pool_bytes, pool_bytes, table_bytes};
+    for (int i = 0; i < 4; ++i)
+        if (overlaps(out, nbytes, ins[i], in_bytes[i]) || overlaps(lse, lbytes, ins[i], in_bytes[i]))
+            return FA_ERR_ALIAS;
+    if (overlaps(out, nbytes, lse, lbytes)) return FA_ERR_ALIAS;
+    int64_t need = 0;
+    rc = fa_fwd_splitkv_workspace_size(B, H, S, D, dtype, n_splits, &need);
+    if (rc != FA_OK) return rc;
+    fa::LaunchArgs a = make_args(q, k_pages, v_pages, out, lse, B, H, S, D, scale, causal,
+                                 window_left, window_right, dtype, stream);
+    a.pg_table = block_table;
+    a.pg_stride = table_stride;
+    a.pg_rows = page_size;
+    a.pg_count = num_pages;
+    if (need > 0) {
+        const int64_t bm = fa::q_tile_rows(dtype, D, S, a.wl, a.wr);
+        int64_t n_wg;
+        if (!mul_ok(B * H, (S + bm - 1) / bm, &n_wg) || !mul_ok(n_wg, n_splits, &n_wg) ||
+            n_wg > (int64_t)(UINT32_MAX / 256))
+            return FA_ERR_SHAPE;
+        if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15u))
+            return FA_ERR_WORKSPACE;
+        for (int i = 0; i < 4; ++i)
+            if (overlaps(workspace, need, ins[i], in_bytes[i])) return FA_ERR_WORKSPACE;
+        if (overlaps(workspace, need, out, nbytes) || overlaps(workspace, need, lse, lbytes))
+            return FA_ERR_WORKSPACE;
+        const int64_t rows = B * H * S;
+        a.n_splits = (int)n_splits;
+        a.part_o = (float*)workspace;
+        a.part_lse = (float*)workspace + n_splits * rows * D;
+    }
     const hipError_t e = fa::launch_fwd(a);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

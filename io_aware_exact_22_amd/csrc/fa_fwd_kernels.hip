@@ -199,13 +199,15 @@ __device__ inline void dma_matrix(__amdgpu_buffer_rsrc_t r, unsigned char* wave_
 // part, in fp32, to part_o [n_splits, B, H, S, D] and part_lse
 // [n_splits, B, H, S], for the merge kernel below (the log-domain merge of the
 // online softmax, applied once across parts).
-template <typename T, int D, int NW, int BN_, bool SPLIT, bool SPARSE>
+template <typename T, int D, int NW, int BN_, bool SPLIT, bool SPARSE, bool PAGED>
 __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ out,
     float* __restrict__ lse, int B, int H, int S, float c, int causal, int wl, int wr, int n_qt,
     int n_splits, float* __restrict__ part_o, float* __restrict__ part_lse,
-    const int* __restrict__ sp_lut, int sp_heads, int sp_stride) {
+    const int* __restrict__ sp_lut, int sp_heads, int sp_stride, const int* __restrict__ pg_table,
+    int pg_stride, int pg_rows, int pg_count) {
     static_assert(!(SPLIT && SPARSE), "a block-sparse launch runs in one part");
+    static_assert(!(SPARSE && PAGED), "block-sparse and paged K/V do not combine");
     typedef Tile<D, NW, BN_> L;
     constexpr int BN = L::BN;
     constexpr int BM = L::BM;
@@ -349,9 +351,27 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
     // the host), so kt * tile_bytes is one 32 x 32 -> 64-bit product.
     const uint32_t tile_bytes = (uint32_t)(BN * row_stride * (int64_t)sizeof(T));
     const uint64_t head_bytes = (uint64_t)(((int64_t)S - 1) * row_stride + D) * sizeof(T);
-    const unsigned char* const k_head = (const unsigned char*)(k + head_base);
-    const unsigned char* const v_head = (const unsigned char*)(v + head_base);
-    auto tile_rsrc = [&](const unsigned char* head, int kt) __attribute__((always_inline)) {
+    // PAGED: k and v are pools [pg_count, pg_rows, H, D]; key j of batch bb is
+    // row j % pg_rows of page pg_table[bb * pg_stride + j / pg_rows].  pg_rows is
+    // a multiple of BN, so a tile lies in one page.
+    const int64_t kv_base = PAGED ? (int64_t)h * D : head_base;
+    const unsigned char* const k_head = (const unsigned char*)(k + kv_base);
+    const unsigned char* const v_head = (const unsigned char*)(v + kv_base);
+    auto tile_rsrc = [&](const unsigned char* head, int kt, int page) __attribute__((always_inline)) {
+        if (PAGED) {
+            // records stop at row S, and a page index outside the pool reads
+            // as zeros instead of reaching past it
+            const int k0 = kt * BN;
+            const int rows = S - k0 < BN ? S - k0 : BN;
+            const bool ok = (unsigned)page < (unsigned)pg_count && rows > 0;
+            const uint64_t off = ((uint64_t)(uint32_t)page * (uint32_t)pg_rows +
+                                  (uint32_t)(k0 % pg_rows)) *
+                                 (uint64_t)row_stride * sizeof(T);
+            const uint32_t nrec =
+                ok ? (uint32_t)(((int64_t)(rows - 1) * row_stride + D) * (int64_t)sizeof(T)) : 0u;
+            return __builtin_amdgcn_make_buffer_rsrc((void*)(head + (ok ? off : 0)), (short)0,
+                                                     (int)nrec, kBufferFlags);
+        }
         const uint64_t off = (uint64_t)(uint32_t)kt * tile_bytes;
         // records run to the end of the head's last row; a tile that starts at
         // or past S gets none, so the hardware range check turns every read of
@@ -361,21 +381,27 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
         return __builtin_amdgcn_make_buffer_rsrc((void*)(head + off), (short)0, (int)nrec,
                                                  kBufferFlags);
     };
-    auto load_k = [&](int kt, unsigned char* buf) __attribute__((always_inline)) {
-        dma_matrix<L::DMA_PER_WAVE>(tile_rsrc(k_head, kt), buf + wave * L::DMA_PER_WAVE * 1024,
-                                    dma_voff);
+    auto load_k = [&](int kt, int page, unsigned char* buf) __attribute__((always_inline)) {
+        dma_matrix<L::DMA_PER_WAVE>(tile_rsrc(k_head, kt, page),
+                                    buf + wave * L::DMA_PER_WAVE * 1024, dma_voff);
     };
-    auto load_v = [&](int kt, unsigned char* buf) __attribute__((always_inline)) {
-        dma_matrix<L::DMA_PER_WAVE>(tile_rsrc(v_head, kt), buf + wave * L::DMA_PER_WAVE * 1024,
-                                    dma_voff);
+    auto load_v = [&](int kt, int page, unsigned char* buf) __attribute__((always_inline)) {
+        dma_matrix<L::DMA_PER_WAVE>(tile_rsrc(v_head, kt, page),
+                                    buf + wave * L::DMA_PER_WAVE * 1024, dma_voff);
     };
-    // SPARSE: list entry p, read by a vector load (it lands with the step's
-    // K/V loads and is waited for with them; a scalar load would make every
-    // LDS wait of the step wait for it too).  Entries past the count read 0.
-    const __amdgpu_buffer_rsrc_t sp_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(SPARSE ? sp_row + 4 : sp_lut), (short)0, SPARSE ? kt1 * 4 : 0, kBufferFlags);
-    auto sp_entry = [&](int p) __attribute__((always_inline)) {
-        return (int)__builtin_amdgcn_raw_buffer_load_b32(sp_rsrc, 4 * p, 0, 0);
+    // Look-ahead table (SPARSE: the kept-tile list, entry p = the tile at
+    // position p; PAGED: the batch's block table, entry p = the page of tile
+    // p).  Entries are read by a vector load one step ahead: it lands with the
+    // step's K/V loads and is waited for with them (a scalar load would make
+    // every LDS wait of the step wait for it too).  Entries past the table
+    // read 0.
+    const int* const la_base = SPARSE ? sp_row + 4 : PAGED ? pg_table + (int64_t)bb * pg_stride : sp_lut;
+    const int la_count = SPARSE ? kt1 : PAGED ? (S + pg_rows - 1) / pg_rows : 0;
+    const __amdgpu_buffer_rsrc_t la_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)la_base, (short)0, la_count * 4, kBufferFlags);
+    auto la_entry = [&](int p) __attribute__((always_inline)) {
+        const int idx = PAGED ? p * BN / pg_rows : p;
+        return (int)__builtin_amdgcn_raw_buffer_load_b32(la_rsrc, 4 * idx, 0, 0);
     };
 
     // ---- per-lane LDS operand addresses (bytes within a tile)
@@ -512,18 +538,23 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
     // ---- prologue: K of the first two tiles, V of the first, scores of the first
     f32x16 sc[KB];  // scores of the current tile (masked)
     int tile_a = kt0, tile_b = kt0 + 1;  // tiles of positions kt0, kt0 + 1
-    int sp_t1 = 0;                       // SPARSE: tile of position j + 1 at step j
-    int sp_nx = 0;                       // SPARSE: entry j + 2, in flight from step j - 1
+    int page_a = 0, page_b = 0;          // PAGED: their pages
+    int la_t1 = 0;                       // look-ahead entry of position j + 1 at step j
+    int la_nx = 0;                       // entry j + 2, in flight from step j - 1
     if (SPARSE) {
         tile_a = __builtin_amdgcn_readfirstlane(sp_row[4]);
         tile_b = kt1 > 1 ? __builtin_amdgcn_readfirstlane(sp_row[5]) : 0;
     }
-    load_k(tile_a, lds_k0);
-    if (kt0 + 1 < kt1) load_k(tile_b, lds_k1);
-    load_v(tile_a, lds_v0);
-    if (SPARSE) {
-        sp_t1 = tile_b;
-        sp_nx = sp_entry(2);
+    if (PAGED) {
+        page_a = __builtin_amdgcn_readfirstlane(la_base[tile_a * BN / pg_rows]);
+        page_b = kt0 + 1 < kt1 ? __builtin_amdgcn_readfirstlane(la_base[tile_b * BN / pg_rows]) : 0;
+    }
+    load_k(tile_a, page_a, lds_k0);
+    if (kt0 + 1 < kt1) load_k(tile_b, page_b, lds_k1);
+    load_v(tile_a, page_a, lds_v0);
+    if (SPARSE || PAGED) {
+        la_t1 = SPARSE ? tile_b : page_b;
+        la_nx = la_entry(kt0 + 2);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -548,6 +579,26 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
     }
     kw0 = __builtin_amdgcn_readfirstlane(kw0);
     kw1 = __builtin_amdgcn_readfirstlane(kw1);
+    // tiles (and pages) of positions j + 1 and j + 2 at the step of position
+    // j; advances the look-ahead by one position (every wave runs it once per
+    // position, in its compute steps and its idle steps alike)
+    auto look_ahead = [&](int j, int& tn1, int& tn2, int& pn1, int& pn2) __attribute__((always_inline)) {
+        tn1 = j + 1;
+        tn2 = j + 2;
+        pn1 = pn2 = 0;
+        if (SPARSE || PAGED) {
+            const int e1 = la_t1, e2 = __builtin_amdgcn_readfirstlane(la_nx);
+            la_t1 = e2;
+            la_nx = la_entry(j + 3);
+            if (SPARSE) {
+                tn1 = e1;
+                tn2 = e2;
+            } else {
+                pn1 = e1;
+                pn2 = e2;
+            }
+        }
+    };
     // scores of the tile at position pos (tile number `tile`)
     auto first_scores = [&](int pos, int tile, unsigned char* kst) __attribute__((always_inline)) {
         qk(sc, kst);
@@ -572,19 +623,14 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
         unsigned char* const v_next = ST ? lds_v0 : lds_v1;  // V_{j+1}
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K_{j+1}, V_j have landed
         __syncthreads();  // ... for every wave; every wave is done with tile j-1
-        int tn1 = j + 1, tn2 = j + 2;  // tiles of positions j + 1 and j + 2
-        if (SPARSE) {
-            tn1 = sp_t1;
-            tn2 = __builtin_amdgcn_readfirstlane(sp_nx);
-            sp_t1 = tn2;
-            sp_nx = sp_entry(j + 3);
-        }
+        int tn1, tn2, pn1, pn2;  // tiles of positions j + 1 and j + 2, and their pages
+        look_ahead(j, tn1, tn2, pn1, pn2);
         if (!LAST) {
-            if (j + 2 < kt1) load_k(tn2, k_this);
-            load_v(tn1, v_next);
+            if (j + 2 < kt1) load_k(tn2, pn2, k_this);
+            load_v(tn1, pn1, v_next);
         } else {  // this wave's last tile; the workgroup may go on
-            if (j + 2 < kt1) load_k(tn2, k_this);
-            if (j + 1 < kt1) load_v(tn1, v_next);
+            if (j + 2 < kt1) load_k(tn2, pn2, k_this);
+            if (j + 1 < kt1) load_v(tn1, pn1, v_next);
         }
         rescale_if_moved();
         u32x4 p[NCH];
@@ -646,8 +692,10 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
         const bool st = ((j - kt0) & 1) != 0;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (j + 2 < kt1) load_k(j + 2, st ? lds_k1 : lds_k0);
-        if (j + 1 < kt1) load_v(j + 1, st ? lds_v0 : lds_v1);
+        int tn1, tn2, pn1, pn2;
+        look_ahead(j, tn1, tn2, pn1, pn2);
+        if (j + 2 < kt1) load_k(tn2, pn2, st ? lds_k1 : lds_k0);
+        if (j + 1 < kt1) load_v(tn1, pn1, st ? lds_v0 : lds_v1);
     };
     if (!SPARSE) {
         for (int j = kt0; j + 1 < kw0; ++j) idle_step(j);
@@ -1325,12 +1373,16 @@ template <int D> struct Lds32 {
 
 // SPARSE: K/V tiles whose mask byte is 0 are skipped (bmask [sp_heads, n_qb,
 // n_kb]; block_m a multiple of the Q tile, block_n of the K/V tile).
-template <int D, bool SPARSE>
+// PAGED: k and v are pools [pg_count, pg_rows, H, D] read through the block
+// table (pg_rows a multiple of the K/V tile; a page index outside the pool
+// reads as zeros).
+template <int D, bool SPARSE, bool PAGED>
 __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ out, float* __restrict__ lse, int B, int H, int S, float c, int causal,
     int wl, int wr, int n_qt, const uint8_t* __restrict__ bmask, int sp_heads, int n_qb, int n_kb,
-    int block_m, int block_n) {
+    int block_m, int block_n, const int* __restrict__ pg_table, int pg_stride, int pg_rows,
+    int pg_count) {
     typedef Lds32<D> L;
     constexpr int BN = L::BN;
     constexpr int DB = D / 32;
@@ -1372,12 +1424,20 @@ __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
     for (int64_t kt = kt0; kt < kt1; ++kt) {
         const int64_t k0 = kt * BN;
         if (SPARSE && mrow[k0 / block_n] == 0) continue;  // the same for the whole workgroup
+        int64_t tile_row0 = 0;  // PAGED: pool row of the tile's first key (-1: outside the pool)
+        if (PAGED) {
+            const int page = pg_table[(int64_t)bb * pg_stride + k0 / pg_rows];
+            tile_row0 = (unsigned)page < (unsigned)pg_count
+                            ? (int64_t)page * pg_rows + k0 % pg_rows
+                            : -1;
+        }
         __syncthreads();
         for (int id = tid; id < BN * (D / 4); id += kThreads32) {
             const int r = id / (D / 4), cc = id % (D / 4);
             const int64_t key = k0 + r;
-            const bool ok = key < S;
-            const int64_t off = head_base + (ok ? key : 0) * row_stride + cc * 4;
+            const bool ok = key < S && tile_row0 >= 0;
+            const int64_t off = PAGED ? ((ok ? tile_row0 + r : 0) * H + h) * D + cc * 4
+                                      : head_base + (ok ? key : 0) * row_stride + cc * 4;
             f32x4 xk = *reinterpret_cast<const f32x4*>(k + off);
             f32x4 xv = *reinterpret_cast<const f32x4*>(v + off);
 #pragma unroll
@@ -1472,25 +1532,44 @@ static hipError_t launch_mfma_cfg(const LaunchArgs& a) {
                            (int)a.block_n, stride, a.lut);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, true>), dim3((unsigned)n_wg),
-                           dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
-                           (T*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl,
-                           (int)a.wr, n_qt, 1, nullptr, nullptr, (const int*)a.lut, (int)a.n_mask,
-                           stride);
+        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, true, false>),
+                           dim3((unsigned)n_wg), dim3(NW * 64), 0, a.stream, (const T*)a.q,
+                           (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
+                           (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr, nullptr,
+                           (const int*)a.lut, (int)a.n_mask, stride, nullptr, 0, 1, 0);
         return hipGetLastError();
     }
+    const bool paged = a.pg_table != nullptr;
+    const int pg_stride = (int)a.pg_stride, pg_rows = paged ? (int)a.pg_rows : 1,
+              pg_count = (int)a.pg_count;
     if (a.n_splits <= 1) {
-        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, false>), dim3((unsigned)n_wg),
-                           dim3(NW * 64), 0, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
-                           (T*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl,
-                           (int)a.wr, n_qt, 1, nullptr, nullptr, nullptr, 0, 0);
+        if (paged)
+            hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, false, true>),
+                               dim3((unsigned)n_wg), dim3(NW * 64), 0, a.stream, (const T*)a.q,
+                               (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
+                               (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr,
+                               nullptr, nullptr, 0, 0, a.pg_table, pg_stride, pg_rows, pg_count);
+        else
+            hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, false, false>),
+                               dim3((unsigned)n_wg), dim3(NW * 64), 0, a.stream, (const T*)a.q,
+                               (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
+                               (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr,
+                               nullptr, nullptr, 0, 0, nullptr, 0, 1, 0);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, true, false>),
-                       dim3((unsigned)(n_wg * a.n_splits)), dim3(NW * 64), 0, a.stream,
-                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B,
-                       (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, a.n_splits,
-                       a.part_o, a.part_lse, nullptr, 0, 0);
+    if (paged)
+        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, true, false, true>),
+                           dim3((unsigned)(n_wg * a.n_splits)), dim3(NW * 64), 0, a.stream,
+                           (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B,
+                           (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt,
+                           a.n_splits, a.part_o, a.part_lse, nullptr, 0, 0, a.pg_table, pg_stride,
+                           pg_rows, pg_count);
+    else
+        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, true, false, false>),
+                           dim3((unsigned)(n_wg * a.n_splits)), dim3(NW * 64), 0, a.stream,
+                           (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B,
+                           (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt,
+                           a.n_splits, a.part_o, a.part_lse, nullptr, 0, 0, nullptr, 0, 1, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     constexpr int RPB = kMergeThreads / (D / 4);
@@ -1547,18 +1626,28 @@ static hipError_t launch_fp32(const LaunchArgs& a) {
     const int n_qt = (int)((a.S + kBM32 - 1) / kBM32);
     const int64_t n_wg = a.B * a.H * n_qt;
     if (a.bmask) {
-        hipLaunchKernelGGL((fa_fwd_fp32_kernel<D, true>), dim3((unsigned)n_wg), dim3(kThreads32), 0,
-                           a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
-                           (float*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S, a.c, a.causal,
-                           (int)a.wl, (int)a.wr, n_qt, a.bmask, (int)a.n_mask,
+        hipLaunchKernelGGL((fa_fwd_fp32_kernel<D, true, false>), dim3((unsigned)n_wg),
+                           dim3(kThreads32), 0, a.stream, (const float*)a.q, (const float*)a.k,
+                           (const float*)a.v, (float*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S,
+                           a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, a.bmask, (int)a.n_mask,
                            (int)((a.S + a.block_m - 1) / a.block_m),
-                           (int)((a.S + a.block_n - 1) / a.block_n), (int)a.block_m, (int)a.block_n);
+                           (int)((a.S + a.block_n - 1) / a.block_n), (int)a.block_m, (int)a.block_n,
+                           nullptr, 0, 1, 0);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((fa_fwd_fp32_kernel<D, false>), dim3((unsigned)n_wg), dim3(kThreads32), 0,
-                       a.stream, (const float*)a.q, (const float*)a.k, (const float*)a.v,
-                       (float*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl,
-                       (int)a.wr, n_qt, nullptr, 0, 0, 0, 1, 1);
+    if (a.pg_table) {
+        hipLaunchKernelGGL((fa_fwd_fp32_kernel<D, false, true>), dim3((unsigned)n_wg),
+                           dim3(kThreads32), 0, a.stream, (const float*)a.q, (const float*)a.k,
+                           (const float*)a.v, (float*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S,
+                           a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, nullptr, 0, 0, 0, 1, 1,
+                           a.pg_table, (int)a.pg_stride, (int)a.pg_rows, (int)a.pg_count);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((fa_fwd_fp32_kernel<D, false, false>), dim3((unsigned)n_wg),
+                       dim3(kThreads32), 0, a.stream, (const float*)a.q, (const float*)a.k,
+                       (const float*)a.v, (float*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S, a.c,
+                       a.causal, (int)a.wl, (int)a.wr, n_qt, nullptr, 0, 0, 0, 1, 1, nullptr, 0, 1,
+                       0);
     return hipGetLastError();
 }
 

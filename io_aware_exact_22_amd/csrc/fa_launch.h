@@ -36,6 +36,10 @@ struct LaunchArgs {
     const uint8_t* bmask = nullptr;
     int64_t n_mask = 0, block_m = 0, block_n = 0;
     int* lut = nullptr;
+    // paged K/V: k and v are pools [pg_count, pg_rows, H, D]; key j of batch b
+    // is row j % pg_rows of page pg_table[b * pg_stride + j / pg_rows]
+    const int* pg_table = nullptr;
+    int64_t pg_stride = 0, pg_rows = 0, pg_count = 0;
 };
 
 // The backward pass: gradients for an output gradient dout (bf16 / fp16).

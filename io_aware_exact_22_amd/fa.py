@@ -3,9 +3,9 @@
 Same names as the C ABI: ``fa_fwd``, ``fa_fwd_check_args``,
 ``fa_status_string``, ``fa_fwd_tile_schedule``, ``fa_fwd_workgroup_tile``, ``fa_fwd_splitkv``,
 ``fa_fwd_splitkv_workspace_size``, ``fa_fwd_splitkv_auto_splits``, ``fa_bwd``,
-``fa_bwd_workspace_size``, ``fa_fwd_blocksparse``, ``fa_fwd_blocksparse_workspace_size``;
-plus ``flash_attn_fwd`` (and ``flash_attn_fwd_splitkv``, ``flash_attn_bwd``,
-``flash_attn_fwd_blocksparse``), the
+``fa_bwd_workspace_size``, ``fa_fwd_blocksparse``, ``fa_fwd_blocksparse_workspace_size``,
+``fa_fwd_paged``; plus ``flash_attn_fwd`` (and ``flash_attn_fwd_splitkv``, ``flash_attn_bwd``,
+``flash_attn_fwd_blocksparse``, ``flash_attn_fwd_paged``), the
 tensor-level call that mirrors the pages' ``flash_attention(q, k, v,
 softmax_scale=None, causal=..., window_size=(-1, -1))`` argument list
 ("FlashAttention技术解析：加速GPT训练的核心优化", section 2.2).  This module only
@@ -86,6 +86,9 @@ def _load():
         lib.fa_fwd_blocksparse.restype = cint
         lib.fa_fwd_blocksparse_workspace_size.argtypes = [i64, i64, i64, i64, cint, i64, p64]
         lib.fa_fwd_blocksparse_workspace_size.restype = cint
+        lib.fa_fwd_paged.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float,
+                                     cint, i64, i64, cint, i64, i64, i64, i64, vp, i64, vp]
+        lib.fa_fwd_paged.restype = cint
         lib.fa_bwd_workspace_size.argtypes = [i64, i64, i64, i64, cint, p64]
         lib.fa_bwd_workspace_size.restype = cint
         _lib = lib
@@ -204,6 +207,17 @@ def fa_fwd_blocksparse_workspace_size(B: int, H: int, S: int, D: int, dtype: int
     if rc != 0:
         raise FaError(rc, "fa_fwd_blocksparse_workspace_size")
     return n.value
+
+
+def fa_fwd_paged(q: int, k_pages: int, v_pages: int, block_table: int, out: int, lse: int, B: int,
+                 H: int, S: int, D: int, scale: float, causal: int, window_left: int,
+                 window_right: int, dtype: int, num_pages: int, page_size: int,
+                 table_stride: int, n_splits: int, workspace: int, workspace_bytes: int,
+                 stream: int | None) -> int:
+    """The paged-K/V C entry point with raw device pointers (ints); returns the status."""
+    return _load().fa_fwd_paged(q, k_pages, v_pages, block_table, out, lse, B, H, S, D, scale,
+                                causal, window_left, window_right, dtype, num_pages, page_size,
+                                table_stride, n_splits, workspace, workspace_bytes, stream)
 
 
 # ------------------------------------------------------------------ tensor call
@@ -367,6 +381,66 @@ def flash_attn_fwd_blocksparse(q, k, v, block_mask, block_m: int, block_n: int,
                                 ws_ptr or None, ws_bytes, st.cuda_stream)
     if rc != 0:
         raise FaError(rc, "fa_fwd_blocksparse")
+    return out, lse
+
+
+def flash_attn_fwd_paged(q, k_pages, v_pages, block_table, softmax_scale: float | None = None,
+                         causal: bool = False, window_size=(-1, -1), n_splits: int = 1, out=None,
+                         lse=None, workspace=None, stream=None):
+    """flash_attn_fwd with keys and values in a paged cache: k_pages and
+    v_pages are contiguous GPU tensors [num_pages, page_size, H, D] (page_size
+    a multiple of 64) and block_table an int32 GPU tensor [B, n] with
+    n >= ceil(S / page_size): key j of batch b is row j % page_size of page
+    block_table[b, j // page_size].  ``n_splits`` > 1 runs the split-KV path
+    (0 = the library's choice); its fp32 workspace is allocated here when
+    None.  Returns (out, lse) like flash_attn_fwd."""
+    import torch
+
+    if not isinstance(q, torch.Tensor) or q.device.type != "cuda" or q.dim() != 4:
+        raise TypeError("q must be a GPU tensor [B, S, H, D]")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, S, H, D]")
+    B, S, H, D = q.shape
+    for name, t in (("k_pages", k_pages), ("v_pages", v_pages)):
+        if not isinstance(t, torch.Tensor) or t.device != q.device or t.dtype != q.dtype:
+            raise TypeError(f"{name} must be a tensor of q's dtype on q's device")
+        if t.dim() != 4 or t.shape != k_pages.shape or tuple(t.shape[2:]) != (H, D):
+            raise ValueError(f"{name} must be [num_pages, page_size, H, D] like the other pool")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if (not isinstance(block_table, torch.Tensor) or block_table.device != q.device or
+            block_table.dtype != torch.int32 or block_table.dim() != 2 or
+            block_table.shape[0] != B or not block_table.is_contiguous()):
+        raise ValueError("block_table must be a contiguous int32 tensor [B, n] on q's device")
+    num_pages, page_size = k_pages.shape[0], k_pages.shape[1]
+    dtype = _dtype_code(q)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    wl, wr = (int(x) for x in window_size)
+    with torch.cuda.device(q.device):
+        if n_splits == 0:
+            n_splits = fa_fwd_splitkv_auto_splits(B, H, S, D, int(bool(causal)), wl, wr, dtype)
+        need = fa_fwd_splitkv_workspace_size(B, H, S, D, dtype, n_splits)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped and typed like q")
+    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous fp32 tensor [B, H, S]")
+    if workspace is None and need > 0:
+        workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        rc = fa_fwd_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                          block_table.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, S, D,
+                          scale, int(bool(causal)), wl, wr, dtype, num_pages, page_size,
+                          block_table.shape[1], n_splits, ws_ptr or None, ws_bytes,
+                          st.cuda_stream)
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_paged")
     return out, lse
 
 

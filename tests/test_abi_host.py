@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
                           "fa_fwd_workgroup_tile", "fa_fwd_splitkv",
                           "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv_auto_splits",
                           "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_blocksparse",
-                          "fa_fwd_blocksparse_workspace_size"}
+                          "fa_fwd_blocksparse_workspace_size", "fa_fwd_paged"}
     lib = ctypes.CDLL(fa.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in range(0, -13, -1):
+    for st in range(0, -14, -1):
         s = fa.fa_status_string(st)
         assert s and s != "unknown status"
     assert fa.fa_status_string(-99) == "unknown status"
@@ -187,6 +187,28 @@ def test_blocksparse_rejects_before_any_hip_call(kw, status):
                                a["D"], a["scale"], a["causal"], a["window_left"],
                                a["window_right"], a["dtype"], a["mask"] or None, a["nm"], a["bm"],
                                a["bn"], a["ws"] or None, a["wsb"], None)
+    assert rc == status
+
+
+KP, VP, BT = 12 << 32, 13 << 32, 14 << 32  # fake page pools and block table
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({"kp": 0}, -1), ({"bt": 0}, -1), ({"ps": 32}, -13), ({"ps": 100}, -13), ({"ps": 0}, -13),
+    ({"np": 0}, -13), ({"ts": 2}, -13), ({"kp": KP + 8}, -7), ({"bt": BT + 2}, -7),
+    ({"out": KP}, -8), ({"lse": BT}, -8), ({"out": VP + 64}, -8), ({"ns": 17}, -11),
+    ({"ns": 2, "ws": 0}, -10), ({"ns": 2, "ws": KP}, -10), ({"ns": 2, "ws": WS + 4}, -10),
+    ({"D": 96}, -3), ({"scale": -2.0}, -6), ({"window_right": -5}, -4),
+])
+def test_paged_rejects_before_any_hip_call(kw, status):
+    """Invalid arguments return their status without touching the GPU (S = 300
+    needs 3 table entries at page_size 128)."""
+    a = dict(GOOD, kp=KP, vp=VP, bt=BT, np=40, ps=128, ts=3, ns=1, ws=WS, wsb=1 << 40)
+    a.update(kw)
+    rc = fa.fa_fwd_paged(a["q"], a["kp"] or None, a["vp"], a["bt"] or None, a["out"], a["lse"],
+                         a["B"], a["H"], a["S"], a["D"], a["scale"], a["causal"],
+                         a["window_left"], a["window_right"], a["dtype"], a["np"], a["ps"],
+                         a["ts"], a["ns"], a["ws"] or None, a["wsb"], None)
     assert rc == status
 
 
