@@ -182,6 +182,10 @@ def main() -> int:
                          "blocks: 'local:KEYS[:GLOBAL]' keeps, for each 128-row block, the KEYS "
                          "keys ending at its last row and the first GLOBAL 64-key blocks "
                          "(default 1)")
+    ap.add_argument("--paged", type=int, default=0,
+                    help="time fa_fwd_paged with K/V cut into pages of this many rows (a multiple "
+                         "of 64), placed at a seeded random permutation of a pool with spare "
+                         "pages; combines with --splitkv")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the benchmark, run --steps plain device copies of this many "
                          "MiB (the reference kernel for scaling HBM byte counters)")
@@ -221,6 +225,7 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
 
     n_splits = None
+    paged = None  # paged K/V: description of the pools
     bs = None  # block-sparse: (mask [1, n_qb, n_kb] on the CPU, description)
     if args.blocksparse:
         from fa_inputs import local_global_block_mask
@@ -259,6 +264,39 @@ def main() -> int:
             fa.flash_attn_bwd(dod, qd, kd, vd, out, lse, softmax_scale=w.scale, causal=w.causal,
                               window_size=w.window, workspace=ws_b, dq=dq, dk=dk, dv=dv,
                               stream=stream)
+    elif args.paged:
+        ps = args.paged
+        n_pg = -(-w.S // ps)
+        num_pages = w.B * n_pg + max(1, w.B * n_pg // 8)
+        g = torch.Generator(device="cpu")
+        g.manual_seed(w.seed + 2000)
+        slots = torch.randperm(num_pages, generator=g)[: w.B * n_pg]
+        pools = []
+        for t in (kd, vd):
+            pad = torch.zeros((w.B, n_pg * ps, w.H, w.D), dtype=w.dtype, device=dev)
+            pad[:, : w.S] = t
+            pool = torch.zeros((num_pages, ps, w.H, w.D), dtype=w.dtype, device=dev)
+            pool[slots.to(dev)] = pad.view(w.B * n_pg, ps, w.H, w.D)
+            pools.append(pool)
+            del pad
+        kp, vp = pools
+        table = slots.view(w.B, n_pg).to(torch.int32).to(dev).contiguous()
+        dcode = {torch.float32: fa.FA_DTYPE_FP32, torch.float16: fa.FA_DTYPE_FP16,
+                 torch.bfloat16: fa.FA_DTYPE_BF16}[w.dtype]
+        ns = max(1, args.splitkv) if args.splitkv >= 0 else 1
+        if args.splitkv == 0:
+            ns = fa.fa_fwd_splitkv_auto_splits(w.B, w.H, w.S, w.D, int(w.causal), w.window[0],
+                                               w.window[1], dcode)
+        need = fa.fa_fwd_splitkv_workspace_size(w.B, w.H, w.S, w.D, dcode, ns)
+        ws = torch.empty(max(1, (need + 3) // 4), dtype=torch.float32, device=dev)
+        n_splits = ns if ns > 1 else None
+        paged = {"page_size": ps, "num_pages": num_pages, "pages_used": w.B * n_pg,
+                 "placement": "seeded random permutation"}
+
+        def step():
+            fa.flash_attn_fwd_paged(qd, kp, vp, table, softmax_scale=w.scale, causal=w.causal,
+                                    window_size=w.window, n_splits=ns, out=out, lse=lse,
+                                    workspace=ws, stream=stream)
     elif args.splitkv >= 0:
         dcode = {torch.float32: fa.FA_DTYPE_FP32, torch.float16: fa.FA_DTYPE_FP16,
                  torch.bfloat16: fa.FA_DTYPE_BF16}[w.dtype]
@@ -318,7 +356,7 @@ def main() -> int:
         roof = {"bound": "mfma", "achieved": kern_tflops, "peak": peak, "unit": "TFLOP/s",
                 "frac": kern_tflops / peak}
     # the recorded counters are those of fa_fwd on its default workload
-    roof["traffic"] = (None if (args.backward or n_splits is not None or bs is not None)
+    roof["traffic"] = (None if (args.backward or n_splits is not None or bs is not None or paged)
                        else measured_traffic(w.name))
     roof["kernel_ms"] = avg_launch_ms
     roof["algorithmic_flops_per_launch"] = flops
@@ -349,14 +387,16 @@ def main() -> int:
                    "causal": w.causal, "window": list(w.window), "S_eff": s_eff,
                    "flops_per_step": flops, "parallelism": "single GPU",
                    "entry": ("fa_bwd" if args.backward else "fa_fwd_blocksparse" if bs else
+                             "fa_fwd_paged" if paged else
                              "fa_fwd" if n_splits is None else "fa_fwd_splitkv"),
                    **({} if n_splits is None else {"n_splits": n_splits}),
+                   **({} if paged is None else {"paged_kv": paged}),
                    **({} if bs is None else {"block_mask": bs[1]})},
         "roofline": roof,
     }
     if not args.no_cpu_baseline and bs is not None:
         rec["cpu_baseline"] = cpu_baseline_blocksparse(w, q, k, v, bs[0].numpy(), 128, 64)
-    elif not args.no_cpu_baseline and not args.backward and n_splits is None:
+    elif not args.no_cpu_baseline and not args.backward and n_splits is None and not paged:
         rec["cpu_baseline"] = cpu_baseline(w, q, k, v)
     else:
         rec["cpu_baseline"] = None

@@ -199,8 +199,13 @@ __device__ inline void dma_matrix(__amdgpu_buffer_rsrc_t r, unsigned char* wave_
 // part, in fp32, to part_o [n_splits, B, H, S, D] and part_lse
 // [n_splits, B, H, S], for the merge kernel below (the log-domain merge of the
 // online softmax, applied once across parts).
+// SPARSE and PAGED: see the look-ahead table below.
+// Occupancy: D = 64 fits three workgroups per CU in 168 VGPRs; the paged
+// variant's page look-ahead needs a few more, and at that cap it spills (bf16:
+// 10 dwords a lane), which cost more than the third workgroup gains, so it
+// takes two.
 template <typename T, int D, int NW, int BN_, bool SPLIT, bool SPARSE, bool PAGED>
-__global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
+__global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd_mfma_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ out,
     float* __restrict__ lse, int B, int H, int S, float c, int causal, int wl, int wr, int n_qt,
     int n_splits, float* __restrict__ part_o, float* __restrict__ part_lse,
@@ -357,16 +362,19 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
     const int64_t kv_base = PAGED ? (int64_t)h * D : head_base;
     const unsigned char* const k_head = (const unsigned char*)(k + kv_base);
     const unsigned char* const v_head = (const unsigned char*)(v + kv_base);
-    auto tile_rsrc = [&](const unsigned char* head, int kt, int page) __attribute__((always_inline)) {
+    // PAGED: tiles per page, and the bytes of one page of one pool
+    const int pg_tiles = PAGED ? pg_rows / BN : 1;
+    const uint64_t page_bytes = PAGED ? (uint64_t)pg_rows * (uint64_t)row_stride * sizeof(T) : 0;
+    // K/V tile kt; PAGED: it is tile `in_page` of page `page`
+    auto tile_rsrc = [&](const unsigned char* head, int kt, int page, int in_page) __attribute__((always_inline)) {
         if (PAGED) {
             // records stop at row S, and a page index outside the pool reads
             // as zeros instead of reaching past it
             const int k0 = kt * BN;
             const int rows = S - k0 < BN ? S - k0 : BN;
             const bool ok = (unsigned)page < (unsigned)pg_count && rows > 0;
-            const uint64_t off = ((uint64_t)(uint32_t)page * (uint32_t)pg_rows +
-                                  (uint32_t)(k0 % pg_rows)) *
-                                 (uint64_t)row_stride * sizeof(T);
+            const uint64_t off = (uint64_t)(uint32_t)page * page_bytes +
+                                 (uint64_t)(uint32_t)in_page * tile_bytes;
             const uint32_t nrec =
                 ok ? (uint32_t)(((int64_t)(rows - 1) * row_stride + D) * (int64_t)sizeof(T)) : 0u;
             return __builtin_amdgcn_make_buffer_rsrc((void*)(head + (ok ? off : 0)), (short)0,
@@ -381,26 +389,24 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
         return __builtin_amdgcn_make_buffer_rsrc((void*)(head + off), (short)0, (int)nrec,
                                                  kBufferFlags);
     };
-    auto load_k = [&](int kt, int page, unsigned char* buf) __attribute__((always_inline)) {
-        dma_matrix<L::DMA_PER_WAVE>(tile_rsrc(k_head, kt, page),
+    auto load_k = [&](int kt, int page, int rem, unsigned char* buf) __attribute__((always_inline)) {
+        dma_matrix<L::DMA_PER_WAVE>(tile_rsrc(k_head, kt, page, rem),
                                     buf + wave * L::DMA_PER_WAVE * 1024, dma_voff);
     };
-    auto load_v = [&](int kt, int page, unsigned char* buf) __attribute__((always_inline)) {
-        dma_matrix<L::DMA_PER_WAVE>(tile_rsrc(v_head, kt, page),
+    auto load_v = [&](int kt, int page, int rem, unsigned char* buf) __attribute__((always_inline)) {
+        dma_matrix<L::DMA_PER_WAVE>(tile_rsrc(v_head, kt, page, rem),
                                     buf + wave * L::DMA_PER_WAVE * 1024, dma_voff);
     };
-    // Look-ahead table (SPARSE: the kept-tile list, entry p = the tile at
-    // position p; PAGED: the batch's block table, entry p = the page of tile
-    // p).  Entries are read by a vector load one step ahead: it lands with the
-    // step's K/V loads and is waited for with them (a scalar load would make
-    // every LDS wait of the step wait for it too).  Entries past the table
-    // read 0.
+    // Look-ahead table (SPARSE: the kept-tile list, indexed by position;
+    // PAGED: the batch's block table, indexed by page).  Entries are read by a
+    // vector load one step ahead: it lands with the step's K/V loads and is
+    // waited for with them (a scalar load would make every LDS wait of the
+    // step wait for it too).  Entries past the table read 0.
     const int* const la_base = SPARSE ? sp_row + 4 : PAGED ? pg_table + (int64_t)bb * pg_stride : sp_lut;
     const int la_count = SPARSE ? kt1 : PAGED ? (S + pg_rows - 1) / pg_rows : 0;
     const __amdgpu_buffer_rsrc_t la_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)la_base, (short)0, la_count * 4, kBufferFlags);
-    auto la_entry = [&](int p) __attribute__((always_inline)) {
-        const int idx = PAGED ? p * BN / pg_rows : p;
+    auto la_entry = [&](int idx) __attribute__((always_inline)) {
         return (int)__builtin_amdgcn_raw_buffer_load_b32(la_rsrc, 4 * idx, 0, 0);
     };
 
@@ -539,22 +545,49 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
     f32x16 sc[KB];  // scores of the current tile (masked)
     int tile_a = kt0, tile_b = kt0 + 1;  // tiles of positions kt0, kt0 + 1
     int page_a = 0, page_b = 0;          // PAGED: their pages
-    int la_t1 = 0;                       // look-ahead entry of position j + 1 at step j
-    int la_nx = 0;                       // entry j + 2, in flight from step j - 1
+    int rem_a = 0, rem_b = 0;            // PAGED: their tile numbers within their pages
+    // look-ahead state at step j: the entry of position j + 1 (la_t1) and the
+    // entry of position j + 2 (la_nx, in flight since step j - 1); PAGED also
+    // carries the in-page tile numbers of positions j + 1, j + 2 (rm1, rm2)
+    // and the table index and in-page number of position j + 3 (nx_idx,
+    // nx_rem), advanced by counting instead of dividing
+    int la_t1 = 0, la_nx = 0, rm1 = 0, rm2 = 0, nx_idx = 0, nx_rem = 0;
+    auto next_tile = [&](int& idx, int& rem) __attribute__((always_inline)) {
+        if (++rem == pg_tiles) {
+            rem = 0;
+            ++idx;
+        }
+    };
     if (SPARSE) {
         tile_a = __builtin_amdgcn_readfirstlane(sp_row[4]);
         tile_b = kt1 > 1 ? __builtin_amdgcn_readfirstlane(sp_row[5]) : 0;
     }
+    int idx_b = 0;
     if (PAGED) {
-        page_a = __builtin_amdgcn_readfirstlane(la_base[tile_a * BN / pg_rows]);
-        page_b = kt0 + 1 < kt1 ? __builtin_amdgcn_readfirstlane(la_base[tile_b * BN / pg_rows]) : 0;
+        const int idx_a = kt0 / pg_tiles;
+        rem_a = kt0 - idx_a * pg_tiles;
+        idx_b = idx_a;
+        rem_b = rem_a;
+        next_tile(idx_b, rem_b);
+        page_a = __builtin_amdgcn_readfirstlane(la_base[idx_a]);
+        page_b = kt0 + 1 < kt1 ? __builtin_amdgcn_readfirstlane(la_base[idx_b]) : 0;
     }
-    load_k(tile_a, page_a, lds_k0);
-    if (kt0 + 1 < kt1) load_k(tile_b, page_b, lds_k1);
-    load_v(tile_a, page_a, lds_v0);
-    if (SPARSE || PAGED) {
-        la_t1 = SPARSE ? tile_b : page_b;
+    load_k(tile_a, page_a, rem_a, lds_k0);
+    if (kt0 + 1 < kt1) load_k(tile_b, page_b, rem_b, lds_k1);
+    load_v(tile_a, page_a, rem_a, lds_v0);
+    if (SPARSE) {
+        la_t1 = tile_b;
         la_nx = la_entry(kt0 + 2);
+    }
+    if (PAGED) {
+        la_t1 = page_b;
+        rm1 = rem_b;
+        nx_idx = idx_b;
+        nx_rem = rem_b;
+        next_tile(nx_idx, nx_rem);  // position kt0 + 2
+        la_nx = la_entry(nx_idx);
+        rm2 = nx_rem;
+        next_tile(nx_idx, nx_rem);  // position kt0 + 3
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -582,21 +615,27 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
     // tiles (and pages) of positions j + 1 and j + 2 at the step of position
     // j; advances the look-ahead by one position (every wave runs it once per
     // position, in its compute steps and its idle steps alike)
-    auto look_ahead = [&](int j, int& tn1, int& tn2, int& pn1, int& pn2) __attribute__((always_inline)) {
+    auto look_ahead = [&](int j, int& tn1, int& tn2, int& pn1, int& pn2, int& r1, int& r2)
+                          __attribute__((always_inline)) {
         tn1 = j + 1;
         tn2 = j + 2;
-        pn1 = pn2 = 0;
-        if (SPARSE || PAGED) {
-            const int e1 = la_t1, e2 = __builtin_amdgcn_readfirstlane(la_nx);
-            la_t1 = e2;
+        pn1 = pn2 = r1 = r2 = 0;
+        if (SPARSE) {
+            tn1 = la_t1;
+            tn2 = __builtin_amdgcn_readfirstlane(la_nx);
+            la_t1 = tn2;
             la_nx = la_entry(j + 3);
-            if (SPARSE) {
-                tn1 = e1;
-                tn2 = e2;
-            } else {
-                pn1 = e1;
-                pn2 = e2;
-            }
+        }
+        if (PAGED) {
+            pn1 = la_t1;
+            pn2 = __builtin_amdgcn_readfirstlane(la_nx);
+            r1 = rm1;
+            r2 = rm2;
+            la_t1 = pn2;
+            rm1 = rm2;
+            la_nx = la_entry(nx_idx);  // position j + 3
+            rm2 = nx_rem;
+            next_tile(nx_idx, nx_rem);
         }
     };
     // scores of the tile at position pos (tile number `tile`)
@@ -623,14 +662,14 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
         unsigned char* const v_next = ST ? lds_v0 : lds_v1;  // V_{j+1}
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // K_{j+1}, V_j have landed
         __syncthreads();  // ... for every wave; every wave is done with tile j-1
-        int tn1, tn2, pn1, pn2;  // tiles of positions j + 1 and j + 2, and their pages
-        look_ahead(j, tn1, tn2, pn1, pn2);
+        int tn1, tn2, pn1, pn2, r1, r2;  // tiles of positions j + 1, j + 2; their pages
+        look_ahead(j, tn1, tn2, pn1, pn2, r1, r2);
         if (!LAST) {
-            if (j + 2 < kt1) load_k(tn2, pn2, k_this);
-            load_v(tn1, pn1, v_next);
+            if (j + 2 < kt1) load_k(tn2, pn2, r2, k_this);
+            load_v(tn1, pn1, r1, v_next);
         } else {  // this wave's last tile; the workgroup may go on
-            if (j + 2 < kt1) load_k(tn2, pn2, k_this);
-            if (j + 1 < kt1) load_v(tn1, pn1, v_next);
+            if (j + 2 < kt1) load_k(tn2, pn2, r2, k_this);
+            if (j + 1 < kt1) load_v(tn1, pn1, r1, v_next);
         }
         rescale_if_moved();
         u32x4 p[NCH];
@@ -692,10 +731,10 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? 3 : 1) void fa_fwd_mfma_kernel(
         const bool st = ((j - kt0) & 1) != 0;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        int tn1, tn2, pn1, pn2;
-        look_ahead(j, tn1, tn2, pn1, pn2);
-        if (j + 2 < kt1) load_k(tn2, pn2, st ? lds_k1 : lds_k0);
-        if (j + 1 < kt1) load_v(tn1, pn1, st ? lds_v0 : lds_v1);
+        int tn1, tn2, pn1, pn2, r1, r2;
+        look_ahead(j, tn1, tn2, pn1, pn2, r1, r2);
+        if (j + 2 < kt1) load_k(tn2, pn2, r2, st ? lds_k1 : lds_k0);
+        if (j + 1 < kt1) load_v(tn1, pn1, r1, st ? lds_v0 : lds_v1);
     };
     if (!SPARSE) {
         for (int j = kt0; j + 1 < kw0; ++j) idle_step(j);
