@@ -36,6 +36,7 @@ PEAK_MFMA_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp32": 157.3}  # MI355X den
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "causal_16k"
 KERNEL_SOURCES = ["io_aware_exact_22_amd/csrc/fa_fwd_kernels.hip",
+                  "io_aware_exact_22_amd/csrc/fa_kernel_common.h",
                   "io_aware_exact_22_amd/csrc/fa_schedule.h"]
 
 
