@@ -262,31 +262,46 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_kernel(
     }
 }
 
-// ---- dK, dV: workgroup = 128 keys (4 waves x 32, lane = key), Q tiles of 64
-// rows streamed with dO and their LSE / D values.  Per Q tile and per half of
-// 32 rows: S = Q K^T and dP = dO V^T on the score MFMA with the K and V
-// fragments of the lane's key as B operands (the rows of the Q / dO tile are
-// fed in the permuted order that leaves each lane 8 consecutive rows per
-// 16-row chunk), P = exp2(c S - L) and dS = P (dP - D) in registers, then
-// dV^T += dO^T P and dK^T += Q^T dS on the P V MFMA with the tiles read
-// through the transposing LDS read.
+// ---- dK, dV: workgroup = 128 keys (4 waves x 32, lane = key), Q tiles of
+// bwd_rows(D) rows streamed with dO and their LSE / D values.  Per 32-row half
+// of a Q tile: S = Q K^T and
+// dP = dO V^T on the score MFMA with the K and V fragments of the lane's key
+// as B operands (the rows of the Q / dO tile are fed in the permuted order
+// that leaves each lane 8 consecutive rows per 16-row chunk), P = exp2(c S -
+// L) and dS = P (dP - D) in registers, then dV^T += dO^T P and dK^T += Q^T dS
+// on the P V MFMA with the tiles read through the transposing LDS read.
+// Two workgroups share a CU, so one wave's exp / dS work runs beside the
+// other's MFMAs.  D = 64 fits that with both fragments in registers and
+// 64-row tiles.  D = 128 does not fit 256 registers with both fragments, both
+// accumulators and the rows' L and D, so there the V fragment is parked in
+// LDS (each lane reads back its own 16 bytes per d chunk, conflict-free), L
+// and D are read from LDS when used, and the Q / dO tiles are 32 rows, which
+// leaves room for two workgroups' LDS in a CU (measured: the kernel 20%
+// faster than at one workgroup per CU with everything in registers; the
+// same changes at D = 64 cost 3%).
 constexpr int kBwdKeys = 128;  // keys per dK / dV workgroup
+__host__ __device__ constexpr int bwd_rows(int d) { return d == 128 ? 32 : 64; }
+__host__ __device__ constexpr bool bwd_vf_in_lds(int d) { return d == 128; }
+__host__ __device__ constexpr bool bwd_stats_when_used(int d) { return d == 128; }
 
 template <typename T, int D>
-__global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
+__global__ __launch_bounds__(256, D == 128 ? 2 : 1) void fa_bwd_dkdv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ di,
     T* __restrict__ dk, T* __restrict__ dv, int B, int H, int S, float c, float scale, int causal,
     int wl, int wr, int n_kt) {
-    typedef Tile<D, 4, 64> L;  // here: Q / dO tiles of 64 rows
+    typedef Tile<D, 4, bwd_rows(D)> L;  // here: Q / dO tiles of bwd_rows(D) rows
     constexpr int BQ = L::BN, RB = L::RB, NCH = L::NCH;
     constexpr int KSTEPS = D / 16, DB = D / 32;
+    constexpr bool VF_LDS = bwd_vf_in_lds(D);
     __shared__ __attribute__((aligned(1024))) unsigned char lds_q0[L::MAT];
     __shared__ __attribute__((aligned(1024))) unsigned char lds_q1[L::MAT];
     __shared__ __attribute__((aligned(1024))) unsigned char lds_g0[L::MAT];
     __shared__ __attribute__((aligned(1024))) unsigned char lds_g1[L::MAT];
     __shared__ __attribute__((aligned(16))) float lds_l[2][BQ];  // log2-domain LSE per row
     __shared__ __attribute__((aligned(16))) float lds_d[2][BQ];  // D per row
+    // VF_LDS: V fragments [wave][d chunk][lane]
+    __shared__ __attribute__((aligned(16))) u32x4 lds_vf[4][VF_LDS ? KSTEPS : 1][64];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hh = lane >> 5, ql = lane & 31;
@@ -317,8 +332,10 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
         return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)(uint32_t)nrec,
                                                  kBufferFlags);
     };
-    // K and V fragments of this lane's key (B operands); keys past S read 0
-    u32x4 kf[KSTEPS], vf[KSTEPS];
+    // K and V fragments of this lane's key (B operands; VF_LDS: the V fragment
+    // parked in LDS for this lane alone); keys past S read 0
+    u32x4 kf[KSTEPS], vf[VF_LDS ? 1 : KSTEPS];
+    u32x4(&vfl)[VF_LDS ? KSTEPS : 1][64] = lds_vf[wave];
     {
         const __amdgpu_buffer_rsrc_t rk = rows_rsrc(k, kw0 < S ? kw0 : S - 1);
         const __amdgpu_buffer_rsrc_t rv = rows_rsrc(v, kw0 < S ? kw0 : S - 1);
@@ -326,11 +343,16 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
             kf[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, voff + 32 * ks, 0, 0));
-            vf[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff + 32 * ks, 0, 0));
+            u32x4 vx = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, voff + 32 * ks, 0, 0));
+            if (kw0 >= S) vx = u32x4{0, 0, 0, 0};
+            if (VF_LDS)
+                vfl[VF_LDS ? ks : 0][lane] = vx;
+            else
+                vf[VF_LDS ? 0 : ks] = vx;
         }
         if (kw0 >= S) {
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) kf[ks] = vf[ks] = u32x4{0, 0, 0, 0};
+            for (int ks = 0; ks < KSTEPS; ++ks) kf[ks] = u32x4{0, 0, 0, 0};
         }
     }
     int dma_voff[L::DMA_PER_WAVE];
@@ -351,18 +373,18 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
             __builtin_amdgcn_make_buffer_rsrc((void*)(head + off), (short)0, (int)nrec, kBufferFlags),
             buf + wave * L::DMA_PER_WAVE * 1024, dma_voff);
     };
-    // row statistics of Q tile t: threads 0..63 fetch L, 64..127 fetch D
+    // row statistics of Q tile t: threads 0..BQ-1 fetch L, BQ..2BQ-1 fetch D
     const float* lse_h = lse + (int64_t)bh * S;
     const float* di_h = di + (int64_t)bh * S;
     auto fetch_stats = [&](int t) __attribute__((always_inline)) {
-        const int r = t * BQ + (tid & 63);
-        float x = tid < 64 ? __builtin_inff() : 0.f;  // rows past S: weights 0
-        if (tid < 128 && r < S) x = tid < 64 ? log2_lse(lse_h[r]) : di_h[r];
+        const int r = t * BQ + (tid % BQ);
+        float x = tid < BQ ? __builtin_inff() : 0.f;  // rows past S: weights 0
+        if (tid < 2 * BQ && r < S) x = tid < BQ ? log2_lse(lse_h[r]) : di_h[r];
         return x;
     };
     auto store_stats = [&](int stage, float x) __attribute__((always_inline)) {
-        if (tid < 64) lds_l[stage][tid] = x;
-        else if (tid < 128) lds_d[stage][tid - 64] = x;
+        if (tid < BQ) lds_l[stage][tid] = x;
+        else if (tid < 2 * BQ) lds_d[stage][tid - BQ] = x;
     };
     int kaddr[KSTEPS];
     {
@@ -383,12 +405,15 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
             for (int d = 0; d < DB; ++d) vaddr[rd][d] = vb ^ (64 * d);
         }
     }
-    // the 32 rows of half kb of `tile` against the fragment f (lane = key)
-    auto scores = [&](f32x16& s, const unsigned char* tile, int kb, const u32x4(&f)[KSTEPS]) __attribute__((always_inline)) {
+    // the 32 rows of half kb of `tile` against the K fragment (lane = key), or,
+    // FROM_LDS, against the V fragment (parked in LDS when VF_LDS)
+    auto scores = [&](f32x16& s, const unsigned char* tile, int kb, auto from_lds_tag) __attribute__((always_inline)) {
+        constexpr bool FROM_LDS = decltype(from_lds_tag)::value;
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
             const u32x4 a = *reinterpret_cast<const u32x4*>(tile + 32 * kb * RB + kaddr[kk]);
-            s = Mfma<T>::mma(a, f[kk], kk == 0 ? f32x16{0} : s);
+            const u32x4 b = !FROM_LDS ? kf[kk] : VF_LDS ? vfl[VF_LDS ? kk : 0][lane] : vf[VF_LDS ? 0 : kk];
+            s = Mfma<T>::mma(a, b, kk == 0 ? f32x16{0} : s);
         }
     };
     // acc^T += tile^T x over the two 16-row chunks of half kb
@@ -407,7 +432,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
     f32x16 acc_k[DB], acc_v[DB];
 #pragma unroll
     for (int d = 0; d < DB; ++d) acc_k[d] = acc_v[d] = f32x16{0};
-    static_assert(NCH == 4, "two halves of two 16-row chunks");
+    static_assert(NCH == 2 * (BQ / 32), "32-row halves of two 16-row chunks");
 
     load(q, t0, lds_q0);
     load(dout, t0, lds_g0);
@@ -428,23 +453,10 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
         const bool masked = r0 + BQ - 1 >= S ||
                             tile_needs_mask(ms, r0, r0 + BQ - 1, j0, kBwdKeys);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < BQ / 32; ++kb) {
             f32x16 s, dp;
-            scores(s, qst, kb, kf);
-            scores(dp, gst, kb, vf);
-            // L and D of the rows in this lane's registers: rows 32 kb + 16 (i/8) + 8 hh + i%8
-            float lr[16], dr[16];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int r = 32 * kb + 16 * (g >> 1) + 8 * hh + 4 * (g & 1);
-                const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lds_l[st][r]);
-                const f32x4 d4 = *reinterpret_cast<const f32x4*>(&lds_d[st][r]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    lr[4 * g + e] = l4[e];
-                    dr[4 * g + e] = d4[e];
-                }
-            }
+            scores(s, qst, kb, BoolTag<false>{});
+            scores(dp, gst, kb, BoolTag<true>{});
             if (masked) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
@@ -456,14 +468,37 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dkdv_kernel(
                     s[i] = ok ? s[i] : kNegInf;
                 }
             }
+            // L and D of the rows in registers 4g .. 4g+3: rows 32 kb + 16 (g/2)
+            // + 8 hh + 4 (g%2) + 0..3 (read all up front, or each group when used)
+            auto stats = [&](int g, f32x4& l4, f32x4& d4) __attribute__((always_inline)) {
+                const int r = 32 * kb + 16 * (g >> 1) + 8 * hh + 4 * (g & 1);
+                l4 = *reinterpret_cast<const f32x4*>(&lds_l[st][r]);
+                d4 = *reinterpret_cast<const f32x4*>(&lds_d[st][r]);
+            };
+            f32x4 lpre[4], dpre[4];
+            if (!bwd_stats_when_used(D)) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) stats(g, lpre[g], dpre[g]);
+            }
             u32x4 pp[2], ds[2];
 #pragma unroll
-            for (int i = 0; i < 16; i += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -lr[i]));
-                const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i + 1], c, -lr[i + 1]));
-                pp[i >> 3][(i & 7) >> 1] = Mfma<T>::pack2(p0, p1);
-                ds[i >> 3][(i & 7) >> 1] =
-                    Mfma<T>::pack2(p0 * (dp[i] - dr[i]), p1 * (dp[i + 1] - dr[i + 1]));
+            for (int g = 0; g < 4; ++g) {
+                f32x4 l4, d4;
+                if (bwd_stats_when_used(D)) {
+                    stats(g, l4, d4);
+                } else {
+                    l4 = lpre[g];
+                    d4 = dpre[g];
+                }
+#pragma unroll
+                for (int e = 0; e < 4; e += 2) {
+                    const int i = 4 * g + e;
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c, -l4[e]));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i + 1], c, -l4[e + 1]));
+                    pp[i >> 3][(i & 7) >> 1] = Mfma<T>::pack2(p0, p1);
+                    ds[i >> 3][(i & 7) >> 1] =
+                        Mfma<T>::pack2(p0 * (dp[i] - d4[e]), p1 * (dp[i + 1] - d4[e + 1]));
+                }
             }
             tmul(acc_v, pp, gst, kb);
             tmul(acc_k, ds, qst, kb);
