@@ -81,6 +81,10 @@ def _load():
         lib.fa_oracle_fwd_rows_blocksparse.restype = ctypes.c_int
         lib.fa_oracle_gather_pages.argtypes = [vp, i64, i64, i64, vp, i64, i64, i64, i64, i64, vp]
         lib.fa_oracle_gather_pages.restype = ctypes.c_int
+        lib.fa_oracle_bwd_sampled.argtypes = [vp, vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, dp,
+                                              ctypes.c_int, i64, i64, i64, i64, vp, i64, vp, i64,
+                                              vp, vp, vp, ctypes.c_int]
+        lib.fa_oracle_bwd_sampled.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -256,6 +260,28 @@ def bwd(q, k, v, dout, scale: float, causal: bool = False, window_size=(-1, -1),
                            dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle: fa_oracle_bwd failed ({rc})")
+    return dq, dk, dv
+
+
+def bwd_sampled(q, k, v, dout, scale: float, causal: bool, window_size, b: int, h: int, rows,
+                keys, nthreads: int = 0):
+    """The gradients of ``bwd`` for the query ``rows`` (dq) and the ``keys`` (dk,
+    dv) of head (b, h), without materialising the S x S matrices.  Returns
+    (dq [len(rows), D], dk [len(keys), D], dv [len(keys), D]) fp64 numpy."""
+    _check_inputs(q, k, v)
+    _check_inputs(q, dout, dout)
+    lib = _load()
+    B, S, H, D = q.shape
+    wl, wr = _window(window_size)
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    c = np.ascontiguousarray(np.asarray(keys, dtype=np.int64))
+    dq = np.empty((len(r), D)); dk = np.empty((len(c), D)); dv = np.empty((len(c), D))
+    rc = lib.fa_oracle_bwd_sampled(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                                   _dtype_code(q), B, H, S, D, float(scale), int(bool(causal)), wl,
+                                   wr, b, h, r.ctypes.data, len(r), c.ctypes.data, len(c),
+                                   dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle: fa_oracle_bwd_sampled failed ({rc})")
     return dq, dk, dv
 
 

@@ -488,3 +488,129 @@ int fa_oracle_bwd(const void* q, const void* k, const void* v, const void* dout,
     free(Q); free(K); free(V); free(dO); free(P); free(dS);
     return 0;
 }
+
+/*
+ * fa_oracle_bwd_sampled -- the gradients of fa_oracle_bwd for chosen query rows
+ * (dq) and chosen keys (dk, dv) of one (b, h), without the S x S matrices:
+ * every row's max m_i, sum l_i and D_i = sum_j p_ij dP_ij are computed first,
+ * then p_ij = exp(s_ij - m_i) / l_i and dS_ij = p_ij (dP_ij - D_i) are formed
+ * again wherever a sampled row or key needs them:
+ *   dQ_i = scale * sum_j dS_ij k_j,  dK_j = scale * sum_i dS_ij q_i,
+ *   dV_j = sum_i p_ij dO_i.
+ * Equal to fa_oracle_bwd's entries up to fp64 rounding (summation order).
+ * rows[n_rows], keys[n_keys] in [0, S); dq_rows is [n_rows, D], dk_keys and
+ * dv_keys [n_keys, D], fp64.  A row with no allowed key contributes nothing.
+ */
+int fa_oracle_bwd_sampled(const void* q, const void* k, const void* v, const void* dout,
+                          int dtype, int64_t B, int64_t H, int64_t S, int64_t D, double scale,
+                          int causal, int64_t wl, int64_t wr, int64_t b, int64_t h,
+                          const int64_t* rows, int64_t n_rows, const int64_t* keys,
+                          int64_t n_keys, double* dq_rows, double* dk_keys, double* dv_keys,
+                          int nthreads) {
+    if (orc_check(dtype, B, H, S, D, wl, wr)) return -1;
+    if (b < 0 || b >= B || h < 0 || h >= H || n_rows < 0 || n_keys < 0) return -1;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= S) return -1;
+    for (int64_t c = 0; c < n_keys; ++c)
+        if (keys[c] < 0 || keys[c] >= S) return -1;
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+    const size_t sd = (size_t)(S * D);
+    double* Qh = (double*)malloc(sizeof(double) * sd);
+    double* Kh = (double*)malloc(sizeof(double) * sd);
+    double* Vh = (double*)malloc(sizeof(double) * sd);
+    double* Gh = (double*)malloc(sizeof(double) * sd); /* dO */
+    double* rmax = (double*)malloc(sizeof(double) * (size_t)S);
+    double* rsum = (double*)malloc(sizeof(double) * (size_t)S);
+    double* rdot = (double*)malloc(sizeof(double) * (size_t)S); /* D_i */
+    if (!Qh || !Kh || !Vh || !Gh || !rmax || !rsum || !rdot) {
+        free(Qh); free(Kh); free(Vh); free(Gh); free(rmax); free(rsum); free(rdot);
+        return -2;
+    }
+#define ORC_SIDX(s_, d_) (((b * S + (s_)) * H + h) * D + (d_))
+    for (int64_t t = 0; t < S; ++t)
+        for (int64_t d = 0; d < D; ++d) {
+            Qh[t * D + d] = orc_load(q, dtype, ORC_SIDX(t, d));
+            Kh[t * D + d] = orc_load(k, dtype, ORC_SIDX(t, d));
+            Vh[t * D + d] = orc_load(v, dtype, ORC_SIDX(t, d));
+            Gh[t * D + d] = orc_load(dout, dtype, ORC_SIDX(t, d));
+        }
+#undef ORC_SIDX
+    /* per-row statistics: every row when keys are sampled, else the sampled rows */
+    const int64_t n_stat = n_keys > 0 ? S : n_rows;
+#pragma omp parallel for schedule(dynamic, 16) num_threads(nthreads)
+    for (int64_t x = 0; x < n_stat; ++x) {
+        const int64_t i = n_keys > 0 ? x : rows[x];
+        double m = -INFINITY;
+        for (int64_t j = 0; j < S; ++j) {
+            if (!orc_allowed(i, j, causal, wl, wr)) continue;
+            double acc = 0.0;
+            for (int64_t d = 0; d < D; ++d) acc += Qh[i * D + d] * Kh[j * D + d];
+            const double sij = scale * acc;
+            if (isnan(sij) || isnan(m)) m = NAN;
+            else if (sij > m) m = sij;
+        }
+        double l = 0.0, di = 0.0;
+        if (m != -INFINITY) {
+            for (int64_t j = 0; j < S; ++j) {
+                if (!orc_allowed(i, j, causal, wl, wr)) continue;
+                double acc = 0.0, g = 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    acc += Qh[i * D + d] * Kh[j * D + d];
+                    g += Gh[i * D + d] * Vh[j * D + d];
+                }
+                const double e = exp(scale * acc - m);
+                l += e;
+                di += e * g; /* divided by l below: sum_j p_ij dP_ij */
+            }
+            di /= l;
+        }
+        rmax[i] = m;
+        rsum[i] = l;
+        rdot[i] = di;
+    }
+    /* p_ij and dS_ij of an allowed pair, from the row statistics */
+#define ORC_P_DS(i_, j_, p_, ds_)                                                    \
+    do {                                                                             \
+        double a_ = 0.0, g_ = 0.0;                                                   \
+        for (int64_t d_ = 0; d_ < D; ++d_) {                                         \
+            a_ += Qh[(i_) * D + d_] * Kh[(j_) * D + d_];                             \
+            g_ += Gh[(i_) * D + d_] * Vh[(j_) * D + d_];                             \
+        }                                                                            \
+        (p_) = exp(scale * a_ - rmax[i_]) / rsum[i_];                                \
+        (ds_) = (p_) * (g_ - rdot[i_]);                                              \
+    } while (0)
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const int64_t i = rows[r];
+        double* out = dq_rows + r * D;
+        for (int64_t d = 0; d < D; ++d) out[d] = 0.0;
+        if (rmax[i] == -INFINITY) continue;
+        for (int64_t j = 0; j < S; ++j) {
+            if (!orc_allowed(i, j, causal, wl, wr)) continue;
+            double p, ds;
+            ORC_P_DS(i, j, p, ds);
+            for (int64_t d = 0; d < D; ++d) out[d] += ds * Kh[j * D + d];
+        }
+        for (int64_t d = 0; d < D; ++d) out[d] *= scale;
+    }
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+    for (int64_t c = 0; c < n_keys; ++c) {
+        const int64_t j = keys[c];
+        double* ok = dk_keys + c * D;
+        double* ov = dv_keys + c * D;
+        for (int64_t d = 0; d < D; ++d) ok[d] = ov[d] = 0.0;
+        for (int64_t i = 0; i < S; ++i) {
+            if (!orc_allowed(i, j, causal, wl, wr) || rmax[i] == -INFINITY) continue;
+            double p, ds;
+            ORC_P_DS(i, j, p, ds);
+            for (int64_t d = 0; d < D; ++d) {
+                ok[d] += ds * Qh[i * D + d];
+                ov[d] += p * Gh[i * D + d];
+            }
+        }
+        for (int64_t d = 0; d < D; ++d) ok[d] *= scale;
+    }
+#undef ORC_P_DS
+    free(Qh); free(Kh); free(Vh); free(Gh); free(rmax); free(rsum); free(rdot);
+    return 0;
+}

@@ -439,3 +439,36 @@ def test_bwd_lengths(S, causal):
 def test_bwd_gpt_causal_2k():
     """The 2K causal workload's shape (B2 H16 S2048 D64 bf16), every element."""
     check_bwd(2, 2048, 16, 64, torch.bfloat16, True, (-1, -1), seed=81)
+
+
+def test_bwd_causal_16k_sampled_and_column_sums():
+    """The backward at the benchmark's full size and launch configuration
+    (1 x 16 heads x 16384 x 128, bf16, causal): sampled dq rows and dk / dv
+    keys of two heads against the oracle's sampled gradients, within
+    TOL_GRAD x max(1, max |reference|); and, over every head and d, the column
+    sums that hold for any inputs, sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i,
+    within 2% of the columns' root-sum-square."""
+    B, S, H, D = 1, 16384, 16, 128
+    scale = 1.0 / math.sqrt(D)
+    q, k, v = make_qkv(B, S, H, D, torch.bfloat16, 5)
+    do = make_qkv(B, S, H, D, torch.bfloat16, 6)[0]
+    print("run bwd causal 16384 x 16 heads", flush=True)
+    dq, dk, dv = gpu_bwd(q, k, v, do, scale, True, (-1, -1))
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert torch.isfinite(g.float()).all(), name
+    dkd, dvd, dod = (t.double()[0] for t in (dk, dv, do))  # [S, H, D]
+    sum_k = dkd.sum(0)
+    assert (sum_k.abs() <= 0.02 * dkd.pow(2).sum(0).sqrt()).all(), "sum_j dK_j != 0"
+    sum_v = dvd.sum(0) - dod.sum(0)
+    assert (sum_v.abs() <= 0.02 * dod.pow(2).sum(0).sqrt()).all(), "sum_j dV_j != sum_i dO_i"
+    rows = [0, 1, 63, 64, 4095, 8192, 16383]
+    keys = [0, 1, 127, 128, 8191, 16320, 16383]
+    for h in (0, 15):
+        rq, rk, rv = oracle.bwd_sampled(q, k, v, do, scale, True, (-1, -1), 0, h, rows, keys)
+        for name, g, r in (("dq", dq[0, rows, h], rq), ("dk", dk[0, keys, h], rk),
+                           ("dv", dv[0, keys, h], rv)):
+            g = g.double().numpy()
+            bound = TOL_GRAD[torch.bfloat16] * max(1.0, float(np.max(np.abs(r))))
+            err = float(np.max(np.abs(g - r)))
+            print(f"bwd 16k head {h}: {name} max err {err:.3e} (bound {bound:.3e})", flush=True)
+            assert err <= bound, f"head {h} {name}: {err} > {bound}"

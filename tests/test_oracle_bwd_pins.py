@@ -125,3 +125,26 @@ def test_bwd_causal_row0():
     do = make_qkv(1, 50, 2, 16, torch.bfloat16, 62)[0]
     dq, _, _ = oracle.bwd(q, k, v, do, 0.25, True, (-1, -1))
     assert not dq[:, 0].any()
+
+
+@pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (-1, -1)), (False, (3, 5)),
+                                           (True, (6, -1))])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_sampled_gradients_equal_the_full_backward(causal, window, dtype):
+    """The sampled backward (dq of chosen rows, dk and dv of chosen keys, with
+    the S x S matrices formed again entry by entry) gives the full backward's
+    entries up to fp64 summation order; it is what the full-size GPU checks
+    use."""
+    B, S, H, D = 2, 29, 2, 16
+    q, k, v = make_qkv(B, S, H, D, dtype, 71)
+    do = make_qkv(B, S, H, D, dtype, 72)[0]
+    dq, dk, dv = oracle.bwd(q, k, v, do, 0.3, causal, window)
+    rows, keys = [0, 1, 7, 28], [0, 13, 27, 28]
+    for b, h in ((0, 1), (1, 0)):
+        sq, sk, sv = oracle.bwd_sampled(q, k, v, do, 0.3, causal, window, b, h, rows, keys)
+        np.testing.assert_allclose(sq, dq[b, rows, h], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(sk, dk[b, keys, h], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(sv, dv[b, keys, h], rtol=1e-12, atol=1e-13)
+    # rows only: no key statistics needed
+    sq2, _, _ = oracle.bwd_sampled(q, k, v, do, 0.3, causal, window, 0, 0, [5, 6], [])
+    np.testing.assert_allclose(sq2, dq[0, [5, 6], 0], rtol=1e-12, atol=1e-13)
