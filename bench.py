@@ -187,6 +187,10 @@ def main() -> int:
                     help="time fa_fwd_paged with K/V cut into pages of this many rows (a multiple "
                          "of 64), placed at a seeded random permutation of a pool with spare "
                          "pages; combines with --splitkv")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="after the timed steps, this many more launches each preceded (outside "
+                         "the events) by a 512 MiB write that evicts L2 and the MALL; their "
+                         "kernel time is reported as roofline.cold_cache_kernel_ms (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the benchmark, run --steps plain device copies of this many "
                          "MiB (the reference kernel for scaling HBM byte counters)")
@@ -329,6 +333,20 @@ def main() -> int:
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
     launch_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    # cold caches: a 512 MiB write before each launch evicts L2 and the 256 MB
+    # MALL; only the launch itself lies between the events
+    cold_ms = []
+    if args.cold_steps > 0:
+        flush = torch.empty(512 << 18, dtype=torch.float32, device=dev)
+        for _ in range(args.cold_steps):
+            flush.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            torch.cuda.synchronize(dev)
+            cold_ms.append(e0.elapsed_time(e1))
+        del flush
 
     if bs is not None:
         pairs = blocksparse_pairs(w.S, w.causal, w.window, bs[0][0], 128, 64)
@@ -360,6 +378,9 @@ def main() -> int:
     roof["traffic"] = (None if (args.backward or n_splits is not None or bs is not None or paged)
                        else measured_traffic(w.name))
     roof["kernel_ms"] = avg_launch_ms
+    roof["kernel_ms_median"] = float(np.median(launch_ms))
+    roof["kernel_ms_min"] = float(np.min(launch_ms))
+    roof["cold_cache_kernel_ms"] = float(np.median(cold_ms)) if cold_ms else None
     roof["algorithmic_flops_per_launch"] = flops
     roof["algorithmic_bytes_per_launch"] = alg_bytes
 
@@ -384,6 +405,12 @@ def main() -> int:
         "dtype": dt_name,
         "data": "synthetic",
         "pct_of_peak": 100.0 * tflops / peak,
+        # the common S/2 count for a causal mask over the whole sequence, for
+        # comparison with figures quoted that way (the value counts exact pairs)
+        "tflops_causal_half_convention": (
+            (10.0 if args.backward else 4.0) * w.B * w.H * w.S * (w.S / 2) * w.D
+            / (ms_per_step * 1e-3) / 1e12
+            if (w.causal and tuple(w.window) == (-1, -1) and bs is None) else None),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "S": w.S, "D": w.D,
                    "causal": w.causal, "window": list(w.window), "S_eff": s_eff,
                    "flops_per_step": flops, "parallelism": "single GPU",
