@@ -131,6 +131,50 @@ def cpu_baseline(w, q, k, v, target_s: float = 15.0):
     }
 
 
+def cpu_baseline_bwd(w, q, k, v, dout, target_s: float = 15.0):
+    """Time the CPU oracle's backward on a bounded sample: dq of chunks of 256
+    query rows of batch 0, from the middle of head 0 on through the following
+    rows and heads, until about target_s seconds (oracle.bwd_sampled: per-row
+    statistics, then P and dS formed again for those rows).  Those rows' part
+    of the metric is the S, dP and dQ products, 6 flops per allowed pair and d."""
+    import numpy as np
+
+    import oracle
+
+    threads = min(16, len(os.sched_getaffinity(0)))
+    wl, wr = w.window
+    CH = 256
+    chunks = [(h, r) for h in range(w.H) for r in range(0, w.S, CH)]
+    first = (w.S // 2) // CH
+    chunks = chunks[first:] + chunks[:first]
+    fl, dt, rows = 0.0, 0.0, 0
+    for h, r0 in chunks:
+        r1 = min(w.S, r0 + CH)
+        t0 = time.perf_counter()
+        oracle.bwd_sampled(q, k, v, dout, w.scale, w.causal, w.window, 0, h, list(range(r0, r1)),
+                           [], nthreads=threads)
+        dt += time.perf_counter() - t0
+        i = np.arange(r0, r1, dtype=np.int64)
+        lo = np.zeros_like(i) if wl < 0 else np.maximum(0, i - wl)
+        hi = np.full_like(i, w.S - 1) if wr < 0 else np.minimum(w.S - 1, i + wr)
+        if w.causal:
+            hi = np.minimum(hi, i)
+        fl += 6.0 * float(np.maximum(0, hi - lo + 1).sum()) * w.D
+        rows += r1 - r0
+        if dt >= target_s:
+            break
+    return {
+        "value": fl / dt / 1e12,
+        "unit": "TFLOPS",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{w.name} backward: dq of {rows} rows of batch 0 in chunks of {CH} from row "
+                   f"{first * CH} of head 0 on (fp64 oracle, P and dS formed again per row); "
+                   f"{fl / 1e9:.1f} GFLOP (S, dP, dQ products of those rows) in {dt:.1f} s on "
+                   f"{threads} threads"),
+    }
+
+
 def cpu_baseline_blocksparse(w, q, k, v, mask, bm, bn, target_s: float = 15.0):
     """Time the CPU oracle's block-sparse rows: chunks of 512 rows of batch 0,
     from the middle of head 0 on through the following rows and heads, until
@@ -261,7 +305,8 @@ def main() -> int:
                                      window_size=w.window, stream=stream)
         g = torch.Generator(device="cpu")
         g.manual_seed(w.seed + 1000)
-        dod = torch.randn(qd.shape, generator=g, dtype=torch.float32).to(w.dtype).to(dev)
+        do_cpu = torch.randn(qd.shape, generator=g, dtype=torch.float32).to(w.dtype)
+        dod = do_cpu.to(dev)
         ws_b = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
         dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
 
@@ -422,12 +467,14 @@ def main() -> int:
                    **({} if bs is None else {"block_mask": bs[1]})},
         "roofline": roof,
     }
-    if not args.no_cpu_baseline and bs is not None:
-        rec["cpu_baseline"] = cpu_baseline_blocksparse(w, q, k, v, bs[0].numpy(), 128, 64)
-    elif not args.no_cpu_baseline and not args.backward and n_splits is None and not paged:
-        rec["cpu_baseline"] = cpu_baseline(w, q, k, v)
-    else:
+    if args.no_cpu_baseline:
         rec["cpu_baseline"] = None
+    elif bs is not None:
+        rec["cpu_baseline"] = cpu_baseline_blocksparse(w, q, k, v, bs[0].numpy(), 128, 64)
+    elif args.backward:
+        rec["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, do_cpu)
+    else:  # fa_fwd, fa_fwd_splitkv and fa_fwd_paged compute the same definition
+        rec["cpu_baseline"] = cpu_baseline(w, q, k, v)
     print(json.dumps(rec), flush=True)
     return 0
 
