@@ -544,6 +544,11 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
             update_max(sn);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) sc[kb] = sn[kb];
+            // The row sum of this tile's weights is finished inside this step,
+            // among its MFMAs.  Without this the compiler sinks the adds of
+            // every other step into the next one, ahead of its first MFMA,
+            // where no MFMA hides them (and ten P V MFMAs go without VALU work).
+            asm volatile("" : "+v"(l_run));
             // interleave: every MFMA of the step (score MFMAs first, then P V)
             // carries the same share of the VALU work -- the weights of tile
             // j, then the row max of tile j+1 -- so neither phase is
