@@ -138,7 +138,10 @@ int fa_fwd_tile_schedule(int64_t S, int64_t D, int dtype, int causal, int64_t wi
  * tiles (its heads' K/V stay in its L2); with causal = 1 each XCD visits its
  * block's Q tiles heaviest first across heads (more K/V tiles to walk =
  * earlier), so that light tiles end the launch (thread-block load balance,
- * the note closing [FA] section 1).
+ * the note closing [FA] section 1).  With causal = 1 and fewer than 8
+ * (batch, head) pairs, whole heads cannot go to XCDs: the tiles of all heads
+ * are then ordered heaviest first and dealt to the XCDs in snake order
+ * (0..7, 7..0, ...), which gives every XCD the same share of the work.
  * Returns FA_OK, or FA_ERR_* for bad arguments or wg outside the grid.
  */
 int fa_fwd_workgroup_tile(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int causal,
@@ -200,6 +203,26 @@ int fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t S, int64_t D, in
 int fa_fwd_splitkv_auto_splits(int64_t B, int64_t H, int64_t S, int64_t D, int causal,
                                int64_t window_left, int64_t window_right, int dtype,
                                int64_t* n_splits);
+
+/*
+ * fa_fwd_splitkv_workgroup_tile -- host-side view of the launch order of
+ * fa_fwd_splitkv (and of fa_fwd_paged with n_splits parts): the (b * H + h,
+ * Q tile, part) that workgroup `wg` of its attention kernel processes.  Pure
+ * function, no HIP call.  With n_splits = 1, or fp32 inputs (which run in one
+ * part), it is fa_fwd_workgroup_tile with part 0.  Otherwise the grid has
+ * B * H * n_q_tiles * n_splits workgroups and the map is a bijection onto the
+ * (batch-head, Q tile, part) triples.  With causal = 1 the parts of all tiles
+ * are ordered heaviest tile first and dealt to the 8 XCDs in snake order, so
+ * that every XCD gets the same share of the work (thread-block load balance,
+ * the note closing [FA] section 1); without the causal mask a tile's parts
+ * are consecutive workgroups, and the tiles follow fa_fwd_workgroup_tile.
+ * Returns FA_OK, or FA_ERR_* for bad arguments (FA_ERR_SPLITS for n_splits
+ * outside [1, FA_MAX_SPLITS]) or wg outside the grid.
+ */
+int fa_fwd_splitkv_workgroup_tile(int64_t B, int64_t H, int64_t S, int64_t D, int dtype,
+                                  int causal, int64_t window_left, int64_t window_right,
+                                  int64_t n_splits, int64_t wg, int64_t* bh, int64_t* q_tile,
+                                  int64_t* part);
 
 /*
  * fa_bwd -- gradients of fa_fwd's output with respect to q, k and v for an

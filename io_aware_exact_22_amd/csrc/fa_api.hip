@@ -239,6 +239,36 @@ FA_API int fa_fwd_workgroup_tile(int64_t B, int64_t H, int64_t S, int64_t D, int
     return FA_OK;
 }
 
+FA_API int fa_fwd_splitkv_workgroup_tile(int64_t B, int64_t H, int64_t S, int64_t D, int dtype,
+                                         int causal, int64_t window_left, int64_t window_right,
+                                         int64_t n_splits, int64_t wg, int64_t* bh,
+                                         int64_t* q_tile, int64_t* part) {
+    if (!part) return FA_ERR_NULL;
+    if (n_splits < 1 || n_splits > FA_MAX_SPLITS) return FA_ERR_SPLITS;
+    if (n_splits == 1 || dtype == FA_DTYPE_FP32) {  // the unsplit launch
+        *part = 0;
+        return fa_fwd_workgroup_tile(B, H, S, D, dtype, causal, window_left, window_right, wg, bh,
+                                     q_tile);
+    }
+    if (!bh || !q_tile) return FA_ERR_NULL;
+    int64_t nbytes, lbytes;
+    const int rc = check_problem(B, H, S, D, causal, window_left, window_right, dtype, &nbytes,
+                                 &lbytes);
+    if (rc != FA_OK) return rc;
+    const int64_t wlc = window_left >= S ? -1 : window_left;
+    const int64_t wrc = window_right >= S ? -1 : window_right;
+    const int64_t BM = fa::q_tile_rows(dtype, D, S, wlc, wrc);
+    const int64_t nq = (S + BM - 1) / BM;
+    if (wg < 0 || wg >= B * H * nq * n_splits) return FA_ERR_SHAPE;
+    uint32_t r_bh, r_qt, r_part;
+    fa::workgroup_tile_part((uint32_t)wg, (uint32_t)(B * H), (uint32_t)nq, (uint32_t)n_splits,
+                            causal != 0, &r_bh, &r_qt, &r_part);
+    *bh = r_bh;
+    *q_tile = r_qt;
+    *part = r_part;
+    return FA_OK;
+}
+
 FA_API int fa_fwd_tile_schedule(int64_t S, int64_t D, int dtype, int causal, int64_t window_left,
                                 int64_t window_right, int64_t q_tile, int64_t* bm, int64_t* bn,
                                 int64_t* n_q_tiles, int64_t* kt_begin, int64_t* kt_end,

@@ -99,13 +99,14 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     const int ql = lane & 31;   // query row of this lane within the wave
 
     // ---- workgroup -> (b, h, q tile[, part]); causal: heaviest Q tiles first per XCD
-    uint32_t bh, qt32, wg = blockIdx.x;
-    int sp = 0;  // K/V part (SPLIT)
-    if (SPLIT) {
-        sp = (int)(wg % (uint32_t)n_splits);
-        wg /= (uint32_t)n_splits;
-    }
-    workgroup_tile(wg, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt, causal != 0, &bh, &qt32);
+    uint32_t bh, qt32, sp32 = 0;
+    if (SPLIT)  // K/V part sp of the tile
+        workgroup_tile_part(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt,
+                            (uint32_t)n_splits, causal != 0, &bh, &qt32, &sp32);
+    else
+        workgroup_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt, causal != 0, &bh,
+                       &qt32);
+    const int sp = (int)sp32;
     const int qt = (int)qt32;
     const int bb = (int)(bh / (uint32_t)H), h = (int)(bh % (uint32_t)H);
 

@@ -119,10 +119,34 @@ __host__ __device__ inline void q_tile_interior_range(const MaskSpec& m, int64_t
 #ifndef FA_LIGHT_DIV
 #define FA_LIGHT_DIV 4  // the lightest 1/FA_LIGHT_DIV of each head's Q tiles close the launch
 #endif
+//
+// Fewer (batch, head) pairs than XCDs (by_weight): whole heads cannot go to
+// XCDs, and contiguous blocks of one head's heaviest-first list would give one
+// XCD its heaviest Q tiles and another its lightest.  The tiles are then dealt
+// in snake order instead (snake_item below): every XCD gets one tile of each
+// group of eight consecutive weights, heaviest first.
+constexpr uint32_t kXcds = 8;
+
+// Item of a weight-sorted list (position 0 = heaviest) that workgroup w runs:
+// workgroup w is XCD w % 8's (w / 8)-th workgroup, and the 8 items of group k
+// go to the XCDs in the order 0..7 for even k and 7..0 for odd k, so that the
+// XCDs' summed weights differ by at most about the heaviest item.  A last,
+// partial group goes in order.  A bijection of [0, n).
+__host__ __device__ inline uint32_t snake_item(uint32_t w, uint32_t n) {
+    const uint32_t x = w % kXcds, k = w / kXcds;
+    const bool whole = kXcds * k + kXcds <= n;
+    return kXcds * k + ((whole && (k & 1)) ? kXcds - 1 - x : x);
+}
+
 __host__ __device__ inline void workgroup_tile(uint32_t w, uint32_t n_bh, uint32_t n_qt,
                                                bool by_weight, uint32_t* bh, uint32_t* qt) {
-    constexpr uint32_t kXcds = 8;
     const uint32_t n = n_bh * n_qt;
+    if (by_weight && n_bh < kXcds) {  // list: rank-major, heads next to each other
+        const uint32_t p = snake_item(w, n);
+        *bh = p % n_bh;
+        *qt = n_qt - 1 - p / n_bh;
+        return;
+    }
     const uint32_t xcd = w % kXcds, idx = w / kXcds;
     const uint32_t per = n / kXcds, rem = n % kXcds;
     const uint32_t s = xcd * per + (xcd < rem ? xcd : rem);  // block start in the list
@@ -185,6 +209,27 @@ __host__ __device__ inline void workgroup_tile(uint32_t w, uint32_t n_bh, uint32
     }
     *bh = row;
     *qt = n_qt - 1 - rank;
+}
+
+// Workgroup w of a split launch (n_parts K/V parts per Q tile) -> (b * H + h,
+// Q tile, part).  by_weight: the parts of all tiles form one list, heaviest
+// tile first (rank-major, then head, then part: a part's weight is its tile's
+// over n_parts), dealt to the XCDs in snake order.  Otherwise the parts of a
+// tile are consecutive workgroups and the tiles follow workgroup_tile.  A
+// bijection of [0, n_bh * n_qt * n_parts).
+__host__ __device__ inline void workgroup_tile_part(uint32_t w, uint32_t n_bh, uint32_t n_qt,
+                                                    uint32_t n_parts, bool by_weight,
+                                                    uint32_t* bh, uint32_t* qt, uint32_t* part) {
+    if (!by_weight) {
+        *part = w % n_parts;
+        workgroup_tile(w / n_parts, n_bh, n_qt, false, bh, qt);
+        return;
+    }
+    const uint32_t p = snake_item(w, n_bh * n_qt * n_parts);
+    const uint32_t t = p / n_parts;
+    *part = p % n_parts;
+    *bh = t % n_bh;
+    *qt = n_qt - 1 - t / n_bh;
 }
 
 }  // namespace fa

@@ -1,7 +1,8 @@
 """ctypes binding of libfa_mi355x (declared in include/fa_mi355x.h).
 
 Same names as the C ABI: ``fa_fwd``, ``fa_fwd_check_args``,
-``fa_status_string``, ``fa_fwd_tile_schedule``, ``fa_fwd_workgroup_tile``, ``fa_fwd_splitkv``,
+``fa_status_string``, ``fa_fwd_tile_schedule``, ``fa_fwd_workgroup_tile``,
+``fa_fwd_splitkv_workgroup_tile``, ``fa_fwd_splitkv``,
 ``fa_fwd_splitkv_workspace_size``, ``fa_fwd_splitkv_auto_splits``, ``fa_bwd``,
 ``fa_bwd_workspace_size``, ``fa_fwd_blocksparse``, ``fa_fwd_blocksparse_workspace_size``,
 ``fa_fwd_paged``; plus ``flash_attn_fwd`` (and ``flash_attn_fwd_splitkv``, ``flash_attn_bwd``,
@@ -71,6 +72,9 @@ def _load():
         lib.fa_fwd_workgroup_tile.argtypes = [i64, i64, i64, i64, cint, cint, i64, i64, i64, p64,
                                               p64]
         lib.fa_fwd_workgroup_tile.restype = cint
+        lib.fa_fwd_splitkv_workgroup_tile.argtypes = [i64, i64, i64, i64, cint, cint, i64, i64,
+                                                      i64, i64, p64, p64, p64]
+        lib.fa_fwd_splitkv_workgroup_tile.restype = cint
         lib.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, cint,
                                        i64, i64, cint, i64, vp, i64, vp]
         lib.fa_fwd_splitkv.restype = cint
@@ -143,6 +147,19 @@ def fa_fwd_workgroup_tile(B: int, H: int, S: int, D: int, dtype: int, causal: in
     if rc != 0:
         raise FaError(rc, "fa_fwd_workgroup_tile")
     return bh.value, qt.value
+
+
+def fa_fwd_splitkv_workgroup_tile(B: int, H: int, S: int, D: int, dtype: int, causal: int,
+                                  window_left: int, window_right: int, n_splits: int,
+                                  wg: int) -> tuple[int, int, int]:
+    """Host view of the split launch order: (b * H + h, Q tile, part) of workgroup ``wg``."""
+    bh, qt, part = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    rc = _load().fa_fwd_splitkv_workgroup_tile(B, H, S, D, dtype, causal, window_left,
+                                               window_right, n_splits, wg, ctypes.byref(bh),
+                                               ctypes.byref(qt), ctypes.byref(part))
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_splitkv_workgroup_tile")
+    return bh.value, qt.value, part.value
 
 
 def fa_fwd_splitkv(q: int, k: int, v: int, out: int, lse: int, B: int, H: int, S: int, D: int,

@@ -25,7 +25,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_check_args", "fa_status_string", "fa_fwd_tile_schedule",
-                          "fa_fwd_workgroup_tile", "fa_fwd_splitkv",
+                          "fa_fwd_workgroup_tile", "fa_fwd_splitkv_workgroup_tile",
+                          "fa_fwd_splitkv",
                           "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv_auto_splits",
                           "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_blocksparse",
                           "fa_fwd_blocksparse_workspace_size", "fa_fwd_paged"}
@@ -270,7 +271,9 @@ def test_workgroup_order(B, H, S, causal):
     tile list.  With the causal mask the XCD runs the heavy three quarters of
     each head's Q tiles head by head, heaviest first, and then the lightest
     quarter of all its heads in non-increasing visited K/V tile count, after
-    every heavier tile."""
+    every heavier tile.  With the causal mask and fewer than 8 (batch, head)
+    pairs the tiles are instead dealt to the XCDs in snake order of weight:
+    each XCD runs heaviest first and the XCDs' summed K/V steps are balanced."""
     dt = fa.FA_DTYPE_BF16
     nq = fa.fa_fwd_tile_schedule(S, 128, dt, causal, -1, -1, 0)["n_q_tiles"]
     n = B * H * nq
@@ -278,6 +281,14 @@ def test_workgroup_order(B, H, S, causal):
     visits = [x["kt_end"] - x["kt_begin"] for x in visits]
     tiles = [fa.fa_fwd_workgroup_tile(B, H, S, 128, dt, causal, -1, -1, w) for w in range(n)]
     assert sorted(tiles) == [(bh, qt) for bh in range(B * H) for qt in range(nq)]
+    if causal and B * H < 8:
+        check_snake_order([visits[qt] for _, qt in tiles])
+        # the list is rank-major: heads next to each other, heaviest rank first
+        order = sorted(range(n), key=lambda w: (w // 8, w % 8 if (w // 8) % 2 == 0 or
+                                                (w // 8 + 1) * 8 > n else 7 - w % 8))
+        assert [tiles[w] for w in order] == [(p % (B * H), nq - 1 - p // (B * H))
+                                             for p in range(n)]
+        return
     for x in range(8):
         seq = tiles[x::8]
         # list position of each tile: head-major, heaviest-first rank when causal
@@ -295,6 +306,62 @@ def test_workgroup_order(B, H, S, causal):
             assert [bh * nq + qt for bh, qt in seq] == pos
     with pytest.raises(fa.FaError):
         fa.fa_fwd_workgroup_tile(B, H, S, 128, dt, causal, -1, -1, n)
+
+
+def check_snake_order(weights):
+    """weights[w]: the K/V steps of workgroup w.  Every XCD (workgroups x, x + 8,
+    ...) runs its items heaviest first, and the XCDs' summed steps differ by at
+    most twice the heaviest item."""
+    sums = []
+    for x in range(8):
+        seq = weights[x::8]
+        assert all(a >= b for a, b in zip(seq, seq[1:])), (x, seq[:20])
+        sums.append(sum(seq))
+    assert max(sums) - min(sums) <= 2 * max(weights), sums
+
+
+@pytest.mark.parametrize("B,H,S,n_splits", [(1, 2, 16384, 4), (1, 2, 16384, 6), (1, 3, 1000, 2),
+                                            (2, 16, 2048, 3), (1, 1, 129, 16), (1, 5, 4097, 5)])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_splitkv_workgroup_order(B, H, S, n_splits, causal):
+    """The split launch order is a bijection onto the (batch-head, Q tile, part)
+    triples.  With the causal mask the parts are dealt to the XCDs in snake order
+    of weight (each XCD heaviest first, summed steps balanced); without it a
+    tile's parts are consecutive workgroups and the tiles follow fa_fwd's order.
+    One part, or fp32 inputs, is fa_fwd's own order."""
+    dt = fa.FA_DTYPE_BF16
+    nq = fa.fa_fwd_tile_schedule(S, 128, dt, causal, -1, -1, 0)["n_q_tiles"]
+    n = B * H * nq * n_splits
+    visits = [fa.fa_fwd_tile_schedule(S, 128, dt, causal, -1, -1, t) for t in range(nq)]
+    visits = [x["kt_end"] - x["kt_begin"] for x in visits]
+    trip = [fa.fa_fwd_splitkv_workgroup_tile(B, H, S, 128, dt, causal, -1, -1, n_splits, w)
+            for w in range(n)]
+    assert sorted(trip) == [(bh, qt, p) for bh in range(B * H) for qt in range(nq)
+                            for p in range(n_splits)]
+
+    def part_steps(qt, p):  # the kernel's near-equal cut of a tile's K/V range
+        L = visits[qt]
+        return L * (p + 1) // n_splits - L * p // n_splits
+
+    if causal:
+        # heaviest tile first; a tile's parts differ by at most one step
+        check_snake_order([visits[qt] for _, qt, _ in trip])
+        sums = [sum(part_steps(qt, p) for _, qt, p in trip[x::8]) for x in range(8)]
+        assert max(sums) - min(sums) <= 2 * max(visits), sums
+    else:
+        for w, (bh, qt, p) in enumerate(trip):
+            assert p == w % n_splits
+            assert (bh, qt) == fa.fa_fwd_workgroup_tile(B, H, S, 128, dt, causal, -1, -1,
+                                                         w // n_splits)
+    for dtype, ns in ((dt, 1), (fa.FA_DTYPE_FP32, n_splits)):
+        nq1 = fa.fa_fwd_tile_schedule(S, 128, dtype, causal, -1, -1, 0)["n_q_tiles"]
+        for w in range(0, B * H * nq1, 7):
+            assert fa.fa_fwd_splitkv_workgroup_tile(B, H, S, 128, dtype, causal, -1, -1, ns, w) == \
+                (*fa.fa_fwd_workgroup_tile(B, H, S, 128, dtype, causal, -1, -1, w), 0)
+    with pytest.raises(fa.FaError):
+        fa.fa_fwd_splitkv_workgroup_tile(B, H, S, 128, dt, causal, -1, -1, n_splits, n)
+    with pytest.raises(fa.FaError):
+        fa.fa_fwd_splitkv_workgroup_tile(B, H, S, 128, dt, causal, -1, -1, 17, 0)
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
