@@ -138,10 +138,12 @@ int fa_fwd_tile_schedule(int64_t S, int64_t D, int dtype, int causal, int64_t wi
  * tiles (its heads' K/V stay in its L2); with causal = 1 each XCD visits its
  * block's Q tiles heaviest first across heads (more K/V tiles to walk =
  * earlier), so that light tiles end the launch (thread-block load balance,
- * the note closing [FA] section 1).  With causal = 1 and fewer than 8
- * (batch, head) pairs, whole heads cannot go to XCDs: the tiles of all heads
- * are then ordered heaviest first and dealt to the XCDs in snake order
- * (0..7, 7..0, ...), which gives every XCD the same share of the work.
+ * the note closing [FA] section 1).  With causal = 1 and either fewer than 8
+ * (batch, head) pairs (whole heads cannot go to XCDs) or K and V of all heads
+ * within 128 MiB (half the MALL, so every XCD can work on every head), the
+ * tiles of all heads are instead ordered heaviest first and dealt to the XCDs
+ * in snake order (0..7, 7..0, ...): every XCD gets the same share of the work
+ * and runs it heaviest first.
  * Returns FA_OK, or FA_ERR_* for bad arguments or wg outside the grid.
  */
 int fa_fwd_workgroup_tile(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int causal,

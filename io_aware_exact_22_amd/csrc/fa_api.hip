@@ -233,7 +233,9 @@ FA_API int fa_fwd_workgroup_tile(int64_t B, int64_t H, int64_t S, int64_t D, int
     const int64_t nq = (S + BM - 1) / BM;
     if (wg < 0 || wg >= B * H * nq) return FA_ERR_SHAPE;
     uint32_t r_bh, r_qt;
-    fa::workgroup_tile((uint32_t)wg, (uint32_t)(B * H), (uint32_t)nq, causal != 0, &r_bh, &r_qt);
+    const int64_t esz = dtype == FA_DTYPE_FP32 ? 4 : 2;
+    fa::workgroup_tile((uint32_t)wg, (uint32_t)(B * H), (uint32_t)nq, causal != 0,
+                       fa::snake_launch(B * H, S, D, esz), &r_bh, &r_qt);
     *bh = r_bh;
     *q_tile = r_qt;
     return FA_OK;

@@ -95,7 +95,8 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_kernel(
     const int hh = lane >> 5, ql = lane & 31;
 
     uint32_t bh, qt32;
-    workgroup_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt, causal != 0, &bh, &qt32);
+    workgroup_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt, causal != 0,
+                   (uint32_t)B * (uint32_t)H < kXcds, &bh, &qt32);
     const int qt = (int)qt32;
     const int bb = (int)(bh / (uint32_t)H), h = (int)(bh % (uint32_t)H);
     const MaskSpec ms{S, causal, wl, wr};
@@ -309,7 +310,8 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 1) void fa_bwd_dkdv_kernel(
     // key blocks: with the causal mask block 0 sees every row, so the lowest
     // blocks (the heaviest) run first
     uint32_t bh, t32;
-    workgroup_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_kt, causal != 0, &bh, &t32);
+    workgroup_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_kt, causal != 0,
+                   (uint32_t)B * (uint32_t)H < kXcds, &bh, &t32);
     const int kblk = causal ? n_kt - 1 - (int)t32 : (int)t32;
     const int bb = (int)(bh / (uint32_t)H), h = (int)(bh % (uint32_t)H);
     const int64_t row_stride = (int64_t)H * D;

@@ -104,8 +104,8 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
         workgroup_tile_part(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt,
                             (uint32_t)n_splits, causal != 0, &bh, &qt32, &sp32);
     else
-        workgroup_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt, causal != 0, &bh,
-                       &qt32);
+        workgroup_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt, causal != 0,
+                       snake_launch((int64_t)B * H, S, D, sizeof(T)), &bh, &qt32);
     const int sp = (int)sp32;
     const int qt = (int)qt32;
     const int bb = (int)(bh / (uint32_t)H), h = (int)(bh % (uint32_t)H);
@@ -827,7 +827,8 @@ __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int hh = lane >> 5, ql = lane & 31;
     uint32_t bh, qt32;
-    workgroup_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt, causal != 0, &bh, &qt32);
+    workgroup_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt, causal != 0,
+                   snake_launch((int64_t)B * H, S, D, sizeof(float)), &bh, &qt32);
     const int qt = (int)qt32;
     const int bb = (int)(bh / (uint32_t)H), h = (int)(bh % (uint32_t)H);
     const MaskSpec ms{S, causal, wl, wr};

@@ -120,12 +120,21 @@ __host__ __device__ inline void q_tile_interior_range(const MaskSpec& m, int64_t
 #define FA_LIGHT_DIV 4  // the lightest 1/FA_LIGHT_DIV of each head's Q tiles close the launch
 #endif
 //
-// Fewer (batch, head) pairs than XCDs (by_weight): whole heads cannot go to
-// XCDs, and contiguous blocks of one head's heaviest-first list would give one
-// XCD its heaviest Q tiles and another its lightest.  The tiles are then dealt
-// in snake order instead (snake_item below): every XCD gets one tile of each
-// group of eight consecutive weights, heaviest first.
+// snake (by_weight only): the tiles of all heads are sorted heaviest first and
+// dealt in snake order instead (snake_item below): every XCD gets one tile of
+// each group of eight consecutive weights and runs them heaviest first.  With
+// fewer (batch, head) pairs than XCDs this is the only balanced choice (whole
+// heads cannot go to XCDs, and contiguous blocks of one head's list would give
+// one XCD its heaviest Q tiles and another its lightest); it is also the
+// closer fit to longest-first scheduling whenever every head's K/V can stay in
+// the MALL while all XCDs work on all heads (snake_launch).
 constexpr uint32_t kXcds = 8;
+// K/V bytes of all heads up to which a causal launch is dealt in snake order:
+// half of the MI355X's 256 MB MALL
+constexpr int64_t kSnakeKvBytes = int64_t(128) << 20;
+__host__ __device__ inline bool snake_launch(int64_t n_bh, int64_t S, int64_t D, int64_t esz) {
+    return n_bh < (int64_t)kXcds || 2 * n_bh * S * D * esz <= kSnakeKvBytes;
+}
 
 // Item of a weight-sorted list (position 0 = heaviest) that workgroup w runs:
 // workgroup w is XCD w % 8's (w / 8)-th workgroup, and the 8 items of group k
@@ -139,9 +148,10 @@ __host__ __device__ inline uint32_t snake_item(uint32_t w, uint32_t n) {
 }
 
 __host__ __device__ inline void workgroup_tile(uint32_t w, uint32_t n_bh, uint32_t n_qt,
-                                               bool by_weight, uint32_t* bh, uint32_t* qt) {
+                                               bool by_weight, bool snake, uint32_t* bh,
+                                               uint32_t* qt) {
     const uint32_t n = n_bh * n_qt;
-    if (by_weight && n_bh < kXcds) {  // list: rank-major, heads next to each other
+    if (by_weight && snake) {  // list: rank-major, heads next to each other
         const uint32_t p = snake_item(w, n);
         *bh = p % n_bh;
         *qt = n_qt - 1 - p / n_bh;
@@ -222,7 +232,7 @@ __host__ __device__ inline void workgroup_tile_part(uint32_t w, uint32_t n_bh, u
                                                     uint32_t* bh, uint32_t* qt, uint32_t* part) {
     if (!by_weight) {
         *part = w % n_parts;
-        workgroup_tile(w / n_parts, n_bh, n_qt, false, bh, qt);
+        workgroup_tile(w / n_parts, n_bh, n_qt, false, false, bh, qt);
         return;
     }
     const uint32_t p = snake_item(w, n_bh * n_qt * n_parts);

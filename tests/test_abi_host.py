@@ -262,8 +262,15 @@ def test_tile_schedule_counts_causal_16k():
     assert tot == 16512 and masked == 256
 
 
+def snake_launch(n_bh, S, D, esz):
+    """Causal launches dealt in snake order: fewer (batch, head) pairs than XCDs,
+    or the K/V of all heads within half of the 256 MB MALL."""
+    return n_bh < 8 or 2 * n_bh * S * D * esz <= 128 << 20
+
+
 @pytest.mark.parametrize("B,H,S", [(1, 16, 16384), (2, 16, 2048), (1, 3, 1000), (1, 5, 16384),
-                                   (3, 7, 300), (1, 1, 128), (2, 1, 129), (1, 12, 4096)])
+                                   (3, 7, 300), (1, 1, 128), (2, 1, 129), (1, 12, 4096),
+                                   (2, 16, 16384), (1, 24, 12288), (3, 5, 30000)])
 @pytest.mark.parametrize("causal", [0, 1])
 def test_workgroup_order(B, H, S, causal):
     """The launch order is a bijection onto the (batch-head, Q tile) pairs; XCD
@@ -272,8 +279,9 @@ def test_workgroup_order(B, H, S, causal):
     each head's Q tiles head by head, heaviest first, and then the lightest
     quarter of all its heads in non-increasing visited K/V tile count, after
     every heavier tile.  With the causal mask and fewer than 8 (batch, head)
-    pairs the tiles are instead dealt to the XCDs in snake order of weight:
-    each XCD runs heaviest first and the XCDs' summed K/V steps are balanced."""
+    pairs, or K/V of all heads within half the MALL, the tiles are instead
+    dealt to the XCDs in snake order of weight: each XCD runs heaviest first
+    and the XCDs' summed K/V steps are balanced."""
     dt = fa.FA_DTYPE_BF16
     nq = fa.fa_fwd_tile_schedule(S, 128, dt, causal, -1, -1, 0)["n_q_tiles"]
     n = B * H * nq
@@ -281,7 +289,7 @@ def test_workgroup_order(B, H, S, causal):
     visits = [x["kt_end"] - x["kt_begin"] for x in visits]
     tiles = [fa.fa_fwd_workgroup_tile(B, H, S, 128, dt, causal, -1, -1, w) for w in range(n)]
     assert sorted(tiles) == [(bh, qt) for bh in range(B * H) for qt in range(nq)]
-    if causal and B * H < 8:
+    if causal and snake_launch(B * H, S, 128, 2):
         check_snake_order([visits[qt] for _, qt in tiles])
         # the list is rank-major: heads next to each other, heaviest rank first
         order = sorted(range(n), key=lambda w: (w // 8, w % 8 if (w // 8) % 2 == 0 or
