@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_kernel(
 
     uint32_t bh, qt32;
     workgroup_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt, causal != 0,
-                   (uint32_t)B * (uint32_t)H < kXcds, &bh, &qt32);
+                   snake_launch((int64_t)B * H, S, D, sizeof(T)), &bh, &qt32);
     const int qt = (int)qt32;
     const int bb = (int)(bh / (uint32_t)H), h = (int)(bh % (uint32_t)H);
     const MaskSpec ms{S, causal, wl, wr};
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 1) void fa_bwd_dkdv_kernel(
     // blocks (the heaviest) run first
     uint32_t bh, t32;
     workgroup_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_kt, causal != 0,
-                   (uint32_t)B * (uint32_t)H < kXcds, &bh, &t32);
+                   snake_launch((int64_t)B * H, S, D, sizeof(T)), &bh, &t32);
     const int kblk = causal ? n_kt - 1 - (int)t32 : (int)t32;
     const int bb = (int)(bh / (uint32_t)H), h = (int)(bh % (uint32_t)H);
     const int64_t row_stride = (int64_t)H * D;
