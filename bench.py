@@ -54,6 +54,19 @@ def allowed_pairs(S: int, causal: bool, window) -> int:
     return int(np.maximum(0, hi - lo + 1).sum())
 
 
+def rows_pairs(S: int, causal: bool, window, r0: int, r1: int) -> int:
+    """Allowed (query, key) pairs of query rows [r0, r1)."""
+    import numpy as np
+
+    wl, wr = window
+    i = np.arange(r0, r1, dtype=np.int64)
+    lo = np.zeros_like(i) if wl < 0 else np.maximum(0, i - wl)
+    hi = np.full_like(i, S - 1) if wr < 0 else np.minimum(S - 1, i + wr)
+    if causal:
+        hi = np.minimum(hi, i)
+    return int(np.maximum(0, hi - lo + 1).sum())
+
+
 def blocksparse_pairs(S: int, causal: bool, window, mask, bm: int, bn: int, r0: int = 0,
                       r1: int | None = None) -> int:
     """Allowed (query, key) pairs of rows [r0, r1) under one head's block mask
@@ -120,6 +133,13 @@ def cpu_baseline(w, q, k, v, target_s: float = 15.0):
     else:
         dt, used = dt1, 1
     fl = per_head_flops * used
+    # per-core figure: one thread on the last rows of head (0, 0), about 1-2 s
+    r1 = w.S
+    r0 = max(0, r1 - max(1, int(2e9 / (4.0 * w.D * w.S))))
+    t0 = time.perf_counter()
+    oracle.fwd_rows(q, k, v, w.scale, w.causal, w.window, 0, 0, r0, r1, nthreads=1)
+    dt_1 = time.perf_counter() - t0
+    fl_1 = 4.0 * rows_pairs(w.S, w.causal, w.window, r0, r1) * w.D
     return {
         "value": fl / dt / 1e12,
         "unit": "TFLOPS",
@@ -128,6 +148,9 @@ def cpu_baseline(w, q, k, v, target_s: float = 15.0):
         "sample": (f"{w.name}: {used} of {len(heads)} (batch, head) pairs in full, fp64 oracle "
                    f"materialising each head's score matrix; {fl / 1e9:.1f} GFLOP (metric count) "
                    f"in {dt:.1f} s on {threads} threads"),
+        "per_core": {"value": fl_1 / dt_1 / 1e12, "unit": "TFLOPS", "threads": 1,
+                     "sample": f"rows [{r0}, {r1}) of (batch 0, head 0), {fl_1 / 1e9:.2f} GFLOP "
+                               f"in {dt_1:.2f} s on one thread"},
     }
 
 
