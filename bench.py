@@ -110,6 +110,70 @@ def measured_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
+def sclk_file(dev_index: int = 0):
+    """The sysfs DPM table of the GPU torch calls cuda:dev_index (its current
+    shader clock level is the line marked '*'); None if it cannot be told."""
+    import glob
+
+    files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    if len(files) == 1:
+        return files[0]
+    try:
+        import torch
+
+        p = torch.cuda.get_device_properties(dev_index)
+        bus = "%02x:%02x" % (p.pci_bus_id, p.pci_device_id)
+        for f in files:
+            if bus in os.path.realpath(os.path.dirname(f)):
+                return f
+    except Exception:
+        pass
+    return None
+
+
+def sample_sclk(step, stream, launch_ms: float, seconds: float = 0.6):
+    """The shader clock while the timed launch runs back to back: about
+    `seconds` of launches are queued after the timed steps and the current DPM
+    clock is read from sysfs every 20 ms until they have run (the first 0.2 s,
+    where the clock may still be ramping, are left out).  None if the clock
+    cannot be read."""
+    import numpy as np
+    import torch
+
+    f = sclk_file()
+    if f is None:
+        return None
+
+    def read():
+        try:
+            for ln in open(f):
+                if "*" in ln:
+                    return float(ln.split(":")[1].strip().rstrip("*").strip().lower()
+                                 .replace("mhz", ""))
+        except Exception:
+            return None
+        return None
+
+    n = max(8, int(seconds * 1e3 / max(launch_ms, 1e-3)))
+    done = torch.cuda.Event()
+    for _ in range(n):
+        step()
+    done.record(stream)
+    t0, mhz = time.perf_counter(), []
+    while not done.query():
+        x = read()
+        if x is not None and time.perf_counter() - t0 > 0.2:
+            mhz.append(x)
+        time.sleep(0.02)
+    torch.cuda.synchronize()
+    if not mhz:
+        return None
+    return {"median_mhz": float(np.median(mhz)), "min_mhz": float(np.min(mhz)),
+            "max_mhz": float(np.max(mhz)), "samples": len(mhz),
+            "source": f"{f} (current DPM level), read every 20 ms while {n} launches queued "
+                      f"after the timed steps ran"}
+
+
 def cpu_baseline(w, q, k, v, target_s: float = 15.0):
     """Time the CPU oracle (as it stands) on whole heads of the workload: one
     head first, then as many heads (b, h) in order as fit about target_s
@@ -239,6 +303,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the shader-clock sample after the timed steps")
     ap.add_argument("--backward", action="store_true",
                     help="time fa_bwd (the gradients of the forward) instead of fa_fwd; "
                          "bf16 / fp16 workloads")
@@ -415,6 +481,7 @@ def main() -> int:
             torch.cuda.synchronize(dev)
             cold_ms.append(e0.elapsed_time(e1))
         del flush
+    sclk = None if args.no_clock else sample_sclk(step, stream, float(np.median(launch_ms)))
 
     if bs is not None:
         pairs = blocksparse_pairs(w.S, w.causal, w.window, bs[0][0], 128, 64)
@@ -451,6 +518,12 @@ def main() -> int:
     roof["cold_cache_kernel_ms"] = float(np.median(cold_ms)) if cold_ms else None
     roof["algorithmic_flops_per_launch"] = flops
     roof["algorithmic_bytes_per_launch"] = alg_bytes
+    # the same rate against the MFMA peak at the shader clock the chip ran at
+    # (the published peak assumes 2.4 GHz)
+    roof["sclk"] = sclk
+    roof["frac_at_observed_sclk"] = (
+        kern_tflops / (peak * sclk["median_mhz"] / 2400.0)
+        if (sclk and not hbm_bound and sclk["median_mhz"] > 0) else None)
 
     # correctness of what was timed: sampled rows against the oracle are the
     # GPU tests' job; here only a finiteness check of the timed output
