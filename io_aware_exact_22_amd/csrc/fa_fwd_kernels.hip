@@ -219,6 +219,10 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     // the host), so kt * tile_bytes is one 32 x 32 -> 64-bit product.
     const uint32_t tile_bytes = (uint32_t)(BN * row_stride * (int64_t)sizeof(T));
     const uint64_t head_bytes = (uint64_t)(((int64_t)S - 1) * row_stride + D) * sizeof(T);
+    // K/V tiles of the head and the bytes of its last one (<= tile_bytes)
+    const int n_kt_head = (S + BN - 1) / BN;
+    const uint32_t last_bytes =
+        (uint32_t)(head_bytes - (uint64_t)(uint32_t)(n_kt_head - 1) * tile_bytes);
     // PAGED: k and v are pools [pg_count, pg_rows, H, D]; key j of batch bb is
     // row j % pg_rows of page pg_table[bb * pg_stride + j / pg_rows].  pg_rows is
     // a multiple of BN, so a tile lies in one page.
@@ -244,11 +248,12 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
                                                      (int)nrec, kBufferFlags);
         }
         const uint64_t off = (uint64_t)(uint32_t)kt * tile_bytes;
-        // records run to the end of the head's last row; a tile that starts at
-        // or past S gets none, so the hardware range check turns every read of
-        // it into a zero instead of an access past the tensor
-        const uint64_t rem = off < head_bytes ? head_bytes - off : 0;
-        const uint32_t nrec = (rem >> 32) ? 0xFFFFFFFFu : (uint32_t)rem;
+        // records cover the tile up to the end of the head's last row: every
+        // tile below the last one lies inside the head (its rows are < S - 1),
+        // the last one ends at the head's end, and a tile that starts at or
+        // past S gets none, so the hardware range check turns every read past
+        // the tensor into a zero.  32-bit scalar compares only.
+        const uint32_t nrec = kt < n_kt_head - 1 ? tile_bytes : kt == n_kt_head - 1 ? last_bytes : 0u;
         return __builtin_amdgcn_make_buffer_rsrc((void*)(head + off), (short)0, (int)nrec,
                                                  kBufferFlags);
     };
@@ -303,8 +308,8 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     // and its weight exp2(-inf) is exactly 0.
     float m_run = kNegInf;  // running reference max
     float m_use = 0.f;      // reference the current tile's weights use
-    float alpha = 1.f;      // factor O and l take before the current tile
-    bool moved = false;     // the reference moved for the current tile
+    float m_prev = kNegInf; // running max before the current tile
+    bool moved = false;     // some row's reference moved for the current tile (wave-uniform)
     float l_run = 0.f;      // running sum over this half's keys
     f32x16 o[DB];
 #pragma unroll
@@ -345,8 +350,8 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
         const float mt = halves_max(mx) * c;
         const float m_new = (valid && mt > m_run + kRescaleSlack) ? mt : m_run;
         m_use = (m_new == kNegInf) ? 0.f : m_new;  // row fully masked so far
-        alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        moved = m_new != m_run;
+        moved = __any(m_new != m_run);
+        m_prev = m_run;
         m_run = m_new;
     };
     // weights of a tile, rounded and packed as the B operand of O^T += V^T P^T;
@@ -358,7 +363,10 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
         constexpr int kExpLag = 4, kPackLag = 8;
         constexpr int NE = 16 * KB;  // weights per lane
         float e[NE];
-        float ls[4] = {0.f, 0.f, 0.f, 0.f};
+        // partial row sums: the first one starts from the running sum, the
+        // others from their first weight (no zero-initialised accumulators,
+        // no additions of 0)
+        float ls[4];
 #pragma unroll
         for (int st = 0; st < NE + kPackLag; ++st) {
             if (st < NE) e[st] = __builtin_fmaf(s[st >> 4][st & 15], c, -m_use);
@@ -366,16 +374,28 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
             if (ie >= 0 && ie < NE) e[ie] = __builtin_amdgcn_exp2f(e[ie]);
             const int ip = st - kPackLag;
             if (ip >= 1 && ip < NE && (ip & 1)) {
+                const int q = ip >> 1;  // weight pair
                 p[ip >> 3][(ip & 7) >> 1] = Mfma<T>::pack2(e[ip - 1], e[ip]);
-                if (Mfma<T>::kSumRounded) {
-                    ls[(ip >> 1) & 3] = Mfma<T>::sum2(p[ip >> 3][(ip & 7) >> 1], ls[(ip >> 1) & 3]);
-                } else {
-                    ls[(ip >> 1) & 3] += e[ip - 1];
-                    ls[((ip >> 1) + 2) & 3] += e[ip];
+                if (Mfma<T>::kSumRounded) {  // two partial sums of packed pairs
+                    const unsigned pk = p[ip >> 3][(ip & 7) >> 1];
+                    if (q == 0) ls[0] = Mfma<T>::sum2(pk, l_run);
+                    else if (q == 1) ls[1] = Mfma<T>::sum2(pk, 0.f);
+                    else ls[q & 1] = Mfma<T>::sum2(pk, ls[q & 1]);
+                } else {  // four partial sums of single weights
+                    if (q == 0) {
+                        ls[0] = l_run + e[ip - 1];
+                        ls[2] = e[ip];
+                    } else if (q == 1) {
+                        ls[1] = e[ip - 1];
+                        ls[3] = e[ip];
+                    } else {
+                        ls[q & 3] += e[ip - 1];
+                        ls[(q + 2) & 3] += e[ip];
+                    }
                 }
             }
         }
-        l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        l_run = Mfma<T>::kSumRounded ? ls[0] + ls[1] : (ls[0] + ls[1]) + (ls[2] + ls[3]);
     };
     // O^T += V^T P^T with V^T from transposing LDS reads of the row-major tile
     auto pv = [&](const u32x4(&p)[NCH], const unsigned char* vst) __attribute__((always_inline)) {
@@ -394,7 +414,10 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
             }
     };
     auto rescale_if_moved = [&]() __attribute__((always_inline)) {
-        if (__any(moved)) {  // wave-uniform: only when some row's reference moved
+        if (moved) {  // only when some row's reference moved
+            // factor O and l take: old reference over new (0 for a row whose
+            // first allowed keys are in this tile: O and l are still 0)
+            const float alpha = __builtin_amdgcn_exp2f(m_prev - m_use);
             l_run *= alpha;
 #pragma unroll
             for (int d = 0; d < DB; ++d) o[d] *= alpha;
