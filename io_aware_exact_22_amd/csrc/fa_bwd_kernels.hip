@@ -159,11 +159,15 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_kernel(
     }
     const uint32_t tile_bytes = (uint32_t)(BN * row_stride * (int64_t)sizeof(T));
     const uint64_t head_bytes = (uint64_t)(((int64_t)S - 1) * row_stride + D) * sizeof(T);
+    // records cover the tile up to the head's end (32-bit scalar compares):
+    // tiles below the last lie inside the head, the last ends at its end, and
+    // a tile at or past S gets none (its reads return zeros)
+    const int n_t = (S + BN - 1) / BN;
+    const uint32_t last_bytes = (uint32_t)(head_bytes - (uint64_t)(uint32_t)(n_t - 1) * tile_bytes);
     auto tile_rsrc = [&](const T* base, int kt) __attribute__((always_inline)) {
         const unsigned char* head = (const unsigned char*)(base + head_base);
         const uint64_t off = (uint64_t)(uint32_t)kt * tile_bytes;
-        const uint64_t rem = off < head_bytes ? head_bytes - off : 0;
-        const uint32_t nrec = (rem >> 32) ? 0xFFFFFFFFu : (uint32_t)rem;
+        const uint32_t nrec = kt < n_t - 1 ? tile_bytes : kt == n_t - 1 ? last_bytes : 0u;
         return __builtin_amdgcn_make_buffer_rsrc((void*)(head + off), (short)0, (int)nrec,
                                                  kBufferFlags);
     };
@@ -366,11 +370,13 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 1) void fa_bwd_dkdv_kernel(
     }
     const uint32_t tile_bytes = (uint32_t)(BQ * row_stride * (int64_t)sizeof(T));
     const uint64_t head_bytes = (uint64_t)(((int64_t)S - 1) * row_stride + D) * sizeof(T);
+    // records cover the tile up to the head's end, as in the dQ kernel
+    const int n_t = (S + BQ - 1) / BQ;
+    const uint32_t last_bytes = (uint32_t)(head_bytes - (uint64_t)(uint32_t)(n_t - 1) * tile_bytes);
     auto load = [&](const T* base, int t, unsigned char* buf) __attribute__((always_inline)) {
         const unsigned char* head = (const unsigned char*)(base + head_base);
         const uint64_t off = (uint64_t)(uint32_t)t * tile_bytes;
-        const uint64_t rem = off < head_bytes ? head_bytes - off : 0;
-        const uint32_t nrec = (rem >> 32) ? 0xFFFFFFFFu : (uint32_t)rem;
+        const uint32_t nrec = t < n_t - 1 ? tile_bytes : t == n_t - 1 ? last_bytes : 0u;
         dma_matrix<L::DMA_PER_WAVE>(
             __builtin_amdgcn_make_buffer_rsrc((void*)(head + off), (short)0, (int)nrec, kBufferFlags),
             buf + wave * L::DMA_PER_WAVE * 1024, dma_voff);
