@@ -498,6 +498,16 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     }
     kw0 = __builtin_amdgcn_readfirstlane(kw0);
     kw1 = __builtin_amdgcn_readfirstlane(kw1);
+    // the tiles this wave runs without the mask: every key allowed for each of
+    // its own 32 rows (a superset of the workgroup's [ki0, ki1): near a window
+    // edge or the causal diagonal a wave needs the mask on fewer tiles than the
+    // workgroup as a whole).  SPARSE positions keep the workgroup's range.
+    if (!SPARSE && qw0 < S) {
+        int64_t b0, b1;
+        q_tile_interior_range(ms, qw0, kWaveRows, BN, kt0, kt1, &b0, &b1);
+        ki0 = __builtin_amdgcn_readfirstlane((int)b0);
+        ki1 = __builtin_amdgcn_readfirstlane((int)b1);
+    }
     // tiles (and pages) of positions j + 1 and j + 2 at the step of position
     // j; advances the look-ahead by one position (every wave runs it once per
     // position, in its compute steps and its idle steps alike)
