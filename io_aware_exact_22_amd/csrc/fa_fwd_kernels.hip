@@ -42,7 +42,10 @@
 //    no mask code at all; the few boundary tiles apply the mask.
 //  * Workgroup ids are remapped so each XCD holds whole (batch, head) groups
 //    (L2 reuse of K/V); for causal masks each XCD runs the heaviest Q tiles of
-//    all its heads first, so the light tiles fill the end of the launch.
+//    all its heads first, so the light tiles fill the end of the launch.  When
+//    every head's K/V fits in half the MALL, or there are fewer heads than
+//    XCDs, and for causal split launches, the tiles (parts) of all heads are
+//    instead dealt to the XCDs in snake order of weight (fa_schedule.h).
 //  * Probabilities are rounded to the input dtype (RNE, v_cvt_pk_*) for the
 //    P V MFMA.  The row sum adds the fp32 weights for bf16 and the fp16-rounded
 //    weights two at a time (v_dot2c with ones) for fp16.  Max, exp and the
