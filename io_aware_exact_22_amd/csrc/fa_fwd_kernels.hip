@@ -86,7 +86,11 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     constexpr int RB = L::RB;
     constexpr int KSTEPS = D / 16;  // 16-wide d chunks of the score MFMA
     constexpr int DB = D / 32;      // 32-wide d blocks of the output
-    constexpr int kLeadK = FA_LEAD_K, kLeadV = FA_LEAD_V;
+    // LDS operand reads run this many MFMAs ahead of their score / P V MFMA;
+    // at D = 128 longer leads hide more LDS latency (measured), at D = 64 the
+    // extra registers cost more than they hide
+    constexpr int kLeadK = D == 128 ? FA_LEAD_K_D128 : FA_LEAD_K;
+    constexpr int kLeadV = D == 128 ? FA_LEAD_V_D128 : FA_LEAD_V;
     // one object per K / V stage: the compiler then sees that the direct-to-LDS
     // load of one stage never aliases the operand reads of the other, and does
     // not wait for the load before them

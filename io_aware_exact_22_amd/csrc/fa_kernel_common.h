@@ -36,6 +36,12 @@ constexpr float kRescaleSlack = 8.f;
 #ifndef FA_LEAD_K
 #define FA_LEAD_K 3
 #endif
+#ifndef FA_LEAD_K_D128
+#define FA_LEAD_K_D128 5
+#endif
+#ifndef FA_LEAD_V_D128
+#define FA_LEAD_V_D128 6
+#endif
 #ifndef FA_LEAD_V
 #define FA_LEAD_V 4
 #endif
