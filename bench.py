@@ -5,12 +5,16 @@ tile schedule, Q/K/V loads, QK^T, mask, online softmax, P V and the epilogue
 all run inside that single kernel launch.  Inputs are synthetic (seeded N(0,1),
 rounded to the workload dtype) and resident in HBM before timing starts.
 
+Timing: every launch is preceded, outside the HIP events that bracket it on
+its stream, by a 512 MiB write that evicts L2 and the 256 MB MALL, so each
+timed launch starts with cold caches (inputs resident in HBM).
+
 Prints ONE JSON line:
-  value         TFLOPS = 4 * B * H * S * S_eff * D / t, t = wall time per step
-                (S_eff = allowed (query, key) pairs / S, counted exactly)
-  roofline      the kernel's per-launch rate from HIP events on its stream
-                against the MI355X dense bf16/fp16 MFMA peak (or HBM for a
-                bandwidth-bound window workload)
+  value         TFLOPS = 4 * B * H * S * S_eff * D / t, t = the median cold
+                launch (S_eff = allowed (query, key) pairs / S, counted exactly)
+  roofline      the kernel's rate over the mean cold launch against the MI355X
+                dense bf16/fp16 MFMA peak (or HBM for a bandwidth-bound
+                workload); warm back-to-back launches are reported beside it
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same
                 workload on this host's cores (rate on the same FLOP count)
 """
@@ -174,13 +178,22 @@ def sample_sclk(step, stream, launch_ms: float, seconds: float = 0.6):
                       f"after the timed steps ran"}
 
 
+def cpu_threads() -> int:
+    """Threads for the CPU oracle: the host cores this process may use --
+    OMP_NUM_THREADS when the host sets it (the CPU share a shared GPU host
+    gives one process), else every core in the affinity mask."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(n, int(env))) if env.isdigit() and int(env) > 0 else n
+
+
 def cpu_baseline(w, q, k, v, target_s: float = 15.0):
     """Time the CPU oracle (as it stands) on whole heads of the workload: one
     head first, then as many heads (b, h) in order as fit about target_s
     seconds; report the rate on the metric's FLOP count."""
     import oracle
 
-    threads = min(16, len(os.sched_getaffinity(0)))
+    threads = cpu_threads()
     per_head_flops = 4.0 * allowed_pairs(w.S, w.causal, w.window) * w.D
     heads = [(b, h) for b in range(w.B) for h in range(w.H)]
 
@@ -208,6 +221,7 @@ def cpu_baseline(w, q, k, v, target_s: float = 15.0):
         "value": fl / dt / 1e12,
         "unit": "TFLOPS",
         "cores": threads,
+        "affinity_cores": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": (f"{w.name}: {used} of {len(heads)} (batch, head) pairs in full, fp64 oracle "
                    f"materialising each head's score matrix; {fl / 1e9:.1f} GFLOP (metric count) "
@@ -228,7 +242,7 @@ def cpu_baseline_bwd(w, q, k, v, dout, target_s: float = 15.0):
 
     import oracle
 
-    threads = min(16, len(os.sched_getaffinity(0)))
+    threads = cpu_threads()
     wl, wr = w.window
     CH = 256
     chunks = [(h, r) for h in range(w.H) for r in range(0, w.S, CH)]
@@ -254,6 +268,7 @@ def cpu_baseline_bwd(w, q, k, v, dout, target_s: float = 15.0):
         "value": fl / dt / 1e12,
         "unit": "TFLOPS",
         "cores": threads,
+        "affinity_cores": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": (f"{w.name} backward: dq of {rows} rows of batch 0 in chunks of {CH} from row "
                    f"{first * CH} of head 0 on (fp64 oracle, P and dS formed again per row); "
@@ -269,7 +284,7 @@ def cpu_baseline_blocksparse(w, q, k, v, mask, bm, bn, target_s: float = 15.0):
     for the rows done."""
     import oracle
 
-    threads = min(16, len(os.sched_getaffinity(0)))
+    threads = cpu_threads()
     CH = 512
     chunks = [(h, r) for h in range(w.H) for r in range(0, w.S, CH)]
     first = (w.S // 2) // CH
@@ -289,6 +304,7 @@ def cpu_baseline_blocksparse(w, q, k, v, mask, bm, bn, target_s: float = 15.0):
         "value": fl / dt / 1e12,
         "unit": "TFLOPS",
         "cores": threads,
+        "affinity_cores": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": (f"{w.name} under the block mask: {rows} rows of batch 0 in chunks of {CH} from "
                    f"row {first * CH} of head 0 on, fp64 oracle materialising those rows' scores; "
@@ -300,7 +316,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-clock", action="store_true",
@@ -320,10 +336,12 @@ def main() -> int:
                     help="time fa_fwd_paged with K/V cut into pages of this many rows (a multiple "
                          "of 64), placed at a seeded random permutation of a pool with spare "
                          "pages; combines with --splitkv")
-    ap.add_argument("--cold-steps", type=int, default=10,
-                    help="after the timed steps, this many more launches each preceded (outside "
-                         "the events) by a 512 MiB write that evicts L2 and the MALL; their "
-                         "kernel time is reported as roofline.cold_cache_kernel_ms (0 = skip)")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="MiB written before every launch, outside the events, to evict L2 and "
+                         "the MALL (0 = no flush: warm back-to-back launches are timed)")
+    ap.add_argument("--warm-steps", type=int, default=50,
+                    help="after the timed region, this many warm back-to-back launches, reported "
+                         "as roofline.warm (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the benchmark, run --steps plain device copies of this many "
                          "MiB (the reference kernel for scaling HBM byte counters)")
@@ -453,34 +471,52 @@ def main() -> int:
             fa.flash_attn_fwd(qd, kd, vd, softmax_scale=w.scale, causal=w.causal,
                               window_size=w.window, out=out, lse=lse, stream=stream)
 
-    for _ in range(args.warmup):
+    # Timing protocol: before every launch (warm-up and timed alike) a 512 MiB
+    # write evicts L2 and the 256 MB MALL, outside the HIP events; the events
+    # on the launch's stream bracket the launch alone.  value and the
+    # roofline use these cold launches (median and mean); inputs stay
+    # resident in HBM throughout.
+    flush = torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev) \
+        if args.flush_mib > 0 else None
+
+    def timed_launch(events=None):
+        if flush is not None:
+            flush.fill_(1.0)
+        if events is not None:
+            events[0].record(stream)
         step()
+        if events is not None:
+            events[1].record(stream)
+
+    for _ in range(args.warmup):
+        timed_launch()
     torch.cuda.synchronize(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
-    for e0, e1 in ev:
-        e0.record(stream)
-        step()
-        e1.record(stream)
+    for e in ev:
+        timed_launch(e)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
     launch_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
-    # cold caches: a 512 MiB write before each launch evicts L2 and the 256 MB
-    # MALL; only the launch itself lies between the events
-    cold_ms = []
-    if args.cold_steps > 0:
-        flush = torch.empty(512 << 18, dtype=torch.float32, device=dev)
-        for _ in range(args.cold_steps):
-            flush.fill_(1.0)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    del flush
+    # warm launches back to back after the timed region (caches hold K and V),
+    # reported beside the headline
+    warm_ms, warm_wall = [], None
+    if args.warm_steps > 0:
+        wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.warm_steps)]
+        step()
+        torch.cuda.synchronize(dev)
+        tw = time.perf_counter()
+        for e0, e1 in wev:
             e0.record(stream)
             step()
             e1.record(stream)
-            torch.cuda.synchronize(dev)
-            cold_ms.append(e0.elapsed_time(e1))
-        del flush
+        torch.cuda.synchronize(dev)
+        warm_wall = (time.perf_counter() - tw) * 1e3 / args.warm_steps
+        warm_ms = [e0.elapsed_time(e1) for e0, e1 in wev]
     sclk = None if args.no_clock else sample_sclk(step, stream, float(np.median(launch_ms)))
 
     if bs is not None:
@@ -490,7 +526,7 @@ def main() -> int:
     s_eff = pairs / w.S
     # the backward's five products (S, dP, dV, dK, dQ) against the forward's two
     flops = (10.0 if args.backward else 4.0) * w.B * w.H * pairs * w.D
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = float(np.median(launch_ms))  # the median cold launch
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     avg_launch_ms = float(np.mean(launch_ms))
     kern_tflops = flops / (avg_launch_ms * 1e-3) / 1e12
@@ -515,7 +551,20 @@ def main() -> int:
     roof["kernel_ms"] = avg_launch_ms
     roof["kernel_ms_median"] = float(np.median(launch_ms))
     roof["kernel_ms_min"] = float(np.min(launch_ms))
-    roof["cold_cache_kernel_ms"] = float(np.median(cold_ms)) if cold_ms else None
+    roof["timing"] = (f"{args.steps} launches on the launch's stream, each preceded outside the "
+                      f"HIP events by a {args.flush_mib} MiB write that evicts L2 and the MALL "
+                      f"({args.warmup} warm-up launches likewise); achieved uses the mean, value "
+                      f"the median" if args.flush_mib > 0 else
+                      f"{args.steps} back-to-back launches (no cache flush)")
+    roof["warm"] = ({"kernel_ms_mean": float(np.mean(warm_ms)),
+                     "kernel_ms_median": float(np.median(warm_ms)),
+                     "kernel_ms_min": float(np.min(warm_ms)),
+                     "wall_ms_per_step": warm_wall,
+                     "tflops_at_median": flops / (float(np.median(warm_ms)) * 1e-3) / 1e12,
+                     "frac_at_median": (flops / (float(np.median(warm_ms)) * 1e-3) / 1e12) / peak,
+                     "launches": len(warm_ms),
+                     "note": "back to back after the timed region, K and V resident in L2/MALL"}
+                    if warm_ms else None)
     roof["algorithmic_flops_per_launch"] = flops
     roof["algorithmic_bytes_per_launch"] = alg_bytes
     # the same rate against the MFMA peak at the shader clock the chip ran at

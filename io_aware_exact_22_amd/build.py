@@ -39,20 +39,43 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
-    """Compile every HIP source into libfa_mi355x.so (always recompiles)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", os.path.join(ROOT, "include"),
-           "-I", CSRC, *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass warns that it does not know the packed-fp32 feature
-    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if "packed-fp32-ops" not in ln]
-    if r.returncode != 0:
-        sys.stderr.write("\n".join(msgs) + "\n")
-        raise RuntimeError(f"hipcc failed ({r.returncode}) building libfa_mi355x.so")
-    if verbose and msgs:
-        print("\n".join(msgs))
+    """Compile every HIP source into libfa_mi355x.so (always recompiles).  The
+    sources compile to objects in parallel, then one link makes the library."""
+    tag = ".tmp%d" % os.getpid()
+    tmp = LIB + tag
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    flags = [f for f in HIPCC_FLAGS if f not in ("-shared",)]
+    objs, procs = [], []
+    for s in SOURCES:
+        obj = os.path.join(CSRC, s + tag + ".o")
+        cmd = [hipcc(), *flags, *(extra_flags or []), *inc, "-c", os.path.join(CSRC, s), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        objs.append(obj)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                      text=True))
+    outs = [(p, p.communicate()[0]) for p in procs]
+    try:
+        failed = False
+        for (p, out), s in zip(outs, SOURCES):
+            # hipcc's host pass warns that it does not know the packed-fp32 feature
+            msgs = [ln for ln in out.splitlines() if "packed-fp32-ops" not in ln]
+            if p.returncode != 0:
+                sys.stderr.write(f"--- {s}\n" + "\n".join(msgs) + "\n")
+                failed = True
+            elif verbose and msgs:
+                print("\n".join(msgs))
+        if failed:
+            raise RuntimeError("hipcc failed building libfa_mi355x.so")
+        cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError(f"hipcc failed ({r.returncode}) linking libfa_mi355x.so")
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     check_launch_stubs(tmp)
     os.replace(tmp, LIB)
     return LIB

@@ -238,6 +238,10 @@ def fa_fwd_paged(q: int, k_pages: int, v_pages: int, block_table: int, out: int,
 
 
 # ------------------------------------------------------------------ tensor call
+# Every tensor whose data pointer reaches the C ABI is checked here first:
+# type, device (q's device -- a host tensor or one on another GPU would hand
+# the kernels an address they cannot reach), dtype, shape and contiguity.
+# Nothing is launched before these checks pass.
 def _dtype_code(t) -> int:
     import torch
 
@@ -246,6 +250,85 @@ def _dtype_code(t) -> int:
     if t.dtype not in codes:
         raise TypeError(f"unsupported dtype {t.dtype} (fp32, fp16, bf16)")
     return codes[t.dtype]
+
+
+def _check_q(q):
+    import torch
+
+    if not isinstance(q, torch.Tensor) or q.device.type != "cuda":
+        raise TypeError("q must be a GPU tensor")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, S, H, D]")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous [B, S, H, D]")
+
+
+def _check_like(name, t, q, shape=None, dtype=None):
+    """``t`` is a contiguous tensor on q's device, of ``dtype`` (q's by default)
+    and ``shape`` (q's by default)."""
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device != q.device:
+        raise ValueError(f"{name} is on {t.device}; it must be on q's device {q.device}")
+    want_shape = tuple(q.shape) if shape is None else tuple(shape)
+    want_dtype = q.dtype if dtype is None else dtype
+    if tuple(t.shape) != want_shape or t.dtype != want_dtype:
+        raise ValueError(f"{name} must be {want_dtype} {list(want_shape)}, got {t.dtype} "
+                         f"{list(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_qkv(q, k, v):
+    _check_q(q)
+    _check_like("k", k, q)
+    _check_like("v", v, q)
+
+
+def _outputs(q, out, lse, rows=None):
+    """out (like q) and lse (fp32 [B, H, rows]), allocated when None, checked
+    otherwise."""
+    import torch
+
+    B, S, H, _ = q.shape
+    rows = S if rows is None else rows
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, rows), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_like("out", out, q)
+    _check_like("lse", lse, q, shape=(B, H, rows), dtype=torch.float32)
+    return out, lse
+
+
+def _workspace(workspace, need: int, q, dtype, stream=None):
+    """(pointer or None, bytes, tensor) of a caller's workspace (a contiguous
+    tensor on q's device; the library checks its size), or of one allocated
+    here when None and ``need`` > 0.  An allocated workspace is marked as used
+    by ``stream``, so torch does not hand its memory out again before the
+    launch on that stream has run."""
+    import torch
+
+    if workspace is None:
+        if need <= 0:
+            return None, 0, None
+        workspace = torch.empty((need + 3) // 4, dtype=dtype, device=q.device)
+        if stream is not None:
+            workspace.record_stream(stream)
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError("workspace must be a torch tensor")
+    if workspace.device != q.device:
+        raise ValueError(f"workspace is on {workspace.device}; it must be on q's device {q.device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    nbytes = workspace.numel() * workspace.element_size()
+    return (workspace.data_ptr() or None), nbytes, workspace
+
+
+def _stream(stream, q):
+    import torch
+
+    return (stream if stream is not None else torch.cuda.current_stream(q.device)).cuda_stream
 
 
 def flash_attn_fwd(q, k, v, softmax_scale: float | None = None, causal: bool = False,
@@ -258,35 +341,21 @@ def flash_attn_fwd(q, k, v, softmax_scale: float | None = None, causal: bool = F
     Returns (out [B, S, H, D] in the input dtype, lse [B, H, S] fp32).  Runs
     on ``stream`` (a torch stream) or torch's current stream, asynchronously.
     """
-    import torch
-
     if dropout_p != 0.0:
         raise NotImplementedError("dropout is not part of the exact forward pass")
     if alibi_slopes is not None:
         raise NotImplementedError("ALiBi slopes are not supported")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
-            raise TypeError(f"{name} must be a GPU tensor")
-        if t.dim() != 4 or t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
-            raise ValueError("q, k, v must share shape [B, S, H, D], dtype and device")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous [B, S, H, D]")
+    import torch
+
+    _check_qkv(q, k, v)
     B, S, H, D = q.shape
     dtype = _dtype_code(q)
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor shaped and typed like q")
-    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 tensor [B, H, S]")
+    out, lse = _outputs(q, out, lse)
     wl, wr = (int(x) for x in window_size)
-    st = stream if stream is not None else torch.cuda.current_stream(q.device)
     with torch.cuda.device(q.device):
         rc = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
-                    S, D, scale, int(bool(causal)), wl, wr, dtype, st.cuda_stream)
+                    S, D, scale, int(bool(causal)), wl, wr, dtype, _stream(stream, q))
     if rc != 0:
         raise FaError(rc, "fa_fwd")
     return out, lse
@@ -297,18 +366,12 @@ def flash_attn_fwd_splitkv(q, k, v, softmax_scale: float | None = None, causal: 
                            workspace=None, stream=None):
     """flash_attn_fwd with the K/V tiles of each Q tile split into ``n_splits``
     parts (0 = the library's choice for the current device) and merged.  The
-    fp32 workspace is a torch tensor of at least the size
+    fp32 workspace is a torch tensor on q's device of at least the size
     fa_fwd_splitkv_workspace_size reports (allocated here when None).
     Returns (out, lse) like flash_attn_fwd."""
     import torch
 
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
-            raise TypeError(f"{name} must be a GPU tensor")
-        if t.dim() != 4 or t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
-            raise ValueError("q, k, v must share shape [B, S, H, D], dtype and device")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous [B, S, H, D]")
+    _check_qkv(q, k, v)
     B, S, H, D = q.shape
     dtype = _dtype_code(q)
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
@@ -317,23 +380,12 @@ def flash_attn_fwd_splitkv(q, k, v, softmax_scale: float | None = None, causal: 
         if n_splits == 0:
             n_splits = fa_fwd_splitkv_auto_splits(B, H, S, D, int(bool(causal)), wl, wr, dtype)
         need = fa_fwd_splitkv_workspace_size(B, H, S, D, dtype, n_splits)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor shaped and typed like q")
-    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 tensor [B, H, S]")
-    if workspace is None and need > 0:
-        workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else 0
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    out, lse = _outputs(q, out, lse)
+    ws_ptr, ws_bytes, _ws = _workspace(workspace, need, q, torch.float32, stream)
     with torch.cuda.device(q.device):
         rc = fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                             lse.data_ptr(), B, H, S, D, scale, int(bool(causal)), wl, wr, dtype,
-                            n_splits, ws_ptr or None, ws_bytes, st.cuda_stream)
+                            n_splits, ws_ptr, ws_bytes, _stream(stream, q))
     if rc != 0:
         raise FaError(rc, "fa_fwd_splitkv")
     return out, lse
@@ -354,15 +406,9 @@ def flash_attn_fwd_blocksparse(q, k, v, block_mask, block_m: int, block_n: int,
     Returns (out, lse) like flash_attn_fwd."""
     import torch
 
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
-            raise TypeError(f"{name} must be a GPU tensor")
-        if t.dim() != 4 or t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
-            raise ValueError("q, k, v must share shape [B, S, H, D], dtype and device")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous [B, S, H, D]")
+    _check_qkv(q, k, v)
     if not isinstance(block_mask, torch.Tensor) or block_mask.device != q.device:
-        raise TypeError("block_mask must be a tensor on q's device")
+        raise ValueError("block_mask must be a tensor on q's device")
     if block_mask.dtype not in (torch.uint8, torch.bool) or not block_mask.is_contiguous():
         raise ValueError("block_mask must be a contiguous uint8 or bool tensor")
     mask = block_mask.view(torch.uint8) if block_mask.dtype == torch.bool else block_mask
@@ -378,27 +424,44 @@ def flash_attn_fwd_blocksparse(q, k, v, block_mask, block_m: int, block_n: int,
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     wl, wr = (int(x) for x in window_size)
     need = fa_fwd_blocksparse_workspace_size(B, H, S, D, dtype, n_mask)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor shaped and typed like q")
-    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 tensor [B, H, S]")
-    if workspace is None and need > 0:
-        workspace = torch.empty((need + 3) // 4, dtype=torch.int32, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else 0
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    out, lse = _outputs(q, out, lse)
+    ws_ptr, ws_bytes, _ws = _workspace(workspace, need, q, torch.int32, stream)
     with torch.cuda.device(q.device):
         rc = fa_fwd_blocksparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                 lse.data_ptr(), B, H, S, D, scale, int(bool(causal)), wl, wr,
                                 dtype, mask.data_ptr(), n_mask, int(block_m), int(block_n),
-                                ws_ptr or None, ws_bytes, st.cuda_stream)
+                                ws_ptr, ws_bytes, _stream(stream, q))
     if rc != 0:
         raise FaError(rc, "fa_fwd_blocksparse")
     return out, lse
+
+
+def _check_pools(q, k_pages, v_pages):
+    import torch
+
+    _, _, H, D = q.shape
+    for name, t in (("k_pages", k_pages), ("v_pages", v_pages)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor")
+        if t.device != q.device:
+            raise ValueError(f"{name} is on {t.device}; it must be on q's device {q.device}")
+        if t.dtype != q.dtype:
+            raise ValueError(f"{name} must have q's dtype {q.dtype}")
+        if t.dim() != 4 or t.shape != k_pages.shape or tuple(t.shape[2:]) != (H, D):
+            raise ValueError(f"{name} must be [num_pages, page_size, H, D] like the other pool")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _check_table(name, t, q, rows: int):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device != q.device:
+        raise ValueError(f"{name} is on {t.device}; it must be on q's device {q.device}")
+    if t.dtype != torch.int32 or t.dim() != 2 or t.shape[0] != rows or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 tensor [{rows}, n]")
 
 
 def flash_attn_fwd_paged(q, k_pages, v_pages, block_table, softmax_scale: float | None = None,
@@ -413,22 +476,10 @@ def flash_attn_fwd_paged(q, k_pages, v_pages, block_table, softmax_scale: float 
     None.  Returns (out, lse) like flash_attn_fwd."""
     import torch
 
-    if not isinstance(q, torch.Tensor) or q.device.type != "cuda" or q.dim() != 4:
-        raise TypeError("q must be a GPU tensor [B, S, H, D]")
-    if not q.is_contiguous():
-        raise ValueError("q must be contiguous [B, S, H, D]")
+    _check_q(q)
     B, S, H, D = q.shape
-    for name, t in (("k_pages", k_pages), ("v_pages", v_pages)):
-        if not isinstance(t, torch.Tensor) or t.device != q.device or t.dtype != q.dtype:
-            raise TypeError(f"{name} must be a tensor of q's dtype on q's device")
-        if t.dim() != 4 or t.shape != k_pages.shape or tuple(t.shape[2:]) != (H, D):
-            raise ValueError(f"{name} must be [num_pages, page_size, H, D] like the other pool")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if (not isinstance(block_table, torch.Tensor) or block_table.device != q.device or
-            block_table.dtype != torch.int32 or block_table.dim() != 2 or
-            block_table.shape[0] != B or not block_table.is_contiguous()):
-        raise ValueError("block_table must be a contiguous int32 tensor [B, n] on q's device")
+    _check_pools(q, k_pages, v_pages)
+    _check_table("block_table", block_table, q, B)
     num_pages, page_size = k_pages.shape[0], k_pages.shape[1]
     dtype = _dtype_code(q)
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
@@ -437,25 +488,13 @@ def flash_attn_fwd_paged(q, k_pages, v_pages, block_table, softmax_scale: float 
         if n_splits == 0:
             n_splits = fa_fwd_splitkv_auto_splits(B, H, S, D, int(bool(causal)), wl, wr, dtype)
         need = fa_fwd_splitkv_workspace_size(B, H, S, D, dtype, n_splits)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError("out must be a contiguous tensor shaped and typed like q")
-    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous fp32 tensor [B, H, S]")
-    if workspace is None and need > 0:
-        workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=q.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else 0
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+    out, lse = _outputs(q, out, lse)
+    ws_ptr, ws_bytes, _ws = _workspace(workspace, need, q, torch.float32, stream)
     with torch.cuda.device(q.device):
         rc = fa_fwd_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
                           block_table.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, S, D,
                           scale, int(bool(causal)), wl, wr, dtype, num_pages, page_size,
-                          block_table.shape[1], n_splits, ws_ptr or None, ws_bytes,
-                          st.cuda_stream)
+                          block_table.shape[1], n_splits, ws_ptr, ws_bytes, _stream(stream, q))
     if rc != 0:
         raise FaError(rc, "fa_fwd_paged")
     return out, lse
@@ -470,17 +509,11 @@ def flash_attn_bwd(dout, q, k, v, out, lse, softmax_scale: float | None = None,
     and the gradients are allocated here when None."""
     import torch
 
-    ts = (("dout", dout), ("q", q), ("k", k), ("v", v), ("out", out))
-    for name, t in ts:
-        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
-            raise TypeError(f"{name} must be a GPU tensor")
-        if t.dim() != 4 or t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
-            raise ValueError("dout, q, k, v, out must share shape [B, S, H, D], dtype and device")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous [B, S, H, D]")
+    _check_qkv(q, k, v)
+    _check_like("dout", dout, q)
+    _check_like("out", out, q)
     B, S, H, D = q.shape
-    if lse.shape != (B, H, S) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be the forward's contiguous fp32 [B, H, S]")
+    _check_like("lse", lse, q, shape=(B, H, S), dtype=torch.float32)
     dtype = _dtype_code(q)
     scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
     wl, wr = (int(x) for x in window_size)
@@ -488,16 +521,14 @@ def flash_attn_bwd(dout, q, k, v, out, lse, softmax_scale: float | None = None,
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous tensor shaped and typed like q")
-    if workspace is None:
-        workspace = torch.empty((B, H, S), dtype=torch.float32, device=q.device)
-    st = stream if stream is not None else torch.cuda.current_stream(q.device)
+        _check_like(name, t, q)
+    need = B * H * S * 4
+    ws_ptr, ws_bytes, _ws = _workspace(workspace, need, q, torch.float32, stream)
     with torch.cuda.device(q.device):
         rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                     dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, S, D,
-                    scale, int(bool(causal)), wl, wr, dtype, workspace.data_ptr(),
-                    workspace.numel() * workspace.element_size(), st.cuda_stream)
+                    scale, int(bool(causal)), wl, wr, dtype, ws_ptr, ws_bytes,
+                    _stream(stream, q))
     if rc != 0:
         raise FaError(rc, "fa_bwd")
     return dq, dk, dv

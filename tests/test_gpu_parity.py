@@ -5,7 +5,7 @@ Tolerances (max-abs, on every compared element): O <= 1e-4 for fp32,
 <= 4e-3 for fp16, <= 2e-2 for bf16; LSE <= 1e-3.  Any NaN or Inf where the
 oracle is finite fails.  Sizes here span several Q and K/V tiles plus a ragged
 tail, so the oracle checks every element; the named workloads at full size
-are checked on sampled rows that the oracle computes one by one.
+are checked on every element too, the oracle running head by head.
 """
 import math
 
@@ -108,7 +108,7 @@ def test_parity_launch_order_blocks(B, H, S):
 
 def test_parity_launch_order_many_workgroups():
     """5 heads of 16384 causal rows: 640 workgroups, more than the device holds
-    at once, with XCD blocks that split heads; sampled rows of every head."""
+    at once, with XCD blocks that split heads; every element of every head."""
     from types import SimpleNamespace
 
     w = SimpleNamespace(name="causal_16k_h5", B=1, H=5, S=16384, D=128, dtype=torch.bfloat16,
@@ -116,9 +116,7 @@ def test_parity_launch_order_many_workgroups():
     q, k, v = make_qkv(w.B, w.S, w.H, w.D, w.dtype, 55)
     print("run causal 16384 x 5 heads", flush=True)
     out, lse = gpu_fwd(q, k, v, w.scale, w.causal, w.window)
-    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
-    rows = [0, 127, 128, 4095, 4096, 8191, 12288, 16255, 16256, 16383]
-    check_sampled_rows(w, q, k, v, out, lse, [(0, h) for h in range(w.H)], rows)
+    check_every_row(w, q, k, v, out, lse)
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "gpt_causal_2k", "full_4k_d64"])
@@ -127,42 +125,46 @@ def test_parity_named_small_workloads(name, seed):
     """The tiny fp32, 2K causal and 4K full workloads at full size, every
     element, three seeds each."""
     w = WORKLOADS[name]
-    if name == "full_4k_d64":
-        # B4 H16 S4096 in full: oracle cost is ~275 GFLOP fp64; check two heads
-        # of every batch in full and the rest on sampled rows below
+    if name == "full_4k_d64":  # 64 heads: the oracle runs head by head
         q, k, v = workload_qkv(w, seed)
+        print("run", w.describe(), "seed", seed, flush=True)
         out, lse = gpu_fwd(q, k, v, w.scale, w.causal, w.window)
-        check_sampled_rows(w, q, k, v, out, lse, heads=[(b, h) for b in range(w.B) for h in (0, 15)],
-                           rows=np.arange(0, w.S, 97))
+        check_every_row(w, q, k, v, out, lse)
         return
     check_full(w.B, w.S, w.H, w.D, w.dtype, w.causal, w.window, w.seed if seed is None else seed)
 
 
-def check_sampled_rows(w, q, k, v, out, lse, heads, rows):
-    for b, h in heads:
-        for r0 in rows:
-            r1 = min(w.S, int(r0) + 1)
-            ro, rl = oracle.fwd_rows(q, k, v, w.scale, w.causal, w.window, b, h, int(r0), r1)
-            assert_close(out[b, r0:r1, h, :], lse[b, h, r0:r1], ro, rl, w.dtype,
-                         f"{w.name} b{b} h{h} row{r0}")
+def check_every_row(w, q, k, v, out, lse, chunk_rows=None):
+    """Every element of out and lse against the oracle, head by head in chunks
+    of query rows (the oracle materialises a chunk x S score matrix), with the
+    largest errors over the whole tensor printed and checked."""
+    chunk_rows = w.S if chunk_rows is None else chunk_rows
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    eo = el = 0.0
+    for b in range(w.B):
+        for h in range(w.H):
+            for r0 in range(0, w.S, chunk_rows):
+                r1 = min(w.S, r0 + chunk_rows)
+                ro, rl = oracle.fwd_rows(q, k, v, w.scale, w.causal, w.window, b, h, r0, r1)
+                assert np.all(np.isfinite(ro)) and np.all(np.isfinite(rl))
+                eo = max(eo, float(np.max(np.abs(out[b, r0:r1, h, :].double().numpy() - ro))))
+                el = max(el, float(np.max(np.abs(lse[b, h, r0:r1].double().numpy() - rl))))
+    print(f"{w.name} every element: max|dO|={eo:.3e} max|dLSE|={el:.3e}", flush=True)
+    assert eo <= TOL_O[w.dtype], f"{w.name}: O error {eo} > {TOL_O[w.dtype]}"
+    assert el <= TOL_LSE, f"{w.name}: LSE error {el} > {TOL_LSE}"
 
 
-@pytest.mark.parametrize("name", ["window_8k", "causal_16k", "causal_32k", "gpt_causal_2k",
-                                  "full_4k_d64"])
-def test_parity_named_full_size_sampled(name):
-    """Full-size named workloads in the launch configuration the benchmark
-    times: sampled rows (first, last, tile edges, random) of several heads
-    against the oracle row by row, plus finiteness everywhere."""
+@pytest.mark.parametrize("name", ["window_8k", "causal_16k", "causal_32k"])
+def test_parity_named_full_size_every_element(name):
+    """The full-size named workloads in the launch configuration the benchmark
+    times (one fa_fwd over the whole workload): every element of O and LSE
+    against the oracle.  The 32K run goes through the oracle in chunks of 8192
+    rows (a 32768 x 32768 fp64 matrix per head would be 8 GiB)."""
     w = WORKLOADS[name]
     q, k, v = workload_qkv(w)
     print("run", w.describe(), flush=True)
     out, lse = gpu_fwd(q, k, v, w.scale, w.causal, w.window)
-    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
-    rng = np.random.default_rng(w.seed)
-    rows = sorted(set([0, 1, 63, 64, 127, 128, 129, w.S // 2, w.S - 129, w.S - 2, w.S - 1] +
-                      list(rng.integers(0, w.S, 6))))
-    heads = sorted({(0, 0), (w.B - 1, w.H - 1), (int(rng.integers(w.B)), int(rng.integers(w.H)))})
-    check_sampled_rows(w, q, k, v, out, lse, heads, rows)
+    check_every_row(w, q, k, v, out, lse, chunk_rows=8192)
 
 
 # ---------------------------------------------------------------- exact cases
@@ -346,16 +348,14 @@ def test_splitkv_gpt_causal_2k(n_splits):
 
 
 @pytest.mark.parametrize("n_splits", [0, 4])
-def test_splitkv_head_sharded_16k_sampled(n_splits):
+def test_splitkv_head_sharded_16k(n_splits):
     """One GPU's share of the 16K causal workload under head sharding (2 of
-    16 heads) in the library's part count and in 4 parts: sampled rows of both
-    heads."""
+    16 heads) in the library's part count and in 4 parts: every element of
+    both heads."""
     w = WORKLOADS["causal_16k_h2"]
     q, k, v = workload_qkv(w)
     out, lse = gpu_fwd_splitkv(q, k, v, w.scale, w.causal, w.window, n_splits)
-    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
-    rows = [0, 1, 127, 128, 255, 4096, 8191, 12345, 16255, 16383]
-    check_sampled_rows(w, q, k, v, out, lse, [(0, 0), (0, 1)], rows)
+    check_every_row(w, q, k, v, out, lse)
 
 
 def test_splitkv_nan_rows_propagate_like_the_oracle():
