@@ -59,6 +59,109 @@
 
 namespace fa {
 
+// ---------------------------------------------------------------- exact rows
+// The P V MFMA multiplies every key of a visited K/V tile by its weight, and a
+// key outside a row's mask has weight exactly 0.  For finite values that adds
+// exactly 0, but a NaN or an infinity in such a key's value row turns 0 * v
+// into NaN for rows that do not allow the key, while the definition sums over
+// allowed keys only.  Any non-finite value in a visited tile leaves a
+// non-finite O in every row of the wave, so after its last tile a wave tests
+// its O accumulator (one FMA with 0 per element) and, only if it finds a NaN
+// or an infinity, recomputes its rows with the vector ALU from the final row
+// statistics, summing the allowed keys alone.  Finite inputs never take this
+// path.  (It also bounds every weight by 1, so huge finite values that
+// overflowed the un-normalised fp32 accumulator come out finite.)
+
+// Eight consecutive elements of a row as fp32 (16-byte aligned for 2-byte types).
+template <typename T> __device__ inline void load8(const T* p, float (&x)[8]);
+template <> __device__ inline void load8<__bf16>(const __bf16* p, float (&x)[8]) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+}
+template <> __device__ inline void load8<_Float16>(const _Float16* p, float (&x)[8]) {
+    const f16x8 w = *reinterpret_cast<const f16x8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (float)w[i];
+}
+template <> __device__ inline void load8<float>(const float* p, float (&x)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[i] = a[i];
+        x[4 + i] = b[i];
+    }
+}
+
+// The normalised O columns [hh * D/2, hh * D/2 + D/2) of this lane's query row:
+// sum over the keys of K/V positions [w0, w1) that allowed(key) admits of
+// p_j * v_j, p_j = exp2(c * s_j - m_ref) * inv_l with the row's final
+// reference m_ref and normaliser inv_l = 1 / l.  The two lanes of a row (wave
+// halves) split the dot product s_j = q . k_j by the same column halves and
+// add the halves in the same order.  q_half points at the row's columns of
+// this half (nullptr for a padding row past S).  tile_of(pos, k0, row0, valid)
+// gives position pos's first key, the row of that key in the K/V tensors (or
+// pools) counted from k_head / v_head, and whether the tile lies inside them
+// (a tile outside reads as zeros, as the tile loads make it).  Every loop
+// bound is wave-uniform, so the half exchange sees all 64 lanes.
+template <typename T, int D, int BN, typename TileOf, typename Allowed>
+__device__ inline __attribute__((always_inline)) void exact_row(
+    const T* __restrict__ q_half, const T* __restrict__ k_head, const T* __restrict__ v_head,
+    int64_t row_stride, int hh, int S, int w0, int w1, TileOf tile_of, Allowed allowed, float c,
+    float m_ref, float inv_l, float (&acc)[D / 2]) {
+    constexpr int DH = D / 2;
+#pragma unroll
+    for (int d = 0; d < DH; ++d) acc[d] = 0.f;
+    for (int pos = w0; pos < w1; ++pos) {
+        int k0;
+        int64_t row0;
+        bool valid;
+        tile_of(pos, k0, row0, valid);
+        for (int jj = 0; jj < BN && k0 + jj < S; ++jj) {
+            const int64_t off = (row0 + jj) * row_stride + (int64_t)hh * DH;
+            float part = 0.f;
+            // a rolled loop: unrolled, the compiler would hoist every chunk's
+            // loads at once and raise the kernel's register count
+#pragma unroll 1
+            for (int c8 = 0; c8 < DH / 8; ++c8) {
+                float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                if (valid) load8<T>(k_head + off + 8 * c8, x);
+                if (q_half) load8<T>(q_half + 8 * c8, y);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) part = __builtin_fmaf(y[i], x[i], part);
+            }
+            const float s = halves_sum(part);
+            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s, c, -m_ref)) * inv_l;
+            if (q_half && allowed(k0 + jj)) {
+#pragma unroll
+                for (int c8 = 0; c8 < DH / 8; ++c8) {
+                    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                    if (valid) load8<T>(v_head + off + 8 * c8, x);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[8 * c8 + i] = __builtin_fmaf(p, x[i], acc[8 * c8 + i]);
+                }
+            }
+        }
+    }
+}
+
+// True in every lane when some lane's accumulator holds a NaN or an infinity.
+template <int DB> __device__ inline bool any_nonfinite(const f32x16 (&o)[DB]) {
+    float z0 = 0.f, z1 = 0.f;
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+            z0 = __builtin_fmaf(o[d][i], 0.f, z0);
+            z1 = __builtin_fmaf(o[d][i + 1], 0.f, z1);
+        }
+    return __any((z0 + z1) != (z0 + z1));
+}
+
 // SPLIT: the K/V tiles of each Q tile are cut into n_splits contiguous parts,
 // one workgroup per (Q tile, part); each writes the partial (O, LSE) of its
 // part, in fp32, to part_o [n_splits, B, H, S, D] and part_lse
@@ -431,6 +534,9 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
         }
     };
 
+    // K/V positions this wave computed: [ex_w0, ex_w1) (for the exact
+    // recomputation in the epilogue)
+    int ex_w0 = kt0, ex_w1 = kt0;
     // A block-sparse Q tile may keep no tile at all: its rows have no allowed
     // key, and the epilogue writes O = 0, LSE = -inf.
     if (!SPARSE || kt1 > kt0) {
@@ -505,6 +611,8 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     }
     kw0 = __builtin_amdgcn_readfirstlane(kw0);
     kw1 = __builtin_amdgcn_readfirstlane(kw1);
+    ex_w0 = kw0;
+    ex_w1 = kw1;
     // the tiles this wave runs without the mask: every key allowed for each of
     // its own 32 rows (a superset of the workgroup's [ki0, ki1): near a window
     // edge or the causal diagonal a wave needs the mask on fewer tiles than the
@@ -675,6 +783,49 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
     const float m_fin = (m_run == kNegInf) ? 0.f : m_run;
     const float lse_v = (l_tot == 0.f) ? kNegInf : 0.69314718055994531f * (m_fin + __log2f(l_tot));
+    // a NaN or an infinity in O: this wave recomputes its rows over their
+    // allowed keys only (exact_row), stores them and its LSE, and is done
+    if (any_nonfinite<DB>(o)) {
+        constexpr int DH = D / 2;
+        float acc[DH];
+        auto tile_of = [&](int pos, int& k0, int64_t& row0, bool& valid) __attribute__((always_inline)) {
+            const int tile = SPARSE ? sp_row[4 + pos] : pos;
+            k0 = tile * BN;
+            row0 = k0;
+            valid = true;
+            if (PAGED) {
+                const int page = pg_table[(int64_t)bb * pg_stride + tile / pg_tiles];
+                valid = (unsigned)page < (unsigned)pg_count;
+                row0 = (int64_t)(valid ? page : 0) * pg_rows + (int64_t)(tile % pg_tiles) * BN;
+            }
+        };
+        auto allowed = [&](int key) __attribute__((always_inline)) {
+            return (unsigned)(key - key_lo) <= (unsigned)key_w;
+        };
+        const T* q_half = qrow < S ? q + head_base + (int64_t)qrow * row_stride + hh * DH : nullptr;
+        exact_row<T, D, BN>(q_half, (const T*)k_head, (const T*)v_head, row_stride, hh, S, ex_w0,
+                            ex_w1, tile_of, allowed, c, m_fin, inv, acc);
+        if (qrow < S) {
+            if (SPLIT) {
+                if (hh == 0) part_lse[part_row] = lse_v;
+#pragma unroll
+                for (int c4 = 0; c4 < DH / 4; ++c4)
+                    *reinterpret_cast<f32x4*>(part_o + part_row * D + hh * DH + 4 * c4) =
+                        f32x4{acc[4 * c4], acc[4 * c4 + 1], acc[4 * c4 + 2], acc[4 * c4 + 3]};
+            } else {
+                if (hh == 0) lse[((int64_t)bb * H + h) * S + qrow] = lse_v;
+                T* const orow = out + head_base + (int64_t)qrow * row_stride + hh * DH;
+#pragma unroll
+                for (int c8 = 0; c8 < DH / 8; ++c8)
+                    *reinterpret_cast<u32x4*>(orow + 8 * c8) = u32x4{
+                        Mfma<T>::pack2(acc[8 * c8], acc[8 * c8 + 1]),
+                        Mfma<T>::pack2(acc[8 * c8 + 2], acc[8 * c8 + 3]),
+                        Mfma<T>::pack2(acc[8 * c8 + 4], acc[8 * c8 + 5]),
+                        Mfma<T>::pack2(acc[8 * c8 + 6], acc[8 * c8 + 7])};
+            }
+        }
+        return;
+    }
     if (SPLIT) {  // the part's normalised O and its LSE, in fp32
         if (qrow < S) {
             if (hh == 0) part_lse[part_row] = lse_v;
@@ -974,6 +1125,44 @@ __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
     // l == 0 only for a row with no allowed key; a NaN l (NaN scores) propagates
     const float l_tot = halves_sum(l_run);
     const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
+    const float m_fin = (m_run == kNegInf) ? 0.f : m_run;
+    const float lse_v = (l_tot == 0.f) ? kNegInf : 0.69314718055994531f * (m_fin + __log2f(l_tot));
+    // a NaN or an infinity in O: this wave recomputes its rows over their
+    // allowed keys only (exact_row), stores them and its LSE, and is done
+    if (any_nonfinite<DB>(o)) {
+        constexpr int DH = D / 2;
+        float acc[DH];
+        const int64_t kv_base = PAGED ? (int64_t)h * D : head_base;
+        auto tile_of = [&](int pos, int& k0, int64_t& row0, bool& valid) __attribute__((always_inline)) {
+            k0 = pos * BN;
+            row0 = k0;
+            valid = !SPARSE || mrow[k0 / block_n] != 0;  // a dropped tile adds nothing
+            if (PAGED) {
+                const int page = pg_table[(int64_t)bb * pg_stride + k0 / pg_rows];
+                valid = (unsigned)page < (unsigned)pg_count;
+                row0 = (int64_t)(valid ? page : 0) * pg_rows + k0 % pg_rows;
+            }
+        };
+        auto allowed = [&](int key) __attribute__((always_inline)) {
+            bool ok = key < S;
+            if (causal) ok = ok && key <= qrow;
+            if (wl >= 0) ok = ok && qrow - key <= wl;
+            if (wr >= 0) ok = ok && key - qrow <= wr;
+            return ok && (!SPARSE || mrow[key / block_n] != 0);
+        };
+        const float* q_half = qrow < S ? q + head_base + (int64_t)qrow * row_stride + hh * DH : nullptr;
+        exact_row<float, D, BN>(q_half, k + kv_base, v + kv_base, row_stride, hh, S, (int)kt0,
+                                (int)kt1, tile_of, allowed, c, m_fin, inv, acc);
+        if (qrow < S) {
+            float* eo = out + head_base + (int64_t)qrow * row_stride + hh * DH;
+#pragma unroll
+            for (int c4 = 0; c4 < DH / 4; ++c4)
+                *reinterpret_cast<f32x4*>(eo + 4 * c4) =
+                    f32x4{acc[4 * c4], acc[4 * c4 + 1], acc[4 * c4 + 2], acc[4 * c4 + 3]};
+            if (hh == 0) lse[((int64_t)bb * H + h) * S + qrow] = lse_v;
+        }
+        return;
+    }
     if (qrow < S) {
         float* op = out + head_base + (int64_t)qrow * row_stride + 4 * hh;
 #pragma unroll
@@ -984,11 +1173,7 @@ __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
                            o[d][4 * g + 3] * inv};
                 *reinterpret_cast<f32x4*>(op + 32 * d + 8 * g) = w;
             }
-        if (hh == 0) {
-            const float m_fin = (m_run == kNegInf) ? 0.f : m_run;
-            const float lse_v = (l_tot == 0.f) ? kNegInf : 0.69314718055994531f * (m_fin + __log2f(l_tot));
-            lse[((int64_t)bb * H + h) * S + qrow] = lse_v;
-        }
+        if (hh == 0) lse[((int64_t)bb * H + h) * S + qrow] = lse_v;
     }
 }
 
