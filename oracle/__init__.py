@@ -85,6 +85,10 @@ def _load():
                                               ctypes.c_int, i64, i64, i64, i64, vp, i64, vp, i64,
                                               vp, vp, vp, ctypes.c_int]
         lib.fa_oracle_bwd_sampled.restype = ctypes.c_int
+        lib.fa_oracle_fwd_kvcache.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, i64, i64,
+                                              dp, ctypes.c_int, i64, i64, vp, vp, vp,
+                                              ctypes.c_int]
+        lib.fa_oracle_fwd_kvcache.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -240,6 +244,60 @@ def fwd_paged(q, k_pages, v_pages, block_table, scale: float, causal: bool = Fal
     k = gather_pages(k_pages, block_table, S)
     v = gather_pages(v_pages, block_table, S)
     return fwd(q, k, v, scale, causal, window_size, nthreads)
+
+
+def fwd_kvcache(q, k_cache, v_cache, seqlens, scale: float, causal: bool = False,
+                window_size=(-1, -1), nthreads: int = 0):
+    """Attention of S_q new queries against a key/value cache (decoding):
+    q [B, S_q, H, D]; k_cache, v_cache [B, S_k, H, D] of q's dtype; seqlens
+    [B] ints, the valid rows L_b <= S_k of each sequence's cache.  Query i of
+    sequence b sits at position L_b - S_q + i, and the causal / window masks
+    apply to positions ("FlashAttention技术解析：加速GPT训练的核心优化" section 5
+    names FlashDecoding for the KV cache of inference).  Returns (out
+    [B, S_q, H, D] fp64, lse [B, H, S_q] fp64)."""
+    _check_inputs(q, q, q)
+    _check_inputs(k_cache, k_cache, v_cache)
+    if k_cache.dtype != q.dtype or k_cache.shape[0] != q.shape[0] or \
+            tuple(k_cache.shape[2:]) != tuple(q.shape[2:]):
+        raise ValueError("oracle: the caches must be [B, S_k, H, D] of q's dtype")
+    lib = _load()
+    B, S_q, H, D = q.shape
+    S_k = k_cache.shape[1]
+    lens = np.ascontiguousarray(np.asarray(seqlens, dtype=np.int64))
+    if lens.shape != (B,):
+        raise ValueError("oracle: seqlens must hold one length per sequence")
+    wl, wr = _window(window_size)
+    out = np.empty((B, S_q, H, D), dtype=np.float64)
+    lse = np.empty((B, H, S_q), dtype=np.float64)
+    rc = lib.fa_oracle_fwd_kvcache(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                   _dtype_code(q), B, H, S_q, S_k, D, float(scale),
+                                   int(bool(causal)), wl, wr, lens.ctypes.data, out.ctypes.data,
+                                   lse.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle: fa_oracle_fwd_kvcache failed ({rc})")
+    return out, lse
+
+
+def fwd_kvcache_paged(q, k_pages, v_pages, block_table, seqlens, S_k: int, scale: float,
+                      causal: bool = False, window_size=(-1, -1), nthreads: int = 0):
+    """fwd_kvcache with the caches in paged pools [num_pages, page_size, H, D]
+    found through block_table [B, n]: sequence b's first L_b rows are gathered
+    (gather_pages) into a contiguous cache of capacity S_k, the rest of which
+    stays zero and is never read."""
+    import torch
+
+    bt = np.ascontiguousarray(np.asarray(block_table), dtype=np.int32)
+    B = q.shape[0]
+    _, _, H, D = k_pages.shape
+    caches = []
+    for pool in (k_pages, v_pages):
+        dense = torch.zeros((B, S_k, H, D), dtype=pool.dtype)
+        for b in range(B):
+            L = int(seqlens[b])
+            if L > 0:
+                dense[b, :L] = gather_pages(pool, bt[b:b + 1], L)[0]
+        caches.append(dense)
+    return fwd_kvcache(q, caches[0], caches[1], seqlens, scale, causal, window_size, nthreads)
 
 
 def bwd(q, k, v, dout, scale: float, causal: bool = False, window_size=(-1, -1),

@@ -614,3 +614,105 @@ int fa_oracle_bwd_sampled(const void* q, const void* k, const void* v, const voi
     free(Qh); free(Kh); free(Vh); free(Gh); free(rmax); free(rsum); free(rdot);
     return 0;
 }
+
+/*
+ * fa_oracle_fwd_kvcache -- attention of S_q new queries against a key/value
+ * cache, as at inference ("FlashAttention技术解析：加速GPT训练的核心优化",
+ * section 5, names FlashDecoding, the variant of the method for the KV cache of
+ * inference; "突破大模型训练瓶颈：Flash-Attention编译优化与内存占用解决方案",
+ * section 总结与最佳实践, names the call flash_attn_with_kvcache).  The pages
+ * give no more, and the plainest reading is taken:
+ *  - sequence b's keys and values are the first L_b = seqlens[b] rows of the
+ *    cache, the new tokens' own keys and values included (rows past L_b are
+ *    never read);
+ *  - its S_q queries are the last S_q positions of that sequence, so query i
+ *    sits at position  p = L_b - S_q + i;
+ *  - key j (0 <= j < L_b) is allowed for it when allowed(p, j), the causal and
+ *    window rules of the dense definition applied to positions.
+ * Then, as before, s_pj = scale * q_i . k_j over the allowed keys,
+ * O_i = softmax(s) V and LSE_i = ln sum_j exp(s_pj).  A row with no allowed
+ * key (p < 0 under the causal mask, or L_b = 0) gets O = 0 and LSE = -inf.
+ * With S_q = L_b = S_k every row sits at its own index and this is
+ * fa_oracle_fwd.
+ *
+ * q, out: [B, S_q, H, D]; k, v: [B, S_k, H, D], S_k the cache's capacity
+ * (0 <= L_b <= S_k); lse: [B, H, S_q].  Outputs fp64.  Each (b, h) scores
+ * matrix (S_q x L_b) is materialised; rows run over nthreads threads.
+ */
+int fa_oracle_fwd_kvcache(const void* q, const void* k, const void* v, int dtype, int64_t B,
+                          int64_t H, int64_t S_q, int64_t S_k, int64_t D, double scale,
+                          int causal, int64_t wl, int64_t wr, const int64_t* seqlens,
+                          double* out, double* lse, int nthreads) {
+    if (orc_check(dtype, B, H, S_q, D, wl, wr) || S_k < 1 || !seqlens) return -1;
+    for (int64_t b = 0; b < B; ++b)
+        if (seqlens[b] < 0 || seqlens[b] > S_k) return -1;
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t L = seqlens[b];
+        for (int64_t h = 0; h < H; ++h) {
+            double* Q = (double*)malloc(sizeof(double) * (size_t)(S_q * D));
+            double* K = (double*)malloc(sizeof(double) * (size_t)((L > 0 ? L : 1) * D));
+            double* V = (double*)malloc(sizeof(double) * (size_t)((L > 0 ? L : 1) * D));
+            double* P = (double*)malloc(sizeof(double) * (size_t)(S_q * (L > 0 ? L : 1)));
+            if (!Q || !K || !V || !P) {
+                free(Q); free(K); free(V); free(P);
+                return -2;
+            }
+            for (int64_t r = 0; r < S_q; ++r)
+                for (int64_t d = 0; d < D; ++d)
+                    Q[r * D + d] = orc_load(q, dtype, ((b * S_q + r) * H + h) * D + d);
+            for (int64_t j = 0; j < L; ++j)
+                for (int64_t d = 0; d < D; ++d) {
+                    K[j * D + d] = orc_load(k, dtype, ((b * S_k + j) * H + h) * D + d);
+                    V[j * D + d] = orc_load(v, dtype, ((b * S_k + j) * H + h) * D + d);
+                }
+#pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads)
+            for (int64_t r = 0; r < S_q; ++r) {
+                const int64_t p = L - S_q + r; /* the query's position in its sequence */
+                double* prow = P + r * (L > 0 ? L : 1);
+                double* orow = out + ((b * S_q + r) * H + h) * D;
+                double* lrow = lse + (b * H + h) * S_q + r;
+                /* 1. scores of the allowed keys; -inf elsewhere */
+                for (int64_t j = 0; j < L; ++j) {
+                    if (!orc_allowed(p, j, causal, wl, wr)) {
+                        prow[j] = -INFINITY;
+                        continue;
+                    }
+                    double dot = 0.0;
+                    for (int64_t d = 0; d < D; ++d) dot += Q[r * D + d] * K[j * D + d];
+                    prow[j] = scale * dot;
+                }
+                /* 2. row max (a NaN anywhere makes it NaN) */
+                double m = -INFINITY;
+                for (int64_t j = 0; j < L; ++j) {
+                    if (isnan(prow[j])) {
+                        m = prow[j];
+                        break;
+                    }
+                    if (prow[j] > m) m = prow[j];
+                }
+                if (m == -INFINITY) { /* no allowed key */
+                    for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
+                    *lrow = -INFINITY;
+                    continue;
+                }
+                /* 3. softmax */
+                double l = 0.0;
+                for (int64_t j = 0; j < L; ++j) {
+                    prow[j] = exp(prow[j] - m);
+                    l += prow[j];
+                }
+                for (int64_t j = 0; j < L; ++j) prow[j] /= l;
+                /* 4. O = P V over the allowed keys */
+                for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
+                for (int64_t j = 0; j < L; ++j) {
+                    if (!orc_allowed(p, j, causal, wl, wr)) continue; /* p = 0 exactly */
+                    for (int64_t d = 0; d < D; ++d) orow[d] += prow[j] * V[j * D + d];
+                }
+                *lrow = m + log(l);
+            }
+            free(Q); free(K); free(V); free(P);
+        }
+    }
+    return 0;
+}

@@ -1,7 +1,7 @@
 """Plants plausible mistakes in copies of the CPU oracle (on the CPU only) and
 checks that the pins in test_oracle_pins.py, test_oracle_bwd_pins.py,
-test_oracle_blocksparse_pins.py and test_oracle_paged_pins.py catch every one of
-them."""
+test_oracle_blocksparse_pins.py, test_oracle_paged_pins.py and
+test_oracle_kvcache_pins.py catch every one of them."""
 import os
 import subprocess
 import sys
@@ -48,6 +48,15 @@ MUTANTS = {
                           "const int64_t src_row = page * page_size + j / page_size;"),
     "paged_table_stride": ("const int64_t page = block_table[b * table_stride + j / page_size];",
                            "const int64_t page = block_table[b * (S + page_size - 1) / page_size + j / page_size];"),
+    # KV-cache forward
+    "kv_top_left_alignment": ("const int64_t p = L - S_q + r; /* the query's position in its sequence */",
+                              "const int64_t p = r; /* the query's position in its sequence */"),
+    "kv_position_off_by_one": ("const int64_t p = L - S_q + r; /* the query's position in its sequence */",
+                               "const int64_t p = L - S_q + r + 1; /* the query's position in its sequence */"),
+    "kv_cache_stride": ("K[j * D + d] = orc_load(k, dtype, ((b * S_k + j) * H + h) * D + d);",
+                        "K[j * D + d] = orc_load(k, dtype, ((b * S_q + j) * H + h) * D + d);"),
+    "kv_mask_on_row_index": ("if (!orc_allowed(p, j, causal, wl, wr)) {\n                        prow[j] = -INFINITY;",
+                             "if (!orc_allowed(r, j, causal, wl, wr)) {\n                        prow[j] = -INFINITY;"),
     "bs_only_in_scores": ("!orc_block_on(bmask, i, j, block_m, block_n, n_kb))\n                continue;",
                           "0)\n                continue;"),
 }
@@ -68,6 +77,7 @@ def test_pins_catch_mutant(name, tmp_path):
                         os.path.join(ROOT, "tests", "test_oracle_pins.py"),
                         os.path.join(ROOT, "tests", "test_oracle_bwd_pins.py"),
                         os.path.join(ROOT, "tests", "test_oracle_blocksparse_pins.py"),
-                        os.path.join(ROOT, "tests", "test_oracle_paged_pins.py")],
+                        os.path.join(ROOT, "tests", "test_oracle_paged_pins.py"),
+                        os.path.join(ROOT, "tests", "test_oracle_kvcache_pins.py")],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
