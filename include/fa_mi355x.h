@@ -22,8 +22,10 @@
  * kept on chip ([CG] 项目核心价值; [AN] section 2) -- reaches this exact result
  * up to floating-point rounding.
  *
- * Every function is thread-safe and re-entrant.  The library keeps no state
- * and allocates no memory.
+ * The library allocates no memory.  Its one piece of state is the static
+ * device buffer of fa_fwd_splitkv_noalloc (with that buffer's address per
+ * GPU, looked up once); every other function is stateless, thread-safe and
+ * re-entrant.
  */
 #ifndef FA_MI355X_H
 #define FA_MI355X_H
@@ -58,9 +60,11 @@ typedef enum {
     FA_ERR_BLOCKMASK = -12, /* fa_fwd_blocksparse: block_m not a positive multiple of 128,
                                block_n not a positive multiple of 64, or n_mask not 1, H
                                or B*H */
-    FA_ERR_PAGES = -13    /* fa_fwd_paged: page_size not a positive multiple of 64,
+    FA_ERR_PAGES = -13,   /* fa_fwd_paged: page_size not a positive multiple of 64,
                              num_pages < 1, table_stride < ceil(S / page_size), or a
                              pool / table size outside the index ranges */
+    FA_ERR_SCRATCH = -14  /* fa_fwd_splitkv_noalloc: the partials need more than
+                             FA_NOALLOC_SCRATCH_BYTES */
 } fa_status_t;
 
 /* The most K/V parts per Q tile fa_fwd_splitkv takes. */
@@ -340,6 +344,33 @@ int fa_fwd_paged(const void* q, const void* k_pages, const void* v_pages,
                  int64_t window_right, int dtype, int64_t num_pages, int64_t page_size,
                  int64_t table_stride, int64_t n_splits, void* workspace,
                  int64_t workspace_bytes, void* stream);
+
+/* Bytes of the static device buffer fa_fwd_splitkv_noalloc keeps its split
+ * partials in (one copy per GPU, held until the process ends). */
+#define FA_NOALLOC_SCRATCH_BYTES (128LL << 20)
+
+/*
+ * fa_fwd_splitkv_noalloc -- fa_fwd_splitkv for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation.  It computes exactly what fa_fwd_splitkv
+ * computes, with the same kernels, but keeps the fp32 partial O and LSE in a
+ * static device buffer of the library (FA_NOALLOC_SCRATCH_BYTES, one per GPU)
+ * instead of a workspace argument.  It calls no allocator.  The first call on
+ * a GPU looks the buffer's address up (hipGetSymbolAddress) and keeps it.
+ *
+ * Arguments and results as fa_fwd_splitkv without workspace and
+ * workspace_bytes; the launch runs on `stream`'s device (the current device
+ * for NULL).  Returns FA_ERR_SCRATCH, before any launch, when the partials
+ * (fa_fwd_splitkv_workspace_size bytes) exceed FA_NOALLOC_SCRATCH_BYTES.
+ * Every call on one GPU uses the same buffer: calls that overlap in time on
+ * one GPU (other streams, other host threads) race and must be serialised
+ * by the caller.  Nothing in the buffer needs to start at zero -- every
+ * partial the merge reads is written by the same call.
+ */
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* out, float* lse,
+                           int64_t B, int64_t H, int64_t S, int64_t D, float scale, int causal,
+                           int64_t window_left, int64_t window_right, int dtype,
+                           int64_t n_splits, void* stream);
 
 #ifdef __cplusplus
 }

@@ -6,6 +6,7 @@
 #include <cfloat>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "fa_launch.h"
 #include "fa_mi355x.h"
@@ -77,6 +78,9 @@ FA_API const char* fa_status_string(int status) {
     case FA_ERR_PAGES:
         return "page_size must be a positive multiple of 64, num_pages >= 1, the block table as "
                "wide as ceil(S / page_size), and the pools must fit the index ranges";
+    case FA_ERR_SCRATCH:
+        return "the split partials need more than the library's static scratch buffer "
+               "(FA_NOALLOC_SCRATCH_BYTES); use fa_fwd_splitkv with a workspace";
     default: return "unknown status";
     }
 }
@@ -498,6 +502,95 @@ FA_API int fa_fwd_paged(const void* q, const void* k_pages, const void* v_pages,
         a.n_splits = (int)n_splits;
         a.part_o = (float*)workspace;
         a.part_lse = (float*)workspace + n_splits * rows * D;
+    }
+    const hipError_t e = fa::launch_fwd(a);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+// ---------------------------------------------------------------- no allocation
+// fa_fwd_splitkv_noalloc keeps the split partials in this file-scope device
+// array instead of a caller's workspace.  In host code `scratch` names a
+// host-side stand-in, not device memory: its device address is taken once per
+// device with hipGetSymbolAddress and only that address is used afterwards.
+// Every call on a device shares that device's copy; the split kernel writes
+// every partial the merge reads (empty parts included), so nothing needs
+// clearing between calls, and calls that overlap on one device race.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The device address of `scratch` on device `dev`, looked up (with that device
+// current) the first time and kept.  FA_OK or FA_ERR_HIP.
+int scratch_address(int dev, void** ptr) {
+    if (dev < 0 || dev >= kMaxScratchDevices) return FA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) {
+            (void)hipGetLastError();
+            return FA_ERR_HIP;
+        }
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return FA_ERR_HIP;
+        }
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) (void)hipSetDevice(cur);
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return FA_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return FA_OK;
+}
+
+}  // namespace
+
+FA_API int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* out,
+                                  float* lse, int64_t B, int64_t H, int64_t S, int64_t D,
+                                  float scale, int causal, int64_t window_left,
+                                  int64_t window_right, int dtype, int64_t n_splits,
+                                  void* stream) {
+    int rc = fa_fwd_check_args(q, k, v, out, lse, B, H, S, D, scale, causal, window_left,
+                               window_right, dtype);
+    if (rc != FA_OK) return rc;
+    int64_t need = 0;
+    rc = fa_fwd_splitkv_workspace_size(B, H, S, D, dtype, n_splits, &need);
+    if (rc != FA_OK) return rc;
+    if (need > (int64_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+    fa::LaunchArgs a = make_args(q, k, v, out, lse, B, H, S, D, scale, causal, window_left,
+                                 window_right, dtype, stream);
+    if (need > 0) {
+        const int64_t bm = fa::q_tile_rows(dtype, D, S, a.wl, a.wr);
+        int64_t n_wg;
+        if (!mul_ok(B * H, (S + bm - 1) / bm, &n_wg) || !mul_ok(n_wg, n_splits, &n_wg) ||
+            n_wg > (int64_t)(UINT32_MAX / 256))
+            return FA_ERR_SHAPE;
+        // the device the launch runs on: the stream's, or the current one
+        int dev = -1;
+        if (stream) {
+            if (hipStreamGetDevice((hipStream_t)stream, &dev) != hipSuccess) {
+                (void)hipGetLastError();
+                return FA_ERR_HIP;
+            }
+        } else if (hipGetDevice(&dev) != hipSuccess) {
+            (void)hipGetLastError();
+            return FA_ERR_HIP;
+        }
+        void* base = nullptr;
+        rc = scratch_address(dev, &base);
+        if (rc != FA_OK) return rc;
+        const int64_t rows = B * H * S;
+        a.n_splits = (int)n_splits;
+        a.part_o = (float*)base;
+        a.part_lse = (float*)base + n_splits * rows * D;
     }
     const hipError_t e = fa::launch_fwd(a);
     return e == hipSuccess ? FA_OK : FA_ERR_HIP;

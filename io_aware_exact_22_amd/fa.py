@@ -23,6 +23,8 @@ FA_DTYPE_FP32 = 0
 FA_DTYPE_FP16 = 1
 FA_DTYPE_BF16 = 2
 FA_MAX_SPLITS = 16
+FA_NOALLOC_SCRATCH_BYTES = 128 << 20
+FA_ERR_SCRATCH = -14
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libfa_mi355x.so")
@@ -95,6 +97,9 @@ def _load():
         lib.fa_fwd_paged.restype = cint
         lib.fa_bwd_workspace_size.argtypes = [i64, i64, i64, i64, cint, p64]
         lib.fa_bwd_workspace_size.restype = cint
+        lib.fa_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                               ctypes.c_float, cint, i64, i64, cint, i64, vp]
+        lib.fa_fwd_splitkv_noalloc.restype = cint
         _lib = lib
         return lib
 
@@ -235,6 +240,16 @@ def fa_fwd_paged(q: int, k_pages: int, v_pages: int, block_table: int, out: int,
     return _load().fa_fwd_paged(q, k_pages, v_pages, block_table, out, lse, B, H, S, D, scale,
                                 causal, window_left, window_right, dtype, num_pages, page_size,
                                 table_stride, n_splits, workspace, workspace_bytes, stream)
+
+
+def fa_fwd_splitkv_noalloc(q: int, k: int, v: int, out: int, lse: int, B: int, H: int, S: int,
+                           D: int, scale: float, causal: int, window_left: int, window_right: int,
+                           dtype: int, n_splits: int, stream: int | None) -> int:
+    """The split-KV C entry point that keeps its partials in the library's static
+    device buffer (no workspace, no allocation); raw device pointers; returns
+    the status."""
+    return _load().fa_fwd_splitkv_noalloc(q, k, v, out, lse, B, H, S, D, scale, causal,
+                                          window_left, window_right, dtype, n_splits, stream)
 
 
 # ------------------------------------------------------------------ tensor call

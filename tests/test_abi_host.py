@@ -29,7 +29,8 @@ def test_library_exports_every_declared_symbol():
                           "fa_fwd_splitkv",
                           "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv_auto_splits",
                           "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_blocksparse",
-                          "fa_fwd_blocksparse_workspace_size", "fa_fwd_paged"}
+                          "fa_fwd_blocksparse_workspace_size", "fa_fwd_paged",
+                          "fa_fwd_splitkv_noalloc"}
     lib = ctypes.CDLL(fa.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for st in range(0, -14, -1):
+    for st in range(0, -15, -1):
         s = fa.fa_status_string(st)
         assert s and s != "unknown status"
     assert fa.fa_status_string(-99) == "unknown status"
