@@ -312,6 +312,112 @@ def cpu_baseline_blocksparse(w, q, k, v, mask, bm, bn, target_s: float = 15.0):
     }
 
 
+METRIC_KV = ("attention decode against a KV cache: HBM GB/s (K and V read once, q/O/LSE) and % "
+             "of MI355X 8 TB/s")
+
+
+def bench_kvcache(args, name: str) -> int:
+    """fa_fwd_kvcache on a decoding workload (one new query per sequence
+    against a long cache), timed like the forward: a 512 MiB flush before
+    every launch outside its HIP events; the rate is algorithmic bytes per
+    launch over the median (value) and mean (roofline) cold launch."""
+    import numpy as np
+    import torch
+
+    import io_aware_exact_22_amd as fa
+    from fa_inputs import WORKLOADS_KV, kv_workload_inputs
+
+    w = WORKLOADS_KV[name]
+    dev = torch.device("cuda:0")
+    q, k, v = kv_workload_inputs(w)
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    lens = torch.full((w.B,), w.S_k, dtype=torch.int32, device=dev)
+    out = torch.empty_like(qd)
+    lse = torch.empty((w.B, w.H, w.S_q), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    dcode = fa.FA_DTYPE_BF16 if w.dtype == torch.bfloat16 else fa.FA_DTYPE_FP16
+    ns = args.splitkv if args.splitkv > 0 else fa.fa_fwd_kvcache_auto_splits(
+        w.B, w.H, w.S_q, w.S_k, w.D, dcode)
+    need = fa.fa_fwd_kvcache_workspace_size(w.B, w.H, w.S_q, w.D, dcode, ns)
+    ws = torch.empty(max(1, need // 4), dtype=torch.float32, device=dev)
+
+    def step():
+        fa.flash_attn_fwd_kvcache(qd, kd, vd, lens, softmax_scale=w.scale, causal=True,
+                                  n_splits=ns, out=out, lse=lse, workspace=ws, stream=stream)
+
+    flush = torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev) \
+        if args.flush_mib > 0 else None
+
+    def launch(events=None):
+        if flush is not None:
+            flush.fill_(1.0)
+        if events is not None:
+            events[0].record(stream)
+        step()
+        if events is not None:
+            events[1].record(stream)
+
+    for _ in range(args.warmup):
+        launch()
+    torch.cuda.synchronize(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    for e in ev:
+        launch(e)
+    torch.cuda.synchronize(dev)
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    del flush
+    if not (bool(torch.isfinite(out.float()).all()) and bool(torch.isfinite(lse).all())):
+        print("bench.py: non-finite output", file=sys.stderr)
+        return 1
+    esz = 2
+    kv_bytes = 2 * w.B * w.S_k * w.H * w.D * esz
+    alg_bytes = kv_bytes + 2 * w.B * w.S_q * w.H * w.D * esz + 4 * w.B * w.H * w.S_q
+    flops = 4.0 * w.B * w.H * w.S_q * w.S_k * w.D
+    med, mean = float(np.median(ms)), float(np.mean(ms))
+    gbs = alg_bytes / (med * 1e-3) / 1e9
+    ach = alg_bytes / (mean * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC_KV, "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": med, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if w.dtype == torch.bfloat16 else "fp16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "S_q": w.S_q, "S_k": w.S_k, "D": w.D,
+                   "causal": True, "cache_seqlens": "all S_k", "n_splits": ns,
+                   "entry": "fa_fwd_kvcache", "parallelism": "single GPU",
+                   "flops_per_step": flops},
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": ach / PEAK_HBM_GBS, "traffic": None, "kernel_ms": mean,
+                     "kernel_ms_median": med, "kernel_ms_min": float(np.min(ms)),
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "timing": f"{args.steps} launches, each preceded outside its HIP events by a "
+                               f"{args.flush_mib} MiB write that evicts L2 and the MALL"},
+    }
+    if args.no_cpu_baseline:
+        rec["cpu_baseline"] = None
+    else:
+        import oracle
+
+        threads = cpu_threads()
+        t0 = time.perf_counter()
+        nb = 0
+        for b in range(w.B):  # whole sequences until about 10 s
+            oracle.fwd_kvcache(q[b:b + 1].contiguous(), k[b:b + 1].contiguous(),
+                               v[b:b + 1].contiguous(), [w.S_k], w.scale, True, nthreads=threads)
+            nb += 1
+            if time.perf_counter() - t0 > 10.0:
+                break
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {
+            "value": alg_bytes * nb / w.B / dt / 1e9, "unit": "GB/s", "cores": threads,
+            "affinity_cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{w.name}: {nb} of {w.B} sequences in full (all heads), fp64 oracle, "
+                      f"{dt:.1f} s on {threads} threads; rate on the same byte count"}
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -342,6 +448,10 @@ def main() -> int:
     ap.add_argument("--warm-steps", type=int, default=50,
                     help="after the timed region, this many warm back-to-back launches, reported "
                          "as roofline.warm (0 = skip)")
+    ap.add_argument("--kvcache", default="",
+                    help="time fa_fwd_kvcache on this decoding workload (decode_16k, decode_32k) "
+                         "instead of fa_fwd; --splitkv N sets the part count (default: the "
+                         "library's choice)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the benchmark, run --steps plain device copies of this many "
                          "MiB (the reference kernel for scaling HBM byte counters)")
@@ -360,6 +470,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
+    if args.kvcache:
+        return bench_kvcache(args, args.kvcache)
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")

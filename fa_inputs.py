@@ -63,6 +63,45 @@ WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class KvWorkload:
+    """Decoding against a key/value cache: S_q new queries per sequence, a
+    cache of S_k rows (all of them holding keys unless a test says otherwise)."""
+    name: str
+    B: int
+    H: int
+    S_q: int
+    S_k: int
+    D: int
+    dtype: torch.dtype
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    def describe(self) -> str:
+        dt = {torch.float16: "fp16", torch.bfloat16: "bf16"}[self.dtype]
+        return f"B{self.B} H{self.H} S_q{self.S_q} S_k{self.S_k} D{self.D} {dt} causal"
+
+
+# One new token per sequence against a long cache: the inference step FlashDecoding
+# serves (FlashAttention技术解析 page, section 5), at the 16K and 32K lengths of
+# the forward workloads.  Batch and heads are not stated on the pages.
+WORKLOADS_KV = {
+    "decode_16k": KvWorkload("decode_16k", 8, 16, 1, 16384, 128, torch.bfloat16, 9),
+    "decode_32k": KvWorkload("decode_32k", 4, 16, 1, 32768, 128, torch.bfloat16, 10),
+}
+
+
+def kv_workload_inputs(w: KvWorkload):
+    """q [B, S_q, H, D] and the caches [B, S_k, H, D]: q from generator seed
+    w.seed, k and v from seed w.seed + 1 (make_qkv's draws)."""
+    q, _, _ = make_qkv(w.B, w.S_q, w.H, w.D, w.dtype, w.seed)
+    _, k, v = make_qkv(w.B, w.S_k, w.H, w.D, w.dtype, w.seed + 1)
+    return q, k, v
+
+
 def make_qkv(B: int, S: int, H: int, D: int, dtype: torch.dtype, seed: int):
     """q, k, v as contiguous CPU tensors [B, S, H, D], drawn in that order from
     one torch CPU generator seeded with ``seed``, fp32 N(0, 1), then cast."""

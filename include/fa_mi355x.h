@@ -56,7 +56,8 @@ typedef enum {
     FA_ERR_HIP = -9,      /* the kernel launch failed (hipGetLastError) */
     FA_ERR_WORKSPACE = -10, /* a workspace argument is NULL, too small, not 16-byte
                                aligned, or overlapping an input or output */
-    FA_ERR_SPLITS = -11,  /* fa_fwd_splitkv: n_splits outside [1, FA_MAX_SPLITS] */
+    FA_ERR_SPLITS = -11,  /* fa_fwd_splitkv: n_splits outside [1, FA_MAX_SPLITS];
+                             fa_fwd_kvcache: outside [1, FA_MAX_KV_SPLITS] */
     FA_ERR_BLOCKMASK = -12, /* fa_fwd_blocksparse: block_m not a positive multiple of 128,
                                block_n not a positive multiple of 64, or n_mask not 1, H
                                or B*H */
@@ -69,6 +70,8 @@ typedef enum {
 
 /* The most K/V parts per Q tile fa_fwd_splitkv takes. */
 #define FA_MAX_SPLITS 16
+/* The most K/V parts per query block fa_fwd_kvcache takes. */
+#define FA_MAX_KV_SPLITS 64
 
 /*
  * fa_fwd -- one fused attention forward over all (b, h).
@@ -344,6 +347,72 @@ int fa_fwd_paged(const void* q, const void* k_pages, const void* v_pages,
                  int64_t window_right, int dtype, int64_t num_pages, int64_t page_size,
                  int64_t table_stride, int64_t n_splits, void* workspace,
                  int64_t workspace_bytes, void* stream);
+
+/*
+ * fa_fwd_kvcache -- attention of S_q new queries per sequence against a
+ * key/value cache, as in decoding (FlashDecoding, the variant of the method
+ * for the KV cache of inference: [FA] section 5; the call
+ * flash_attn_with_kvcache and a paged cache found through a block table:
+ * [CG] sections 总结与最佳实践 and Paged KV Cache支持).  For sequence b the
+ * cache's first L_b = cache_seqlens[b] rows are its keys and values (the new
+ * tokens' own included); its queries are the sequence's last S_q positions,
+ * query i at position p = L_b - S_q + i, and
+ *   allowed(i, j) = j < L_b && (!causal || j <= p) && (wl < 0 || p - j <= wl)
+ *                                                 && (wr < 0 || j - p <= wr)
+ *   O[b,i,h,:]   = sum_j softmax_j(scale * q_i . k_j over allowed j) * v[b,j,h,:]
+ *   LSE[b,h,i]   = ln sum_{allowed j} exp(scale * q_i . k_j)
+ * A row with no allowed key (p < 0 under the causal mask, or L_b = 0) gets
+ * O = 0 and LSE = -inf.  With S_q = L_b = S_k this is fa_fwd.  Cache rows past
+ * L_b are never read.  The K/V tiles of each query block may be cut into
+ * n_splits parts processed at the same time and merged in the log domain as
+ * in fa_fwd_splitkv -- the usual case for decoding, where B * H query blocks
+ * of one row each cannot fill the device.
+ *
+ * q, out      device, contiguous [B, S_q, H, D] of `dtype` (bf16 or fp16).
+ * lse         device, contiguous fp32 [B, H, S_q].
+ * k_cache, v_cache  device, read only: contiguous [B, S_k, H, D] caches when
+ *             block_table is NULL, else page pools [num_pages, page_size, H, D]
+ *             (key j of sequence b: row j % page_size of page
+ *             block_table[b * table_stride + j / page_size]; a page index
+ *             outside [0, num_pages) reads as zeros).
+ * cache_seqlens  device int32 [B]: L_b, clamped to [0, S_k] by the kernel (the
+ *             host cannot read it without a synchronisation).
+ * block_table device int32 [B, table_stride] or NULL (contiguous caches).
+ * S_q, S_k    queries per sequence (>= 1), cache capacity in rows (>= 1).
+ * num_pages, page_size, table_stride  as fa_fwd_paged (ignored without a table).
+ * n_splits    parts per query block, 1 .. FA_MAX_KV_SPLITS.
+ * workspace, workspace_bytes  as fa_fwd_splitkv: at least
+ *             fa_fwd_kvcache_workspace_size bytes, 16-byte aligned, caller-owned;
+ *             may be NULL when that size is 0.
+ * Other arguments as fa_fwd; window_left >= S_k and window_right >= S_q are
+ * unbounded.  fp32 is FA_ERR_DTYPE.  Validation happens before any HIP call
+ * (pointer alignment: tensors 16 bytes, lse / seqlens / table 4 bytes;
+ * out and lse must not overlap any input or each other).  Enqueues one kernel
+ * on `stream` (two with a split) and returns without synchronising.  Returns
+ * FA_OK or a negative fa_status_t.
+ */
+int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* cache_seqlens, const int32_t* block_table, void* out, float* lse,
+                   int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D, float scale,
+                   int causal, int64_t window_left, int64_t window_right, int dtype,
+                   int64_t num_pages, int64_t page_size, int64_t table_stride, int64_t n_splits,
+                   void* workspace, int64_t workspace_bytes, void* stream);
+
+/* fa_fwd_kvcache_workspace_size -- the workspace fa_fwd_kvcache needs, in
+ * *bytes: n_splits * B * H * S_q * (D + 1) * 4, or 0 for one part.  Pure
+ * function.  Returns FA_OK, FA_ERR_NULL, FA_ERR_SPLITS, FA_ERR_DTYPE (fp32) or
+ * the shape / head-dimension status of fa_fwd_check_args. */
+int fa_fwd_kvcache_workspace_size(int64_t B, int64_t H, int64_t S_q, int64_t D, int dtype,
+                                  int64_t n_splits, int64_t* bytes);
+
+/* fa_fwd_kvcache_auto_splits -- a part count for fa_fwd_kvcache on the current
+ * device: 1 when B * H * ceil(S_q / 128) query blocks give two workgroups per
+ * compute unit, else enough parts for four per unit, at most
+ * FA_MAX_KV_SPLITS and at most one part per 4 K/V tiles (64 keys each) of a
+ * full cache.  Queries the device, launches nothing.  Returns FA_OK or the
+ * status fa_fwd_kvcache_workspace_size gives. */
+int fa_fwd_kvcache_auto_splits(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D,
+                               int dtype, int64_t* n_splits);
 
 /* Bytes of the static device buffer fa_fwd_splitkv_noalloc keeps its split
  * partials in (one copy per GPU, held until the process ends). */

@@ -72,7 +72,8 @@ FA_API const char* fa_status_string(int status) {
     case FA_ERR_WORKSPACE:
         return "the split-KV workspace is NULL, too small, not 16-byte aligned or overlaps an "
                "input or output";
-    case FA_ERR_SPLITS: return "n_splits must be in [1, FA_MAX_SPLITS]";
+    case FA_ERR_SPLITS:
+        return "n_splits must be in [1, FA_MAX_SPLITS] (fa_fwd_kvcache: [1, FA_MAX_KV_SPLITS])";
     case FA_ERR_BLOCKMASK:
         return "block_m must be a positive multiple of 128, block_n of 64, and n_mask 1, H or B*H";
     case FA_ERR_PAGES:
@@ -499,6 +500,132 @@ FA_API int fa_fwd_paged(const void* q, const void* k_pages, const void* v_pages,
         if (overlaps(workspace, need, out, nbytes) || overlaps(workspace, need, lse, lbytes))
             return FA_ERR_WORKSPACE;
         const int64_t rows = B * H * S;
+        a.n_splits = (int)n_splits;
+        a.part_o = (float*)workspace;
+        a.part_lse = (float*)workspace + n_splits * rows * D;
+    }
+    const hipError_t e = fa::launch_fwd(a);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+// ---------------------------------------------------------------- KV cache
+namespace {
+
+// Bytes of the fp32 partials of a KV-cache launch in n_splits parts (0 for one
+// part), or -1 when the size overflows.
+int64_t kvcache_workspace_bytes(int64_t B, int64_t H, int64_t S_q, int64_t D, int64_t n_splits) {
+    if (n_splits <= 1) return 0;
+    int64_t t, r;
+    if (!mul_ok(B, H, &t) || !mul_ok(t, S_q, &t) || !mul_ok(t, n_splits * (D + 1) * 4, &r))
+        return -1;
+    return r;
+}
+
+// Checks shared by the KV-cache entry points: the query side as fa_fwd, the
+// cache capacity, and the dtypes the KV-cache kernels take (bf16, fp16).
+int check_kvcache_problem(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D, int causal,
+                          int64_t wl, int64_t wr, int dtype, int64_t* q_bytes, int64_t* lse_bytes) {
+    const int rc = check_problem(B, H, S_q, D, causal, wl, wr, dtype, q_bytes, lse_bytes);
+    if (rc != FA_OK) return rc;
+    if (dtype == FA_DTYPE_FP32) return FA_ERR_DTYPE;
+    if (S_k < 1 || S_k > INT32_MAX) return FA_ERR_SHAPE;
+    return FA_OK;
+}
+
+}  // namespace
+
+FA_API int fa_fwd_kvcache_workspace_size(int64_t B, int64_t H, int64_t S_q, int64_t D, int dtype,
+                                         int64_t n_splits, int64_t* bytes) {
+    if (!bytes) return FA_ERR_NULL;
+    int64_t qb, lb;
+    const int rc = check_kvcache_problem(B, H, S_q, 1, D, 0, -1, -1, dtype, &qb, &lb);
+    if (rc != FA_OK) return rc;
+    if (n_splits < 1 || n_splits > FA_MAX_KV_SPLITS) return FA_ERR_SPLITS;
+    const int64_t need = kvcache_workspace_bytes(B, H, S_q, D, n_splits);
+    if (need < 0) return FA_ERR_SHAPE;
+    *bytes = need;
+    return FA_OK;
+}
+
+FA_API int fa_fwd_kvcache_auto_splits(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D,
+                                      int dtype, int64_t* n_splits) {
+    if (!n_splits) return FA_ERR_NULL;
+    int64_t qb, lb;
+    const int rc = check_kvcache_problem(B, H, S_q, S_k, D, 0, -1, -1, dtype, &qb, &lb);
+    if (rc != FA_OK) return rc;
+    *n_splits = fa::kvcache_auto_splits(B, H, S_q, S_k, dtype);
+    return FA_OK;
+}
+
+FA_API int fa_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* cache_seqlens, const int32_t* block_table, void* out,
+                          float* lse, int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D,
+                          float scale, int causal, int64_t window_left, int64_t window_right,
+                          int dtype, int64_t num_pages, int64_t page_size, int64_t table_stride,
+                          int64_t n_splits, void* workspace, int64_t workspace_bytes,
+                          void* stream) {
+    if (!q || !k_cache || !v_cache || !cache_seqlens || !out || !lse) return FA_ERR_NULL;
+    int64_t q_bytes = 0, lse_bytes = 0;
+    int rc = check_kvcache_problem(B, H, S_q, S_k, D, causal, window_left, window_right, dtype,
+                                   &q_bytes, &lse_bytes);
+    if (rc != FA_OK) return rc;
+    if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
+    // the caches: contiguous [B, S_k, H, D], or page pools [num_pages, page_size, H, D]
+    const int64_t row_bytes = H * D * elem_size(dtype);
+    int64_t t, cache_bytes, table_bytes = 0;
+    if (block_table) {
+        if (page_size < 64 || page_size % 64 != 0 || page_size > INT32_MAX || num_pages < 1 ||
+            num_pages > INT32_MAX || table_stride < (S_k + page_size - 1) / page_size ||
+            table_stride > INT32_MAX)
+            return FA_ERR_PAGES;
+        if (!mul_ok(num_pages, page_size, &t) || !mul_ok(t, row_bytes, &cache_bytes) ||
+            !mul_ok(B, table_stride, &t) || !mul_ok(t, 4, &table_bytes))
+            return FA_ERR_PAGES;
+    } else {
+        if (!mul_ok(B, S_k, &t) || !mul_ok(t, row_bytes, &cache_bytes)) return FA_ERR_SHAPE;
+    }
+    if (((uintptr_t)q | (uintptr_t)k_cache | (uintptr_t)v_cache | (uintptr_t)out) & 15u)
+        return FA_ERR_ALIGN;
+    if (((uintptr_t)lse | (uintptr_t)cache_seqlens | (uintptr_t)block_table) & 3u)
+        return FA_ERR_ALIGN;
+    const void* ins[5] = {q, k_cache, v_cache, cache_seqlens, block_table};
+    const int64_t in_bytes[5] = {q_bytes, cache_bytes, cache_bytes, B * 4, table_bytes};
+    for (int i = 0; i < 5; ++i)
+        if (ins[i] && (overlaps(out, q_bytes, ins[i], in_bytes[i]) ||
+                       overlaps(lse, lse_bytes, ins[i], in_bytes[i])))
+            return FA_ERR_ALIAS;
+    if (overlaps(out, q_bytes, lse, lse_bytes)) return FA_ERR_ALIAS;
+    if (n_splits < 1 || n_splits > FA_MAX_KV_SPLITS) return FA_ERR_SPLITS;
+    const int64_t need = kvcache_workspace_bytes(B, H, S_q, D, n_splits);
+    if (need < 0) return FA_ERR_SHAPE;
+    {  // the grid: B * H * ceil(S_q / 128) * n_splits workgroups of 256 threads
+        int64_t n_wg;
+        if (!mul_ok(B * H, (S_q + 127) / 128, &n_wg) || !mul_ok(n_wg, n_splits, &n_wg) ||
+            n_wg > (int64_t)(UINT32_MAX / 256))
+            return FA_ERR_SHAPE;
+    }
+    fa::LaunchArgs a = make_args(q, k_cache, v_cache, out, lse, B, H, S_q, D, scale, causal,
+                                 window_left, window_right, dtype, stream);
+    // a window wider than any position difference is unbounded: a query sees
+    // keys at most S_k - 1 positions before it and S_q - 1 after it
+    a.wl = window_left >= S_k ? -1 : window_left;
+    a.wr = window_right >= S_q ? -1 : window_right;
+    a.kv_lens = cache_seqlens;
+    a.kv_cap = S_k;
+    if (block_table) {
+        a.pg_table = block_table;
+        a.pg_stride = table_stride;
+        a.pg_rows = page_size;
+        a.pg_count = num_pages;
+    }
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 15u))
+            return FA_ERR_WORKSPACE;
+        for (int i = 0; i < 5; ++i)
+            if (ins[i] && overlaps(workspace, need, ins[i], in_bytes[i])) return FA_ERR_WORKSPACE;
+        if (overlaps(workspace, need, out, q_bytes) || overlaps(workspace, need, lse, lse_bytes))
+            return FA_ERR_WORKSPACE;
+        const int64_t rows = B * H * S_q;
         a.n_splits = (int)n_splits;
         a.part_o = (float*)workspace;
         a.part_lse = (float*)workspace + n_splits * rows * D;

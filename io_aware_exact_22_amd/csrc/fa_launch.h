@@ -11,6 +11,11 @@ constexpr int kDtypeFp32 = 0;
 constexpr int kDtypeFp16 = 1;
 constexpr int kDtypeBf16 = 2;
 
+// bf16 / fp16 kernels: 4 waves, 128-row Q tiles, 64-key K/V tiles
+constexpr int kMfmaWaves = 4, kMfmaKeys = 64;
+// the most K/V parts per Q tile a KV-cache launch takes (FA_MAX_KV_SPLITS)
+constexpr int kMaxKvSplits = 64;
+
 struct LaunchArgs {
     const void* q;
     const void* k;
@@ -40,6 +45,13 @@ struct LaunchArgs {
     // is row j % pg_rows of page pg_table[b * pg_stride + j / pg_rows]
     const int* pg_table = nullptr;
     int64_t pg_stride = 0, pg_rows = 0, pg_count = 0;
+    // KV-cache launch (decoding): S is the number of queries per sequence; k
+    // and v are caches of kv_cap rows per sequence ([B, kv_cap, H, D], or page
+    // pools as above), of which sequence b's first kv_lens[b] (device int32
+    // [B], clamped to [0, kv_cap]) are its keys; query row r sits at position
+    // r + kv_lens[b] - S.
+    const int* kv_lens = nullptr;
+    int64_t kv_cap = 0;
 };
 
 // The backward pass: gradients for an output gradient dout (bf16 / fp16).
@@ -68,6 +80,12 @@ hipError_t launch_bwd(const BwdArgs& a);
 // Enqueues the forward kernel (and, for a split launch, the merge kernel) for
 // validated arguments.
 hipError_t launch_fwd(const LaunchArgs& a);
+// The KV-cache forward (a.kv_lens set; bf16 / fp16), split or not.
+hipError_t launch_kvcache(const LaunchArgs& a);
+// The merge of a split launch's partial (O, LSE) into out / lse (bf16 / fp16).
+hipError_t launch_merge_parts(const LaunchArgs& a);
+// K/V parts per Q tile for a KV-cache launch on the current device.
+int kvcache_auto_splits(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int dtype);
 // Bytes of the compacted tile lists a block-sparse launch needs (0 for fp32).
 int64_t blocksparse_lut_bytes(int dtype, int64_t S, int64_t n_mask);
 

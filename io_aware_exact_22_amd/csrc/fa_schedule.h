@@ -61,14 +61,13 @@ __host__ __device__ inline bool tile_fully_masked(const MaskSpec& m, int64_t r0,
     return false;
 }
 
-// K/V tile range [*kt0, *kt1) visited by Q tile qt of height bm.
-__host__ __device__ inline void q_tile_kv_range(const MaskSpec& m, int64_t qt, int64_t bm,
-                                                int64_t bn, int64_t* kt0, int64_t* kt1) {
-    const int64_t r0 = qt * bm;
-    int64_t r1 = r0 + bm - 1;
-    if (r1 > m.S - 1) r1 = m.S - 1;
+// K/V tile range [*kt0, *kt1) holding every allowed key of the query
+// positions [p0, p1] (p1 <= m.S - 1; positions may be negative, see below);
+// empty (0, 0) when they allow no key.
+__host__ __device__ inline void positions_kv_range(const MaskSpec& m, int64_t p0, int64_t p1,
+                                                   int64_t bn, int64_t* kt0, int64_t* kt1) {
     int64_t lo, hi;
-    key_range(m, r0, r1, &lo, &hi);
+    key_range(m, p0, p1, &lo, &hi);
     if (lo > hi) {
         *kt0 = *kt1 = 0;
         return;
@@ -76,6 +75,21 @@ __host__ __device__ inline void q_tile_kv_range(const MaskSpec& m, int64_t qt, i
     *kt0 = lo / bn;
     *kt1 = hi / bn + 1;
 }
+
+// K/V tile range [*kt0, *kt1) visited by Q tile qt of height bm.
+__host__ __device__ inline void q_tile_kv_range(const MaskSpec& m, int64_t qt, int64_t bm,
+                                                int64_t bn, int64_t* kt0, int64_t* kt1) {
+    const int64_t r0 = qt * bm;
+    int64_t r1 = r0 + bm - 1;
+    if (r1 > m.S - 1) r1 = m.S - 1;
+    positions_kv_range(m, r0, r1, bn, kt0, kt1);
+}
+
+// Decoding against a key/value cache: a sequence's S_q queries are the last
+// S_q positions of its L keys, so query row r sits at position r + L - S_q
+// (negative when the cache is shorter than the query block).  With
+// MaskSpec{L, ...} every function above then applies to positions: keys are
+// [0, L), and the last query's position is L - 1 = m.S - 1.
 
 // K/V tiles [*ki0, *ki1) inside [kt0, kt1) where every key is allowed for
 // every row of [r0, r0 + bm - 1] and lies below S: the kernel runs them

@@ -23,6 +23,7 @@ FA_DTYPE_FP32 = 0
 FA_DTYPE_FP16 = 1
 FA_DTYPE_BF16 = 2
 FA_MAX_SPLITS = 16
+FA_MAX_KV_SPLITS = 64
 FA_NOALLOC_SCRATCH_BYTES = 128 << 20
 FA_ERR_SCRATCH = -14
 
@@ -97,6 +98,14 @@ def _load():
         lib.fa_fwd_paged.restype = cint
         lib.fa_bwd_workspace_size.argtypes = [i64, i64, i64, i64, cint, p64]
         lib.fa_bwd_workspace_size.restype = cint
+        lib.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64,
+                                       ctypes.c_float, cint, i64, i64, cint, i64, i64, i64, i64,
+                                       vp, i64, vp]
+        lib.fa_fwd_kvcache.restype = cint
+        lib.fa_fwd_kvcache_workspace_size.argtypes = [i64, i64, i64, i64, cint, i64, p64]
+        lib.fa_fwd_kvcache_workspace_size.restype = cint
+        lib.fa_fwd_kvcache_auto_splits.argtypes = [i64, i64, i64, i64, i64, cint, p64]
+        lib.fa_fwd_kvcache_auto_splits.restype = cint
         lib.fa_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64,
                                                ctypes.c_float, cint, i64, i64, cint, i64, vp]
         lib.fa_fwd_splitkv_noalloc.restype = cint
@@ -240,6 +249,35 @@ def fa_fwd_paged(q: int, k_pages: int, v_pages: int, block_table: int, out: int,
     return _load().fa_fwd_paged(q, k_pages, v_pages, block_table, out, lse, B, H, S, D, scale,
                                 causal, window_left, window_right, dtype, num_pages, page_size,
                                 table_stride, n_splits, workspace, workspace_bytes, stream)
+
+
+def fa_fwd_kvcache(q: int, k_cache: int, v_cache: int, cache_seqlens: int, block_table: int | None,
+                   out: int, lse: int, B: int, H: int, S_q: int, S_k: int, D: int, scale: float,
+                   causal: int, window_left: int, window_right: int, dtype: int, num_pages: int,
+                   page_size: int, table_stride: int, n_splits: int, workspace: int | None,
+                   workspace_bytes: int, stream: int | None) -> int:
+    """The KV-cache C entry point with raw device pointers (ints); returns the status."""
+    return _load().fa_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table, out, lse, B, H,
+                                  S_q, S_k, D, scale, causal, window_left, window_right, dtype,
+                                  num_pages, page_size, table_stride, n_splits, workspace,
+                                  workspace_bytes, stream)
+
+
+def fa_fwd_kvcache_workspace_size(B: int, H: int, S_q: int, D: int, dtype: int,
+                                  n_splits: int) -> int:
+    n = ctypes.c_int64()
+    rc = _load().fa_fwd_kvcache_workspace_size(B, H, S_q, D, dtype, n_splits, ctypes.byref(n))
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_kvcache_workspace_size")
+    return n.value
+
+
+def fa_fwd_kvcache_auto_splits(B: int, H: int, S_q: int, S_k: int, D: int, dtype: int) -> int:
+    n = ctypes.c_int64()
+    rc = _load().fa_fwd_kvcache_auto_splits(B, H, S_q, S_k, D, dtype, ctypes.byref(n))
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_kvcache_auto_splits")
+    return n.value
 
 
 def fa_fwd_splitkv_noalloc(q: int, k: int, v: int, out: int, lse: int, B: int, H: int, S: int,
@@ -512,6 +550,61 @@ def flash_attn_fwd_paged(q, k_pages, v_pages, block_table, softmax_scale: float 
                           block_table.shape[1], n_splits, ws_ptr, ws_bytes, _stream(stream, q))
     if rc != 0:
         raise FaError(rc, "fa_fwd_paged")
+    return out, lse
+
+
+def flash_attn_fwd_kvcache(q, k_cache, v_cache, cache_seqlens, block_table=None,
+                           softmax_scale: float | None = None, causal: bool = False,
+                           window_size=(-1, -1), n_splits: int = 0, out=None, lse=None,
+                           workspace=None, stream=None):
+    """Attention of new queries against a key/value cache (decoding).
+
+    q: GPU tensor [B, S_q, H, D] (bf16 or fp16).  Without ``block_table``,
+    k_cache and v_cache are contiguous [B, S_k, H, D] caches; with it (an
+    int32 [B, n] GPU tensor), they are page pools [num_pages, page_size, H, D]
+    and key j of sequence b is row j % page_size of page block_table[b, j //
+    page_size].  cache_seqlens: int32 GPU tensor [B], the rows of each
+    sequence's cache that hold its keys (the new tokens' own included); query
+    i of sequence b sits at position cache_seqlens[b] - S_q + i.  ``n_splits``
+    parts per query block (0 = the library's choice for the device); the fp32
+    workspace is allocated here when None.  Returns (out [B, S_q, H, D],
+    lse [B, H, S_q] fp32)."""
+    import torch
+
+    _check_q(q)
+    B, S_q, H, D = q.shape
+    paged = block_table is not None
+    if paged:
+        _check_pools(q, k_cache, v_cache)
+        _check_table("block_table", block_table, q, B)
+        num_pages, page_size = k_cache.shape[0], k_cache.shape[1]
+        table_stride = block_table.shape[1]
+        S_k = table_stride * page_size
+    else:
+        if not isinstance(k_cache, torch.Tensor) or k_cache.dim() != 4 or k_cache.shape[0] != B:
+            raise ValueError("k_cache must be a [B, S_k, H, D] tensor")
+        S_k = k_cache.shape[1]
+        _check_like("k_cache", k_cache, q, shape=(B, S_k, H, D))
+        _check_like("v_cache", v_cache, q, shape=(B, S_k, H, D))
+        num_pages = page_size = table_stride = 0
+    _check_like("cache_seqlens", cache_seqlens, q, shape=(B,), dtype=torch.int32)
+    dtype = _dtype_code(q)
+    scale = 1.0 / math.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    wl, wr = (int(x) for x in window_size)
+    with torch.cuda.device(q.device):
+        if n_splits == 0:
+            n_splits = fa_fwd_kvcache_auto_splits(B, H, S_q, S_k, D, dtype)
+        need = fa_fwd_kvcache_workspace_size(B, H, S_q, D, dtype, n_splits)
+    out, lse = _outputs(q, out, lse)
+    ws_ptr, ws_bytes, _ws = _workspace(workspace, need, q, torch.float32, stream)
+    with torch.cuda.device(q.device):
+        rc = fa_fwd_kvcache(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                            cache_seqlens.data_ptr(), block_table.data_ptr() if paged else None,
+                            out.data_ptr(), lse.data_ptr(), B, H, S_q, S_k, D, scale,
+                            int(bool(causal)), wl, wr, dtype, num_pages, page_size, table_stride,
+                            n_splits, ws_ptr, ws_bytes, _stream(stream, q))
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_kvcache")
     return out, lse
 
 

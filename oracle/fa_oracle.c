@@ -650,46 +650,46 @@ int fa_oracle_fwd_kvcache(const void* q, const void* k, const void* v, int dtype
     for (int64_t b = 0; b < B; ++b) {
         const int64_t L = seqlens[b];
         for (int64_t h = 0; h < H; ++h) {
-            double* Q = (double*)malloc(sizeof(double) * (size_t)(S_q * D));
-            double* K = (double*)malloc(sizeof(double) * (size_t)((L > 0 ? L : 1) * D));
-            double* V = (double*)malloc(sizeof(double) * (size_t)((L > 0 ? L : 1) * D));
-            double* P = (double*)malloc(sizeof(double) * (size_t)(S_q * (L > 0 ? L : 1)));
-            if (!Q || !K || !V || !P) {
-                free(Q); free(K); free(V); free(P);
+            double* Qc = (double*)malloc(sizeof(double) * (size_t)(S_q * D));
+            double* Kc = (double*)malloc(sizeof(double) * (size_t)((L > 0 ? L : 1) * D));
+            double* Vc = (double*)malloc(sizeof(double) * (size_t)((L > 0 ? L : 1) * D));
+            double* Pc = (double*)malloc(sizeof(double) * (size_t)(S_q * (L > 0 ? L : 1)));
+            if (!Qc || !Kc || !Vc || !Pc) {
+                free(Qc); free(Kc); free(Vc); free(Pc);
                 return -2;
             }
             for (int64_t r = 0; r < S_q; ++r)
                 for (int64_t d = 0; d < D; ++d)
-                    Q[r * D + d] = orc_load(q, dtype, ((b * S_q + r) * H + h) * D + d);
+                    Qc[r * D + d] = orc_load(q, dtype, ((b * S_q + r) * H + h) * D + d);
             for (int64_t j = 0; j < L; ++j)
                 for (int64_t d = 0; d < D; ++d) {
-                    K[j * D + d] = orc_load(k, dtype, ((b * S_k + j) * H + h) * D + d);
-                    V[j * D + d] = orc_load(v, dtype, ((b * S_k + j) * H + h) * D + d);
+                    Kc[j * D + d] = orc_load(k, dtype, ((b * S_k + j) * H + h) * D + d);
+                    Vc[j * D + d] = orc_load(v, dtype, ((b * S_k + j) * H + h) * D + d);
                 }
 #pragma omp parallel for schedule(dynamic, 4) num_threads(nthreads)
             for (int64_t r = 0; r < S_q; ++r) {
                 const int64_t p = L - S_q + r; /* the query's position in its sequence */
-                double* prow = P + r * (L > 0 ? L : 1);
+                double* srow = Pc + r * (L > 0 ? L : 1);
                 double* orow = out + ((b * S_q + r) * H + h) * D;
                 double* lrow = lse + (b * H + h) * S_q + r;
                 /* 1. scores of the allowed keys; -inf elsewhere */
                 for (int64_t j = 0; j < L; ++j) {
                     if (!orc_allowed(p, j, causal, wl, wr)) {
-                        prow[j] = -INFINITY;
+                        srow[j] = -INFINITY;
                         continue;
                     }
                     double dot = 0.0;
-                    for (int64_t d = 0; d < D; ++d) dot += Q[r * D + d] * K[j * D + d];
-                    prow[j] = scale * dot;
+                    for (int64_t d = 0; d < D; ++d) dot += Qc[r * D + d] * Kc[j * D + d];
+                    srow[j] = scale * dot;
                 }
                 /* 2. row max (a NaN anywhere makes it NaN) */
                 double m = -INFINITY;
                 for (int64_t j = 0; j < L; ++j) {
-                    if (isnan(prow[j])) {
-                        m = prow[j];
+                    if (isnan(srow[j])) {
+                        m = srow[j];
                         break;
                     }
-                    if (prow[j] > m) m = prow[j];
+                    if (srow[j] > m) m = srow[j];
                 }
                 if (m == -INFINITY) { /* no allowed key */
                     for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
@@ -699,19 +699,19 @@ int fa_oracle_fwd_kvcache(const void* q, const void* k, const void* v, int dtype
                 /* 3. softmax */
                 double l = 0.0;
                 for (int64_t j = 0; j < L; ++j) {
-                    prow[j] = exp(prow[j] - m);
-                    l += prow[j];
+                    srow[j] = exp(srow[j] - m);
+                    l += srow[j];
                 }
-                for (int64_t j = 0; j < L; ++j) prow[j] /= l;
+                for (int64_t j = 0; j < L; ++j) srow[j] /= l;
                 /* 4. O = P V over the allowed keys */
                 for (int64_t d = 0; d < D; ++d) orow[d] = 0.0;
                 for (int64_t j = 0; j < L; ++j) {
                     if (!orc_allowed(p, j, causal, wl, wr)) continue; /* p = 0 exactly */
-                    for (int64_t d = 0; d < D; ++d) orow[d] += prow[j] * V[j * D + d];
+                    for (int64_t d = 0; d < D; ++d) orow[d] += srow[j] * Vc[j * D + d];
                 }
                 *lrow = m + log(l);
             }
-            free(Q); free(K); free(V); free(P);
+            free(Qc); free(Kc); free(Vc); free(Pc);
         }
     }
     return 0;

@@ -30,7 +30,8 @@ def test_library_exports_every_declared_symbol():
                           "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv_auto_splits",
                           "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_blocksparse",
                           "fa_fwd_blocksparse_workspace_size", "fa_fwd_paged",
-                          "fa_fwd_splitkv_noalloc"}
+                          "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_size",
+                          "fa_fwd_kvcache_auto_splits", "fa_fwd_splitkv_noalloc"}
     lib = ctypes.CDLL(fa.library_path())
     for n in names:
         assert hasattr(lib, n), n
@@ -417,3 +418,51 @@ def test_bench_refuses_several_gpus():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "8"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+# ---------------------------------------------------------------- KV cache
+KC, VC, SL, KT = 10 << 32, 11 << 32, 12 << 32, 13 << 32  # caches, seqlens, table
+
+
+@pytest.mark.parametrize("B,H,S_q,D,dtype,ns", [(8, 16, 1, 128, fa.FA_DTYPE_BF16, 16),
+                                                  (3, 5, 130, 64, fa.FA_DTYPE_FP16, 64)])
+def test_kvcache_workspace_size(B, H, S_q, D, dtype, ns):
+    """fp32 partial O and LSE of every part: ns * B * H * S_q * (D + 1) * 4
+    bytes; nothing for one part; fp32 inputs are not taken."""
+    assert fa.fa_fwd_kvcache_workspace_size(B, H, S_q, D, dtype, ns) == ns * B * H * S_q * (D + 1) * 4
+    assert fa.fa_fwd_kvcache_workspace_size(B, H, S_q, D, dtype, 1) == 0
+    for bad, st in ((0, -11), (fa.FA_MAX_KV_SPLITS + 1, -11)):
+        with pytest.raises(fa.FaError) as e:
+            fa.fa_fwd_kvcache_workspace_size(B, H, S_q, D, dtype, bad)
+        assert e.value.status == st
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_fwd_kvcache_workspace_size(B, H, S_q, D, fa.FA_DTYPE_FP32, ns)
+    assert e.value.status == -5
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, None),
+    ({"q": 0}, -1), ({"kc": 0}, -1), ({"vc": 0}, -1), ({"sl": 0}, -1), ({"out": 0}, -1),
+    ({"D": 96}, -3), ({"dtype": fa.FA_DTYPE_FP32}, -5), ({"Sk": 0}, -2), ({"Sq": 0}, -2),
+    ({"scale": float("nan")}, -6), ({"window_left": -3}, -4),
+    ({"kc": KC + 8}, -7), ({"sl": SL + 2}, -7), ({"lse": LSE + 2}, -7),
+    ({"out": KC}, -8), ({"lse": SL}, -8), ({"out": VC + 4096}, -8),
+    ({"ns": 0}, -11), ({"ns": 65}, -11),
+    ({"ns": 4, "ws": 0}, -10), ({"ns": 4, "ws": KC}, -10), ({"ns": 4, "wsb": 16}, -10),
+    ({"bt": KT, "ps": 100}, -13), ({"bt": KT, "ps": 64, "ts": 3}, -13), ({"bt": KT, "np": 0}, -13),
+    ({"bt": KT + 2, "ps": 64, "ts": 8}, -7), ({"bt": KT, "ps": 64, "ts": 8, "lse": KT}, -8),
+])
+def test_kvcache_rejects_before_any_hip_call(kw, status):
+    """Invalid arguments return their status without touching the GPU (B = 2,
+    S_q = 3 queries against a 500-row cache; a paged cache of 64-row pages
+    needs 8 table entries)."""
+    if status is None:  # the valid call itself is a GPU test; here only its checks
+        return
+    a = dict(GOOD, kc=KC, vc=VC, sl=SL, bt=0, Sq=3, Sk=500, np=40, ps=0, ts=0, ns=1, ws=WS,
+             wsb=1 << 40)
+    a.update(kw)
+    rc = fa.fa_fwd_kvcache(a["q"], a["kc"], a["vc"], a["sl"] or None, a["bt"] or None, a["out"],
+                           a["lse"], a["B"], a["H"], a["Sq"], a["Sk"], a["D"], a["scale"],
+                           a["causal"], a["window_left"], a["window_right"], a["dtype"], a["np"],
+                           a["ps"], a["ts"], a["ns"], a["ws"] or None, a["wsb"], None)
+    assert rc == status

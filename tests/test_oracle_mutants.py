@@ -53,10 +53,15 @@ MUTANTS = {
                               "const int64_t p = r; /* the query's position in its sequence */"),
     "kv_position_off_by_one": ("const int64_t p = L - S_q + r; /* the query's position in its sequence */",
                                "const int64_t p = L - S_q + r + 1; /* the query's position in its sequence */"),
-    "kv_cache_stride": ("K[j * D + d] = orc_load(k, dtype, ((b * S_k + j) * H + h) * D + d);",
-                        "K[j * D + d] = orc_load(k, dtype, ((b * S_q + j) * H + h) * D + d);"),
-    "kv_mask_on_row_index": ("if (!orc_allowed(p, j, causal, wl, wr)) {\n                        prow[j] = -INFINITY;",
-                             "if (!orc_allowed(r, j, causal, wl, wr)) {\n                        prow[j] = -INFINITY;"),
+    "kv_cache_stride": ("Kc[j * D + d] = orc_load(k, dtype, ((b * S_k + j) * H + h) * D + d);",
+                        "Kc[j * D + d] = orc_load(k, dtype, ((b * S_q + j) * H + h) * D + d);"),
+    "kv_mask_on_row_index": ("if (!orc_allowed(p, j, causal, wl, wr)) {\n                        srow[j] = -INFINITY;",
+                             "if (!orc_allowed(r, j, causal, wl, wr)) {\n                        srow[j] = -INFINITY;"),
+    "kv_scale_dropped": ("srow[j] = scale * dot;", "srow[j] = dot;"),
+    "kv_no_normalisation": ("for (int64_t j = 0; j < L; ++j) srow[j] /= l;",
+                            "for (int64_t j = 0; j < L; ++j) srow[j] /= 1.0;"),
+    "kv_v_row_index": ("orow[d] += srow[j] * Vc[j * D + d];", "orow[d] += srow[j] * Vc[(L - 1 - j) * D + d];"),
+    "kv_lse_without_max": ("*lrow = m + log(l);", "*lrow = log(l);"),
     "bs_only_in_scores": ("!orc_block_on(bmask, i, j, block_m, block_n, n_kb))\n                continue;",
                           "0)\n                continue;"),
 }
