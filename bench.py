@@ -39,7 +39,8 @@ METRIC_BS = ("attention fwd TFLOPS over the pairs a block mask keeps (4·B·H·p
 PEAK_MFMA_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp32": 157.3}  # MI355X dense, 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "causal_16k"
-KERNEL_SOURCES = ["io_aware_exact_22_amd/csrc/fa_fwd_kernels.hip",
+KERNEL_SOURCES = ["io_aware_exact_22_amd/csrc/fa_fwd_device.h",
+                  "io_aware_exact_22_amd/csrc/fa_fwd_kernels.hip",
                   "io_aware_exact_22_amd/csrc/fa_kernel_common.h",
                   "io_aware_exact_22_amd/csrc/fa_schedule.h"]
 
@@ -425,8 +426,10 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-clock", action="store_true",
-                    help="skip the shader-clock sample after the timed steps")
+    ap.add_argument("--clock", action="store_true",
+                    help="after the timed steps, sample the shader clock while about 0.6 s of "
+                         "further launches run back to back (roofline.sclk)")
+    ap.add_argument("--no-clock", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--backward", action="store_true",
                     help="time fa_bwd (the gradients of the forward) instead of fa_fwd; "
                          "bf16 / fp16 workloads")
@@ -445,7 +448,7 @@ def main() -> int:
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="MiB written before every launch, outside the events, to evict L2 and "
                          "the MALL (0 = no flush: warm back-to-back launches are timed)")
-    ap.add_argument("--warm-steps", type=int, default=50,
+    ap.add_argument("--warm-steps", type=int, default=0,
                     help="after the timed region, this many warm back-to-back launches, reported "
                          "as roofline.warm (0 = skip)")
     ap.add_argument("--kvcache", default="",
@@ -629,7 +632,9 @@ def main() -> int:
         torch.cuda.synchronize(dev)
         warm_wall = (time.perf_counter() - tw) * 1e3 / args.warm_steps
         warm_ms = [e0.elapsed_time(e1) for e0, e1 in wev]
-    sclk = None if args.no_clock else sample_sclk(step, stream, float(np.median(launch_ms)))
+    # (off by default: the default command launches only the warm-up and timed
+    # launches, so a kernel trace of it averages exactly what achieved uses)
+    sclk = sample_sclk(step, stream, float(np.median(launch_ms))) if args.clock else None
 
     if bs is not None:
         pairs = blocksparse_pairs(w.S, w.causal, w.window, bs[0][0], 128, 64)
