@@ -6,8 +6,10 @@ all run inside that single kernel launch.  Inputs are synthetic (seeded N(0,1),
 rounded to the workload dtype) and resident in HBM before timing starts.
 
 Timing: every launch is preceded, outside the HIP events that bracket it on
-its stream, by a 512 MiB write that evicts L2 and the 256 MB MALL, so each
-timed launch starts with cold caches (inputs resident in HBM).
+its stream, by a 512 MiB write that evicts L2 and the 256 MB MALL, then a read
+of the same buffer that retires the dirty lines the write left behind (their
+write-back would otherwise land inside the timed launch), so each timed launch
+starts with cold caches (inputs resident in HBM) and a clean MALL.
 
 Prints ONE JSON line:
   value         TFLOPS = 4 * B * H * S * S_eff * D / t, t = the median cold
@@ -319,9 +321,10 @@ METRIC_KV = ("attention decode against a KV cache: HBM GB/s (K and V read once, 
 
 def bench_kvcache(args, name: str) -> int:
     """fa_fwd_kvcache on a decoding workload (one new query per sequence
-    against a long cache), timed like the forward: a 512 MiB flush before
-    every launch outside its HIP events; the rate is algorithmic bytes per
-    launch over the median (value) and mean (roofline) cold launch."""
+    against a long cache), timed like the forward: the 512 MiB flush (write,
+    then read back) before every launch outside its HIP events; the rate is
+    algorithmic bytes per launch over the median (value) and mean (roofline)
+    cold launch."""
     import numpy as np
     import torch
 
@@ -352,6 +355,8 @@ def bench_kvcache(args, name: str) -> int:
     def launch(events=None):
         if flush is not None:
             flush.fill_(1.0)
+            if args.flush_mode == "write-read":
+                flush.sum()
         if events is not None:
             events[0].record(stream)
         step()
@@ -393,7 +398,8 @@ def bench_kvcache(args, name: str) -> int:
                      "kernel_ms_median": med, "kernel_ms_min": float(np.min(ms)),
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "timing": f"{args.steps} launches, each preceded outside its HIP events by a "
-                               f"{args.flush_mib} MiB write that evicts L2 and the MALL"},
+                               f"{args.flush_mib} MiB {args.flush_mode} flush that evicts L2 and "
+                               f"the MALL"},
     }
     if args.no_cpu_baseline:
         rec["cpu_baseline"] = None
@@ -448,6 +454,11 @@ def main() -> int:
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="MiB written before every launch, outside the events, to evict L2 and "
                          "the MALL (0 = no flush: warm back-to-back launches are timed)")
+    ap.add_argument("--flush-mode", choices=["write", "write-read"], default="write-read",
+                    help="the flush before each launch: a write of the buffer followed by a read "
+                         "of it (default: the read retires the dirty lines the write leaves in "
+                         "L2 and the MALL, so that writing them back is not part of the timed "
+                         "launch), or the write alone")
     ap.add_argument("--warm-steps", type=int, default=0,
                     help="after the timed region, this many warm back-to-back launches, reported "
                          "as roofline.warm (0 = skip)")
@@ -587,8 +598,9 @@ def main() -> int:
                               window_size=w.window, out=out, lse=lse, stream=stream)
 
     # Timing protocol: before every launch (warm-up and timed alike) a 512 MiB
-    # write evicts L2 and the 256 MB MALL, outside the HIP events; the events
-    # on the launch's stream bracket the launch alone.  value and the
+    # write evicts L2 and the 256 MB MALL and a read of the same buffer retires
+    # the dirty lines it left, outside the HIP events; the events on the
+    # launch's stream bracket the launch alone.  value and the
     # roofline use these cold launches (median and mean); inputs stay
     # resident in HBM throughout.
     flush = torch.empty(args.flush_mib << 18, dtype=torch.float32, device=dev) \
@@ -597,6 +609,8 @@ def main() -> int:
     def timed_launch(events=None):
         if flush is not None:
             flush.fill_(1.0)
+            if args.flush_mode == "write-read":
+                flush.sum()  # reads every line back; the scalar stays on the device
         if events is not None:
             events[0].record(stream)
         step()
@@ -669,7 +683,8 @@ def main() -> int:
     roof["kernel_ms_median"] = float(np.median(launch_ms))
     roof["kernel_ms_min"] = float(np.min(launch_ms))
     roof["timing"] = (f"{args.steps} launches on the launch's stream, each preceded outside the "
-                      f"HIP events by a {args.flush_mib} MiB write that evicts L2 and the MALL "
+                      f"HIP events by a {args.flush_mib} MiB {args.flush_mode} flush that evicts "
+                      f"L2 and the MALL "
                       f"({args.warmup} warm-up launches likewise); achieved uses the mean, value "
                       f"the median" if args.flush_mib > 0 else
                       f"{args.steps} back-to-back launches (no cache flush)")
