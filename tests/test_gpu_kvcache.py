@@ -100,13 +100,15 @@ def test_kvcache_full_cache_is_fa_fwd_bitwise(dtype, D, causal, window):
     assert torch.equal(lse, rl.cpu())
 
 
+@pytest.mark.parametrize("S_q", [1, 4])
 @pytest.mark.parametrize("n_splits", [1, 4])
 @pytest.mark.parametrize("page_size", [64, 128])
-def test_kvcache_paged(n_splits, page_size):
+def test_kvcache_paged(n_splits, page_size, S_q):
     """Page pools with pages at a seeded permutation of slots and NaN in every
     row no sequence uses: equal to the contiguous cache's result bit for bit,
-    and to the oracle."""
-    B, S_q, S_k, H, D, dtype = 3, 4, 640, 2, 128, torch.bfloat16
+    and to the oracle (one query per sequence runs the vector-ALU decoding
+    kernel, four the MFMA kernel)."""
+    B, S_k, H, D, dtype = 3, 640, 2, 128, torch.bfloat16
     q, k, v = case(B, S_q, S_k, H, D, dtype, 300)
     lens = [1, 333, 640]
     n_pg = S_k // page_size
@@ -142,6 +144,29 @@ def test_kvcache_lengths_are_clamped():
     out, lse, scale = run(q, k, v, [-7, S_k + 50], True, (-1, -1), 2)
     ref_o, ref_l = oracle.fwd_kvcache(q, k, v, [0, S_k], scale, True)
     compare(out, lse, ref_o, ref_l, dtype, "kvcache clamped lengths")
+
+
+@pytest.mark.parametrize("dtype,D", [(torch.bfloat16, 128), (torch.float16, 64)])
+@pytest.mark.parametrize("n_splits", [1, 3])
+def test_kvcache_decode_nonfinite_outside_the_window(dtype, D, n_splits):
+    """One query per sequence: NaN in cached keys and values left of a
+    window and in stale rows past the length never reach O; an infinity at an
+    allowed key does, as in the oracle."""
+    B, S_q, S_k, H = 2, 1, 400, 2
+    q, k, v = case(B, S_q, S_k, H, D, dtype, 700)
+    lens = [333, 400]
+    wl = 100
+    for b, L in enumerate(lens):
+        k[b, L - 1 - wl - 5, 0, 1] = float("nan")   # left of the window
+        v[b, L - 1 - wl - 1, 1, 2] = float("nan")
+        if L < S_k:
+            k[b, L:, :, 3] = float("nan")           # stale rows past the length
+            v[b, L:, :, 4] = float("nan")
+    v[1, 399, 0, 7] = float("inf")                   # allowed: the query's own key
+    out, lse, scale = run(q, k, v, lens, True, (wl, -1), n_splits)
+    ref_o, ref_l = oracle.fwd_kvcache(q, k, v, lens, scale, True, (wl, -1))
+    assert np.isinf(ref_o).sum() == 1 and not np.isnan(ref_o).any()
+    compare(out, lse, ref_o, ref_l, dtype, f"decode nonfinite {dtype} D{D} x{n_splits}")
 
 
 def test_kvcache_nonfinite_values_outside_the_mask():
