@@ -43,6 +43,7 @@ PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "causal_16k"
 KERNEL_SOURCES = ["io_aware_exact_22_amd/csrc/fa_fwd_device.h",
                   "io_aware_exact_22_amd/csrc/fa_fwd_kernels.hip",
+                  "io_aware_exact_22_amd/csrc/fa_fwd_launch_cfg.h",
                   "io_aware_exact_22_amd/csrc/fa_kernel_common.h",
                   "io_aware_exact_22_amd/csrc/fa_schedule.h"]
 

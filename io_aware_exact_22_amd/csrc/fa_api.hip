@@ -26,14 +26,21 @@ bool overlaps(const void* p, int64_t n, const void* q, int64_t m) {
 
 int64_t elem_size(int dtype) { return dtype == fa::kDtypeFp32 ? 4 : 2; }
 
-// Shape / window / dtype checks shared by fa_fwd_check_args and
-// fa_fwd_tile_schedule; *tensor_bytes and *lse_bytes are set on success.
+// Shape / window / dtype checks shared by the entry points; *tensor_bytes and
+// *lse_bytes are set on success.  Head dimensions: the bf16 / fp16 forward
+// kernels take any multiple of 16 from 16 to 128 (below 64 or between 64 and
+// 128 they run the next kernel up with zero columns); fp32 inputs and the
+// fixed_d callers (the backward, the KV-cache forward) take 64 or 128.
 int check_problem(int64_t B, int64_t H, int64_t S, int64_t D, int causal, int64_t wl, int64_t wr,
-                  int dtype, int64_t* tensor_bytes, int64_t* lse_bytes) {
+                  int dtype, int64_t* tensor_bytes, int64_t* lse_bytes, bool fixed_d = false) {
     if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16)
         return FA_ERR_DTYPE;
     if (B < 1 || H < 1 || S < 1) return FA_ERR_SHAPE;
-    if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+    if (fixed_d || dtype == FA_DTYPE_FP32) {
+        if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
+    } else if (D < 16 || D > 128 || D % 16 != 0) {
+        return FA_ERR_HEAD_DIM;
+    }
     if ((causal != 0 && causal != 1) || wl < -1 || wr < -1) return FA_ERR_WINDOW;
     // the kernels index rows with 32-bit S, B, H and launch B*H*ceil(S/128)
     // workgroups of 256 threads (grid limit: 2^32 - 1 work-items)
@@ -62,7 +69,9 @@ FA_API const char* fa_status_string(int status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "B, H and S must be >= 1 and the sizes must fit the index ranges";
-    case FA_ERR_HEAD_DIM: return "unsupported head dimension D (supported: 64, 128)";
+    case FA_ERR_HEAD_DIM:
+        return "unsupported head dimension D (bf16 / fp16 forward: a multiple of 16 from 16 to 128; "
+               "fp32 inputs, fa_bwd and fa_fwd_kvcache: 64 or 128)";
     case FA_ERR_WINDOW: return "causal must be 0 or 1 and window bounds must be >= -1";
     case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_FP32, FA_DTYPE_FP16 or FA_DTYPE_BF16";
     case FA_ERR_SCALE: return "scale must be finite and >= 0";
@@ -317,7 +326,7 @@ FA_API int fa_bwd_workspace_size(int64_t B, int64_t H, int64_t S, int64_t D, int
                                  int64_t* bytes) {
     if (!bytes) return FA_ERR_NULL;
     int64_t nbytes, lbytes;
-    const int rc = check_problem(B, H, S, D, 0, -1, -1, dtype, &nbytes, &lbytes);
+    const int rc = check_problem(B, H, S, D, 0, -1, -1, dtype, &nbytes, &lbytes, true);
     if (rc != FA_OK) return rc;
     if (dtype == FA_DTYPE_FP32) return FA_ERR_DTYPE;
     *bytes = lbytes;  // fp32 [B, H, S], the size of lse
@@ -330,7 +339,8 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* out, 
                   int dtype, void* workspace, int64_t workspace_bytes, void* stream) {
     if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
     int64_t nbytes = 0, lbytes = 0;
-    int rc = check_problem(B, H, S, D, causal, window_left, window_right, dtype, &nbytes, &lbytes);
+    int rc = check_problem(B, H, S, D, causal, window_left, window_right, dtype, &nbytes, &lbytes,
+                           true);
     if (rc != FA_OK) return rc;
     if (dtype == FA_DTYPE_FP32) return FA_ERR_DTYPE;
     if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
@@ -525,7 +535,7 @@ int64_t kvcache_workspace_bytes(int64_t B, int64_t H, int64_t S_q, int64_t D, in
 // cache capacity, and the dtypes the KV-cache kernels take (bf16, fp16).
 int check_kvcache_problem(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D, int causal,
                           int64_t wl, int64_t wr, int dtype, int64_t* q_bytes, int64_t* lse_bytes) {
-    const int rc = check_problem(B, H, S_q, D, causal, wl, wr, dtype, q_bytes, lse_bytes);
+    const int rc = check_problem(B, H, S_q, D, causal, wl, wr, dtype, q_bytes, lse_bytes, true);
     if (rc != FA_OK) return rc;
     if (dtype == FA_DTYPE_FP32) return FA_ERR_DTYPE;
     if (S_k < 1 || S_k > INT32_MAX) return FA_ERR_SHAPE;

@@ -111,12 +111,14 @@ template <> __device__ inline void load8<float>(const float* p, float (&x)[8]) {
 // gives position pos's first key, the row of that key in the K/V tensors (or
 // pools) counted from k_head / v_head, and whether the tile lies inside them
 // (a tile outside reads as zeros, as the tile loads make it).  Every loop
-// bound is wave-uniform, so the half exchange sees all 64 lanes.
-template <typename T, int D, int BN, typename TileOf, typename Allowed>
+// bound is wave-uniform, so the half exchange sees all 64 lanes.  PAD: D is
+// the padded head dimension of the kernel, dv < D the tensors' own: columns
+// at or past dv read as zeros and their acc entries stay 0 (otherwise dv = D).
+template <typename T, int D, int BN, bool PAD, typename TileOf, typename Allowed>
 __device__ inline __attribute__((always_inline)) void exact_row(
     const T* __restrict__ q_half, const T* __restrict__ k_head, const T* __restrict__ v_head,
-    int64_t row_stride, int hh, int S, int w0, int w1, TileOf tile_of, Allowed allowed, float c,
-    float m_ref, float inv_l, float (&acc)[D / 2]) {
+    int64_t row_stride, int hh, int dv, int S, int w0, int w1, TileOf tile_of, Allowed allowed,
+    float c, float m_ref, float inv_l, float (&acc)[D / 2]) {
     constexpr int DH = D / 2;
 #pragma unroll
     for (int d = 0; d < DH; ++d) acc[d] = 0.f;
@@ -134,8 +136,9 @@ __device__ inline __attribute__((always_inline)) void exact_row(
             for (int c8 = 0; c8 < DH / 8; ++c8) {
                 float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
                 float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                if (valid) load8<T>(k_head + off + 8 * c8, x);
-                if (q_half) load8<T>(q_half + 8 * c8, y);
+                const bool col = !PAD || hh * DH + 8 * c8 < dv;
+                if (valid && col) load8<T>(k_head + off + 8 * c8, x);
+                if (q_half && col) load8<T>(q_half + 8 * c8, y);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) part = __builtin_fmaf(y[i], x[i], part);
             }
@@ -145,7 +148,8 @@ __device__ inline __attribute__((always_inline)) void exact_row(
 #pragma unroll
                 for (int c8 = 0; c8 < DH / 8; ++c8) {
                     float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                    if (valid) load8<T>(v_head + off + 8 * c8, x);
+                    if (valid && (!PAD || hh * DH + 8 * c8 < dv))
+                        load8<T>(v_head + off + 8 * c8, x);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) acc[8 * c8 + i] = __builtin_fmaf(p, x[i], acc[8 * c8 + i]);
                 }
@@ -184,14 +188,17 @@ template <int DB> __device__ inline bool any_nonfinite(const f32x16 (&o)[DB]) {
 // to positions.  Cache rows past a sequence's length read as zeros.  A wave
 // whose rows are all padding, or allow no key, only takes part in the
 // workgroup's loads and barriers.
-template <typename T, int D, int NW, int BN_, bool SPLIT, bool SPARSE, bool PAGED, bool KVC>
+template <typename T, int D, int NW, int BN_, bool SPLIT, bool SPARSE, bool PAGED, bool KVC,
+          bool PAD = false>
 __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd_mfma_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, T* __restrict__ out,
     float* __restrict__ lse, int B, int H, int S, float c, int causal, int wl, int wr, int n_qt,
     int n_splits, float* __restrict__ part_o, float* __restrict__ part_lse,
     const int* __restrict__ sp_lut, int sp_heads, int sp_stride, const int* __restrict__ pg_table,
-    int pg_stride, int pg_rows, int pg_count, const int* __restrict__ kv_lens, int kv_cap) {
+    int pg_stride, int pg_rows, int pg_count, const int* __restrict__ kv_lens, int kv_cap,
+    int dv_in) {
     static_assert(!(SPLIT && SPARSE), "a block-sparse launch runs in one part");
+    static_assert(!(PAD && KVC), "the KV-cache forward takes head dimensions 64 and 128");
     static_assert(!(SPARSE && PAGED), "block-sparse and paged K/V do not combine");
     static_assert(!(SPARSE && KVC), "a block mask does not apply to a KV cache");
     typedef Tile<D, NW, BN_> L;
@@ -282,10 +289,15 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
         ki1 = __builtin_amdgcn_readfirstlane(sp_row[2]);
     }
 
-    const int64_t row_stride = (int64_t)H * D;                      // elements between rows
-    const int64_t head_base = ((int64_t)bb * S * H + h) * D;        // element (b, 0, h, 0)
+    // PAD: the tensors' head dimension is dv_in (a multiple of 16 below D);
+    // the kernel works on D columns, the ones at or past dv being zeros that
+    // are read as such and never stored.  Otherwise dv = D and every column
+    // test below folds away.
+    const int dv = PAD ? dv_in : D;
+    const int64_t row_stride = (int64_t)H * dv;                     // elements between rows
+    const int64_t head_base = ((int64_t)bb * S * H + h) * dv;       // element (b, 0, h, 0)
     // element (b, 0, h, 0) of the K/V tensors (KVC: of the caches)
-    const int64_t kv_head_base = KVC ? ((int64_t)bb * kv_cap * H + h) * D : head_base;
+    const int64_t kv_head_base = KVC ? ((int64_t)bb * kv_cap * H + h) * dv : head_base;
     const int q0 = qt * BM;
     const int qw0 = q0 + wave * kWaveRows;  // first row of this wave
     const int qrow = qw0 + ql;              // this lane's query row
@@ -298,8 +310,9 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
             for (int d = 0; d < D / 32; ++d)
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
-                    *reinterpret_cast<f32x4*>(part_o + part_row * D + 32 * d + 8 * g + 4 * hh) =
-                        f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (32 * d + 8 * g < dv)
+                        *reinterpret_cast<f32x4*>(part_o + part_row * dv + 32 * d + 8 * g + 4 * hh) =
+                            f32x4{0.f, 0.f, 0.f, 0.f};
         }
         return;
     }
@@ -325,7 +338,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     // past num_records, so the hardware returns zeros for it
     auto rows_rsrc = [&](const T* base, int64_t r0) __attribute__((always_inline)) {
         const T* p = base + head_base + r0 * row_stride;
-        const int64_t bytes = ((S - r0 - 1) * row_stride + D) * (int64_t)sizeof(T);
+        const int64_t bytes = ((S - r0 - 1) * row_stride + dv) * (int64_t)sizeof(T);
         const int64_t nrec = bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes;
         return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)(uint32_t)nrec,
                                                  kBufferFlags);
@@ -337,9 +350,12 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
         const __amdgpu_buffer_rsrc_t rq = rows_rsrc(q, qw0 < S ? qw0 : S - 1);
         const int voff = (ql * (int)row_stride + 8 * hh) * (int)sizeof(T);
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks)
+        for (int ks = 0; ks < KSTEPS; ++ks) {  // columns past dv are zeros
+            const bool col = !PAD || 16 * ks + 8 * hh < dv;
             qf[ks] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, voff + 32 * ks, 0, 0));
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, col ? voff + 32 * ks : voff, 0, 0));
+            if (!col) qf[ks] = u32x4{0, 0, 0, 0};
+        }
         if (qw0 >= S) {
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = u32x4{0, 0, 0, 0};
@@ -350,14 +366,23 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     // [wave * DMA_PER_WAVE KiB, +DMA_PER_WAVE KiB) of the tile; load j writes
     // [(wave * DMA_PER_WAVE + j) * 1024 + 16*lane, +16) with the logical chunk
     // stored there.  dma_voff[j] leaves out the j KiB the load's immediate
-    // offset adds (it is >= 0: chunk j starts at least j KiB into the tile's
-    // rows, whose stride H * D * e is at least the LDS row of D * e bytes).
+    // offset adds.  That is >= 0 when the tensors' rows (H * dv elements) are
+    // at least as long as the LDS rows (D elements); PAD, where they can be
+    // shorter, starts the tile's buffer resource kBias = kDmaBias bytes
+    // before the tile (with kBias more records) instead.  A chunk of columns
+    // at or past dv gets an offset past every record count (records are
+    // below 2^31 + kDmaBias: one tile, checked on the host), so the load
+    // writes zeros.
+    constexpr int kBias = PAD ? kDmaBias : 0;
     int dma_voff[L::DMA_PER_WAVE];
 #pragma unroll
     for (int j = 0; j < L::DMA_PER_WAVE; ++j) {
         const int byte = (wave * L::DMA_PER_WAVE + j) * 1024 + 16 * lane;
         const int r = byte / RB, pc = (byte % RB) / 16;
-        dma_voff[j] = r * (int)row_stride * (int)sizeof(T) + 16 * (pc ^ L::swz(r)) - 1024 * j;
+        const int lc = pc ^ L::swz(r);  // the logical chunk (8 columns) stored there
+        dma_voff[j] = (!PAD || 8 * lc < dv)
+                          ? r * (int)row_stride * (int)sizeof(T) + 16 * lc + kBias - 1024 * j
+                          : kDmaPastRecords;
     }
     // Buffer resource of K/V tile kt, built with a few scalar ops per tile:
     // base = head start + kt * tile bytes, records = the head's bytes from
@@ -365,7 +390,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     // the host), so kt * tile_bytes is one 32 x 32 -> 64-bit product.
     const uint32_t tile_bytes = (uint32_t)(BN * row_stride * (int64_t)sizeof(T));
     const uint64_t head_bytes =
-        Sk > 0 ? (uint64_t)(((int64_t)Sk - 1) * row_stride + D) * sizeof(T) : 0;
+        Sk > 0 ? (uint64_t)(((int64_t)Sk - 1) * row_stride + dv) * sizeof(T) : 0;
     // K/V tiles of the head and the bytes of its last one (<= tile_bytes)
     const int n_kt_head = (Sk + BN - 1) / BN;
     const uint32_t last_bytes =
@@ -373,13 +398,17 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     // PAGED: k and v are pools [pg_count, pg_rows, H, D]; key j of batch bb is
     // row j % pg_rows of page pg_table[bb * pg_stride + j / pg_rows].  pg_rows is
     // a multiple of BN, so a tile lies in one page.
-    const int64_t kv_base = PAGED ? (int64_t)h * D : kv_head_base;
+    const int64_t kv_base = PAGED ? (int64_t)h * dv : kv_head_base;
     const unsigned char* const k_head = (const unsigned char*)(k + kv_base);
     const unsigned char* const v_head = (const unsigned char*)(v + kv_base);
+    // the bases the tile loads use (kBias bytes before the heads)
+    const unsigned char* const k_dma = k_head - kBias;
+    const unsigned char* const v_dma = v_head - kBias;
     // PAGED: tiles per page, and the bytes of one page of one pool
     const int pg_tiles = PAGED ? pg_rows / BN : 1;
     const uint64_t page_bytes = PAGED ? (uint64_t)pg_rows * (uint64_t)row_stride * sizeof(T) : 0;
-    // K/V tile kt; PAGED: it is tile `in_page` of page `page`
+    // K/V tile kt (head: k_dma or v_dma, kBias bytes before the head's first
+    // row); PAGED: it is tile `in_page` of page `page`
     auto tile_rsrc = [&](const unsigned char* head, int kt, int page, int in_page) __attribute__((always_inline)) {
         if (PAGED) {
             // records stop at row S, and a page index outside the pool reads
@@ -390,9 +419,9 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
             const uint64_t off = (uint64_t)(uint32_t)page * page_bytes +
                                  (uint64_t)(uint32_t)in_page * tile_bytes;
             const uint32_t nrec =
-                ok ? (uint32_t)(((int64_t)(rows - 1) * row_stride + D) * (int64_t)sizeof(T)) : 0u;
+                ok ? (uint32_t)(((int64_t)(rows - 1) * row_stride + dv) * (int64_t)sizeof(T)) : 0u;
             return __builtin_amdgcn_make_buffer_rsrc((void*)(head + (ok ? off : 0)), (short)0,
-                                                     (int)nrec, kBufferFlags);
+                                                     (int)(nrec + kBias), kBufferFlags);
         }
         const uint64_t off = (uint64_t)(uint32_t)kt * tile_bytes;
         // records cover the tile up to the end of the head's last row: every
@@ -400,16 +429,18 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
         // the last one ends at the head's end, and a tile that starts at or
         // past S gets none, so the hardware range check turns every read past
         // the tensor into a zero.  32-bit scalar compares only.
-        const uint32_t nrec = kt < n_kt_head - 1 ? tile_bytes : kt == n_kt_head - 1 ? last_bytes : 0u;
+        const uint32_t nrec = kt < n_kt_head - 1 ? tile_bytes + kBias
+                              : kt == n_kt_head - 1 ? last_bytes + kBias
+                                                    : (uint32_t)kBias;
         return __builtin_amdgcn_make_buffer_rsrc((void*)(head + off), (short)0, (int)nrec,
                                                  kBufferFlags);
     };
     auto load_k = [&](int kt, int page, int rem, unsigned char* buf) __attribute__((always_inline)) {
-        dma_matrix<L::DMA_PER_WAVE>(tile_rsrc(k_head, kt, page, rem),
+        dma_matrix<L::DMA_PER_WAVE>(tile_rsrc(k_dma, kt, page, rem),
                                     buf + wave * L::DMA_PER_WAVE * 1024, dma_voff);
     };
     auto load_v = [&](int kt, int page, int rem, unsigned char* buf) __attribute__((always_inline)) {
-        dma_matrix<L::DMA_PER_WAVE>(tile_rsrc(v_head, kt, page, rem),
+        dma_matrix<L::DMA_PER_WAVE>(tile_rsrc(v_dma, kt, page, rem),
                                     buf + wave * L::DMA_PER_WAVE * 1024, dma_voff);
     };
     // Look-ahead table (SPARSE: the kept-tile list, indexed by position;
@@ -848,25 +879,27 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
             return (unsigned)(key - key_lo) <= (unsigned)key_w;
         };
         const T* q_half = qrow < S ? q + head_base + (int64_t)qrow * row_stride + hh * DH : nullptr;
-        exact_row<T, D, BN>(q_half, (const T*)k_head, (const T*)v_head, row_stride, hh, Sk, ex_w0,
+        exact_row<T, D, BN, PAD>(q_half, (const T*)k_head, (const T*)v_head, row_stride, hh, dv, Sk, ex_w0,
                             ex_w1, tile_of, allowed, c, m_fin, inv, acc);
         if (qrow < S) {
             if (SPLIT) {
                 if (hh == 0) part_lse[part_row] = lse_v;
 #pragma unroll
                 for (int c4 = 0; c4 < DH / 4; ++c4)
-                    *reinterpret_cast<f32x4*>(part_o + part_row * D + hh * DH + 4 * c4) =
-                        f32x4{acc[4 * c4], acc[4 * c4 + 1], acc[4 * c4 + 2], acc[4 * c4 + 3]};
+                    if (!PAD || hh * DH + 4 * c4 < dv)
+                        *reinterpret_cast<f32x4*>(part_o + part_row * dv + hh * DH + 4 * c4) =
+                            f32x4{acc[4 * c4], acc[4 * c4 + 1], acc[4 * c4 + 2], acc[4 * c4 + 3]};
             } else {
                 if (hh == 0) lse[((int64_t)bb * H + h) * S + qrow] = lse_v;
                 T* const orow = out + head_base + (int64_t)qrow * row_stride + hh * DH;
 #pragma unroll
                 for (int c8 = 0; c8 < DH / 8; ++c8)
-                    *reinterpret_cast<u32x4*>(orow + 8 * c8) = u32x4{
-                        Mfma<T>::pack2(acc[8 * c8], acc[8 * c8 + 1]),
-                        Mfma<T>::pack2(acc[8 * c8 + 2], acc[8 * c8 + 3]),
-                        Mfma<T>::pack2(acc[8 * c8 + 4], acc[8 * c8 + 5]),
-                        Mfma<T>::pack2(acc[8 * c8 + 6], acc[8 * c8 + 7])};
+                    if (!PAD || hh * DH + 8 * c8 < dv)
+                        *reinterpret_cast<u32x4*>(orow + 8 * c8) = u32x4{
+                            Mfma<T>::pack2(acc[8 * c8], acc[8 * c8 + 1]),
+                            Mfma<T>::pack2(acc[8 * c8 + 2], acc[8 * c8 + 3]),
+                            Mfma<T>::pack2(acc[8 * c8 + 4], acc[8 * c8 + 5]),
+                            Mfma<T>::pack2(acc[8 * c8 + 6], acc[8 * c8 + 7])};
             }
         }
         return;
@@ -878,9 +911,10 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
             for (int d = 0; d < DB; ++d)
 #pragma unroll
                 for (int g = 0; g < 4; ++g)
-                    *reinterpret_cast<f32x4*>(part_o + part_row * D + 32 * d + 8 * g + 4 * hh) =
-                        f32x4{o[d][4 * g] * inv, o[d][4 * g + 1] * inv, o[d][4 * g + 2] * inv,
-                              o[d][4 * g + 3] * inv};
+                    if (32 * d + 8 * g < dv)
+                        *reinterpret_cast<f32x4*>(part_o + part_row * dv + 32 * d + 8 * g + 4 * hh) =
+                            f32x4{o[d][4 * g] * inv, o[d][4 * g + 1] * inv, o[d][4 * g + 2] * inv,
+                                  o[d][4 * g + 3] * inv};
         }
         return;
     }
@@ -915,7 +949,8 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
             const int r = i * ROWS_PER_READ + rl;
             const u32x4 x =
                 *reinterpret_cast<const u32x4*>(stg + r * RB + 16 * (cl ^ (r & (NC - 1))));
-            if (qw0 + r < S) *reinterpret_cast<u32x4*>(orow + (int64_t)(qw0 + r) * row_stride) = x;
+            if (qw0 + r < S && (!PAD || 8 * cl < dv))
+                *reinterpret_cast<u32x4*>(orow + (int64_t)(qw0 + r) * row_stride) = x;
         }
     }
 }
@@ -992,13 +1027,15 @@ constexpr int kMergeThreads = 256;
 template <typename T, int D>
 __global__ __launch_bounds__(kMergeThreads) void fa_merge_parts_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse, T* __restrict__ out,
-    float* __restrict__ lse, int B, int H, int S, int n_splits) {
+    float* __restrict__ lse, int B, int H, int S, int n_splits, int dv) {
+    // D: the padded head dimension (threads per row); dv <= D: the tensors'
+    // own, the column count of the partial rows and of O
     constexpr int TPR = D / 4;                  // threads per row, 4 columns each
     constexpr int RPB = kMergeThreads / TPR;    // rows per workgroup
     const int64_t R = (int64_t)B * H * S;       // rows, ordered (b * H + h) * S + s
     const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
     const int c4 = threadIdx.x % TPR;
-    if (row >= R) return;
+    if (row >= R || 4 * c4 >= dv) return;
     float m = kNegInf;
     bool nan = false;
     for (int p = 0; p < n_splits; ++p) {
@@ -1012,7 +1049,7 @@ __global__ __launch_bounds__(kMergeThreads) void fa_merge_parts_kernel(
         for (int p = 0; p < n_splits; ++p) {
             const float l = part_lse[p * R + row];
             const float w = (l == kNegInf) ? 0.f : expf(l - m);
-            const f32x4 x = *reinterpret_cast<const f32x4*>(part_o + (p * R + row) * D + 4 * c4);
+            const f32x4 x = *reinterpret_cast<const f32x4*>(part_o + (p * R + row) * dv + 4 * c4);
             acc += w * x;
             wsum += w;
         }
@@ -1026,7 +1063,7 @@ __global__ __launch_bounds__(kMergeThreads) void fa_merge_parts_kernel(
     }
     const int64_t bh = row / S, srow = row - bh * S;
     const int64_t b = bh / H, h = bh - b * H;
-    store4<T>(out + ((b * S + srow) * H + h) * D + 4 * c4, o);
+    store4<T>(out + ((b * S + srow) * H + h) * dv + 4 * c4, o);
     if (c4 == 0) lse[row] = lv;
 }
 
@@ -1196,7 +1233,7 @@ __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
             return ok && (!SPARSE || mrow[key / block_n] != 0);
         };
         const float* q_half = qrow < S ? q + head_base + (int64_t)qrow * row_stride + hh * DH : nullptr;
-        exact_row<float, D, BN>(q_half, k + kv_base, v + kv_base, row_stride, hh, S, (int)kt0,
+        exact_row<float, D, BN, false>(q_half, k + kv_base, v + kv_base, row_stride, hh, D, S, (int)kt0,
                                 (int)kt1, tile_of, allowed, c, m_fin, inv, acc);
         if (qrow < S) {
             float* eo = out + head_base + (int64_t)qrow * row_stride + hh * DH;

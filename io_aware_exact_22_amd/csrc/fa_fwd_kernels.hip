@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "fa_fwd_device.h"
+#include "fa_fwd_launch_cfg.h"
 #include "fa_launch.h"
 #include "fa_schedule.h"
 
@@ -18,79 +19,20 @@ static hipError_t launch_merge_cfg(const LaunchArgs& a) {
     hipLaunchKernelGGL((fa_merge_parts_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)),
                        dim3(kMergeThreads), 0, a.stream, (const float*)a.part_o,
                        (const float*)a.part_lse, (T*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S,
-                       a.n_splits);
+                       a.n_splits, (int)a.D);
     return hipGetLastError();
 }
 
 hipError_t launch_merge_parts(const LaunchArgs& a) {
     if (a.dtype == kDtypeBf16)
-        return a.D == 64 ? launch_merge_cfg<__bf16, 64>(a) : launch_merge_cfg<__bf16, 128>(a);
-    return a.D == 64 ? launch_merge_cfg<_Float16, 64>(a) : launch_merge_cfg<_Float16, 128>(a);
-}
-
-template <typename T, int D, int NW, int BN>
-static hipError_t launch_mfma_cfg(const LaunchArgs& a) {
-    constexpr int BM = Tile<D, NW, BN>::BM;
-    const int n_qt = (int)((a.S + BM - 1) / BM);
-    const int64_t n_wg = a.B * a.H * n_qt;
-    if (a.bmask) {  // block-sparse: compact the kept tiles, then walk them
-        const int n_kt = (int)((a.S + BN - 1) / BN);
-        const int stride = (int)sparse_lut_stride(n_kt);
-        hipLaunchKernelGGL((sparse_lut_kernel<BM, BN>), dim3((unsigned)(a.n_mask * n_qt)), dim3(64),
-                           0, a.stream, a.bmask, (int)a.S, a.causal, (int)a.wl, (int)a.wr, n_qt,
-                           (int)((a.S + a.block_n - 1) / a.block_n),
-                           (int)((a.S + a.block_m - 1) / a.block_m), (int)a.block_m,
-                           (int)a.block_n, stride, a.lut);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, true, false, false>),
-                           dim3((unsigned)n_wg), dim3(NW * 64), 0, a.stream, (const T*)a.q,
-                           (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
-                           (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr, nullptr,
-                           (const int*)a.lut, (int)a.n_mask, stride, nullptr, 0, 1, 0, nullptr, 0);
-        return hipGetLastError();
-    }
-    const bool paged = a.pg_table != nullptr;
-    const int pg_stride = (int)a.pg_stride, pg_rows = paged ? (int)a.pg_rows : 1,
-              pg_count = (int)a.pg_count;
-    if (a.n_splits <= 1) {
-        if (paged)
-            hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, false, true, false>),
-                               dim3((unsigned)n_wg), dim3(NW * 64), 0, a.stream, (const T*)a.q,
-                               (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
-                               (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr,
-                               nullptr, nullptr, 0, 0, a.pg_table, pg_stride, pg_rows, pg_count,
-                               nullptr, 0);
-        else
-            hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, false, false, false>),
-                               dim3((unsigned)n_wg), dim3(NW * 64), 0, a.stream, (const T*)a.q,
-                               (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
-                               (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr,
-                               nullptr, nullptr, 0, 0, nullptr, 0, 1, 0, nullptr, 0);
-        return hipGetLastError();
-    }
-    if (paged)
-        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, true, false, true, false>),
-                           dim3((unsigned)(n_wg * a.n_splits)), dim3(NW * 64), 0, a.stream,
-                           (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B,
-                           (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt,
-                           a.n_splits, a.part_o, a.part_lse, nullptr, 0, 0, a.pg_table, pg_stride,
-                           pg_rows, pg_count, nullptr, 0);
-    else
-        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, true, false, false, false>),
-                           dim3((unsigned)(n_wg * a.n_splits)), dim3(NW * 64), 0, a.stream,
-                           (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B,
-                           (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt,
-                           a.n_splits, a.part_o, a.part_lse, nullptr, 0, 0, nullptr, 0, 1, 0,
-                           nullptr, 0);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_merge_parts(a);
+        return a.D <= 64 ? launch_merge_cfg<__bf16, 64>(a) : launch_merge_cfg<__bf16, 128>(a);
+    return a.D <= 64 ? launch_merge_cfg<_Float16, 64>(a) : launch_merge_cfg<_Float16, 128>(a);
 }
 
 template <typename T, int D>
 static hipError_t launch_mfma(const LaunchArgs& a) {
-    return launch_mfma_cfg<T, D, kMfmaWaves, kMfmaKeys>(a);
+    if (a.D != D) return launch_fwd_padded(a);  // fa_fwd_padded.hip
+    return launch_mfma_cfg<T, D, kMfmaWaves, kMfmaKeys, false>(a);
 }
 
 
@@ -129,8 +71,10 @@ static hipError_t launch_fp32(const LaunchArgs& a) {
 hipError_t launch_fwd(const LaunchArgs& a) {
     if (a.kv_lens) return launch_kvcache(a);
     switch (a.dtype) {
-    case kDtypeBf16: return a.D == 64 ? launch_mfma<__bf16, 64>(a) : launch_mfma<__bf16, 128>(a);
-    case kDtypeFp16: return a.D == 64 ? launch_mfma<_Float16, 64>(a) : launch_mfma<_Float16, 128>(a);
+    // bf16 / fp16: a head dimension below 64 or between 64 and 128 runs the
+    // kernel of the next one up, its extra columns zeros
+    case kDtypeBf16: return a.D <= 64 ? launch_mfma<__bf16, 64>(a) : launch_mfma<__bf16, 128>(a);
+    case kDtypeFp16: return a.D <= 64 ? launch_mfma<_Float16, 64>(a) : launch_mfma<_Float16, 128>(a);
     default: return a.D == 64 ? launch_fp32<64>(a) : launch_fp32<128>(a);
     }
 }
@@ -172,9 +116,9 @@ static int auto_splits_cfg(const LaunchArgs& a) {
 
 int auto_splits(const LaunchArgs& a) {
     switch (a.dtype) {
-    case kDtypeBf16: return a.D == 64 ? auto_splits_cfg<__bf16, 64>(a) : auto_splits_cfg<__bf16, 128>(a);
+    case kDtypeBf16: return a.D <= 64 ? auto_splits_cfg<__bf16, 64>(a) : auto_splits_cfg<__bf16, 128>(a);
     case kDtypeFp16:
-        return a.D == 64 ? auto_splits_cfg<_Float16, 64>(a) : auto_splits_cfg<_Float16, 128>(a);
+        return a.D <= 64 ? auto_splits_cfg<_Float16, 64>(a) : auto_splits_cfg<_Float16, 128>(a);
     default: return 1;  // fp32 inputs run in one part
     }
 }

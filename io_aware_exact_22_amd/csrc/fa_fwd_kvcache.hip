@@ -270,13 +270,13 @@ static hipError_t launch_kvcache_cfg(const LaunchArgs& a) {
                                (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
                                (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr,
                                nullptr, nullptr, 0, 0, a.pg_table, pg_stride, pg_rows, pg_count,
-                               a.kv_lens, cap);
+                               a.kv_lens, cap, (int)a.D);
         else
             hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, false, false, true>),
                                dim3((unsigned)n_wg), dim3(NW * 64), 0, a.stream, (const T*)a.q,
                                (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
                                (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr,
-                               nullptr, nullptr, 0, 0, nullptr, 0, 1, 0, a.kv_lens, cap);
+                               nullptr, nullptr, 0, 0, nullptr, 0, 1, 0, a.kv_lens, cap, (int)a.D);
         return hipGetLastError();
     }
     if (paged)
@@ -285,14 +285,14 @@ static hipError_t launch_kvcache_cfg(const LaunchArgs& a) {
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B,
                            (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt,
                            a.n_splits, a.part_o, a.part_lse, nullptr, 0, 0, a.pg_table, pg_stride,
-                           pg_rows, pg_count, a.kv_lens, cap);
+                           pg_rows, pg_count, a.kv_lens, cap, (int)a.D);
     else
         hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, true, false, false, true>),
                            dim3((unsigned)(n_wg * a.n_splits)), dim3(NW * 64), 0, a.stream,
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B,
                            (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt,
                            a.n_splits, a.part_o, a.part_lse, nullptr, 0, 0, nullptr, 0, 1, 0,
-                           a.kv_lens, cap);
+                           a.kv_lens, cap, (int)a.D);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_merge_parts(a);

@@ -1,0 +1,76 @@
+// fa_fwd_launch_cfg.h -- the launch of fa_fwd_mfma_kernel for a dense, split,
+// block-sparse or paged forward, shared by fa_fwd_kernels.hip (head
+// dimensions 64 and 128) and fa_fwd_padded.hip (the others, PAD = true: the
+// kernel for the next of 64 and 128 with zero columns), so that the two sets
+// of instantiations compile in parallel.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_fwd_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+template <typename T, int D, int NW, int BN, bool PAD>
+hipError_t launch_mfma_cfg(const LaunchArgs& a) {
+    constexpr int BM = Tile<D, NW, BN>::BM;
+    const int n_qt = (int)((a.S + BM - 1) / BM);
+    const int64_t n_wg = a.B * a.H * n_qt;
+    if (a.bmask) {  // block-sparse: compact the kept tiles, then walk them
+        const int n_kt = (int)((a.S + BN - 1) / BN);
+        const int stride = (int)sparse_lut_stride(n_kt);
+        hipLaunchKernelGGL((sparse_lut_kernel<BM, BN>), dim3((unsigned)(a.n_mask * n_qt)), dim3(64),
+                           0, a.stream, a.bmask, (int)a.S, a.causal, (int)a.wl, (int)a.wr, n_qt,
+                           (int)((a.S + a.block_n - 1) / a.block_n),
+                           (int)((a.S + a.block_m - 1) / a.block_m), (int)a.block_m,
+                           (int)a.block_n, stride, a.lut);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, true, false, false, PAD>),
+                           dim3((unsigned)n_wg), dim3(NW * 64), 0, a.stream, (const T*)a.q,
+                           (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
+                           (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr, nullptr,
+                           (const int*)a.lut, (int)a.n_mask, stride, nullptr, 0, 1, 0, nullptr, 0, (int)a.D);
+        return hipGetLastError();
+    }
+    const bool paged = a.pg_table != nullptr;
+    const int pg_stride = (int)a.pg_stride, pg_rows = paged ? (int)a.pg_rows : 1,
+              pg_count = (int)a.pg_count;
+    if (a.n_splits <= 1) {
+        if (paged)
+            hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, false, true, false, PAD>),
+                               dim3((unsigned)n_wg), dim3(NW * 64), 0, a.stream, (const T*)a.q,
+                               (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
+                               (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr,
+                               nullptr, nullptr, 0, 0, a.pg_table, pg_stride, pg_rows, pg_count,
+                               nullptr, 0, (int)a.D);
+        else
+            hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, false, false, false, PAD>),
+                               dim3((unsigned)n_wg), dim3(NW * 64), 0, a.stream, (const T*)a.q,
+                               (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
+                               (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr,
+                               nullptr, nullptr, 0, 0, nullptr, 0, 1, 0, nullptr, 0, (int)a.D);
+        return hipGetLastError();
+    }
+    if (paged)
+        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, true, false, true, false, PAD>),
+                           dim3((unsigned)(n_wg * a.n_splits)), dim3(NW * 64), 0, a.stream,
+                           (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B,
+                           (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt,
+                           a.n_splits, a.part_o, a.part_lse, nullptr, 0, 0, a.pg_table, pg_stride,
+                           pg_rows, pg_count, nullptr, 0, (int)a.D);
+    else
+        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, true, false, false, false, PAD>),
+                           dim3((unsigned)(n_wg * a.n_splits)), dim3(NW * 64), 0, a.stream,
+                           (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B,
+                           (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt,
+                           a.n_splits, a.part_o, a.part_lse, nullptr, 0, 0, nullptr, 0, 1, 0,
+                           nullptr, 0, (int)a.D);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_merge_parts(a);
+}
+
+}  // namespace fa

@@ -30,6 +30,13 @@ constexpr int kWaveRows = 32;  // query rows per wave
 constexpr float kNegInf = -__builtin_inff();
 // word 3 of a raw (stride 0) buffer resource on gfx9-family GPUs
 constexpr int kBufferFlags = 0x00020000;
+// Direct-to-LDS tile loads: the tile's buffer resource starts this many bytes
+// before the tile, so that per-lane offsets stay >= 0 after the up to 3 KiB
+// of immediate offset are taken out of them; and an offset that lies past
+// every record count of such a resource (one tile plus kDmaBias is below
+// 2^31 + 4096 bytes), whose loads write zeros.
+constexpr int kDmaBias = 4096;
+constexpr int kDmaPastRecords = (int)0xFFFF0000u;
 // log2-domain slack before the running reference max is moved (weights <= 2^8)
 constexpr float kRescaleSlack = 8.f;
 

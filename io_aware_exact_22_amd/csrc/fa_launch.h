@@ -80,6 +80,9 @@ hipError_t launch_bwd(const BwdArgs& a);
 // Enqueues the forward kernel (and, for a split launch, the merge kernel) for
 // validated arguments.
 hipError_t launch_fwd(const LaunchArgs& a);
+// The bf16 / fp16 forward at a head dimension other than 64 and 128 (a
+// multiple of 16 below 128), dense, split, block-sparse or paged.
+hipError_t launch_fwd_padded(const LaunchArgs& a);
 // The KV-cache forward (a.kv_lens set; bf16 / fp16), split or not.
 hipError_t launch_kvcache(const LaunchArgs& a);
 // The merge of a split launch's partial (O, LSE) into out / lse (bf16 / fp16).

@@ -69,7 +69,11 @@ def check(**kw):
     ({"B": 0}, -2), ({"H": 0}, -2), ({"S": 0}, -2), ({"S": -5}, -2),
     ({"S": 1 << 40}, -2), ({"B": 1 << 40, "H": 1 << 30}, -2),
     ({"H": 131072, "D": 128, "S": 1}, -2), ({"H": 131071, "D": 128, "S": 1}, 0),
-    ({"D": 96}, -3), ({"D": 0}, -3), ({"D": 256}, -3),
+    # bf16 / fp16: any multiple of 16 from 16 to 128; fp32: 64 or 128
+    ({"D": 96}, 0), ({"D": 16}, 0), ({"D": 48}, 0), ({"D": 112}, 0),
+    ({"D": 0}, -3), ({"D": 8}, -3), ({"D": 24}, -3), ({"D": 100}, -3), ({"D": 144}, -3),
+    ({"D": 256}, -3), ({"D": 96, "dtype": fa.FA_DTYPE_FP32}, -3),
+    ({"D": 64, "dtype": fa.FA_DTYPE_FP32}, 0), ({"D": 96, "dtype": fa.FA_DTYPE_FP16}, 0),
     ({"window_left": -2}, -4), ({"window_right": -7}, -4), ({"causal": 2}, -4),
     ({"dtype": 3}, -5), ({"dtype": -1}, -5),
     ({"scale": float("nan")}, -6), ({"scale": float("inf")}, -6), ({"scale": -0.5}, -6),
@@ -85,7 +89,7 @@ def test_check_args(kw, status):
 
 def test_fa_fwd_rejects_before_any_hip_call():
     # invalid arguments return the status without touching the GPU (none here)
-    rc = fa.fa_fwd(Q, K, V, OUT, LSE, 1, 1, 128, 96, 0.1, 0, -1, -1, fa.FA_DTYPE_BF16, None)
+    rc = fa.fa_fwd(Q, K, V, OUT, LSE, 1, 1, 128, 100, 0.1, 0, -1, -1, fa.FA_DTYPE_BF16, None)
     assert rc == -3
     rc = fa.fa_fwd(0, K, V, OUT, LSE, 1, 1, 128, 64, 0.1, 0, -1, -1, fa.FA_DTYPE_BF16, None)
     assert rc == -1
@@ -93,19 +97,22 @@ def test_fa_fwd_rejects_before_any_hip_call():
 
 @pytest.mark.parametrize("B,H,S,D,dtype,ns", [(2, 16, 2048, 64, fa.FA_DTYPE_BF16, 3),
                                                 (1, 2, 16384, 128, fa.FA_DTYPE_BF16, 4),
-                                                (3, 5, 389, 128, fa.FA_DTYPE_FP16, 16)])
+                                                (3, 5, 389, 128, fa.FA_DTYPE_FP16, 16),
+                                                (2, 3, 300, 96, fa.FA_DTYPE_BF16, 5),
+                                                (1, 1, 77, 16, fa.FA_DTYPE_FP16, 2)])
 def test_splitkv_workspace_size(B, H, S, D, dtype, ns):
     """fp32 partial O and LSE of every part: ns * B * H * S * (D + 1) * 4 bytes;
     nothing for one part or fp32 inputs."""
     assert fa.fa_fwd_splitkv_workspace_size(B, H, S, D, dtype, ns) == ns * B * H * S * (D + 1) * 4
     assert fa.fa_fwd_splitkv_workspace_size(B, H, S, D, dtype, 1) == 0
-    assert fa.fa_fwd_splitkv_workspace_size(B, H, S, D, fa.FA_DTYPE_FP32, ns) == 0
+    if D in (64, 128):  # fp32 takes these two only
+        assert fa.fa_fwd_splitkv_workspace_size(B, H, S, D, fa.FA_DTYPE_FP32, ns) == 0
     for bad in (0, -1, fa.FA_MAX_SPLITS + 1):
         with pytest.raises(fa.FaError) as e:
             fa.fa_fwd_splitkv_workspace_size(B, H, S, D, dtype, bad)
         assert e.value.status == -11
     with pytest.raises(fa.FaError) as e:
-        fa.fa_fwd_splitkv_workspace_size(B, H, S, 96, dtype, ns)
+        fa.fa_fwd_splitkv_workspace_size(B, H, S, 100, dtype, ns)
     assert e.value.status == -3
 
 
@@ -116,7 +123,7 @@ WS = 6 << 32  # a fake, aligned workspace address disjoint from the tensors abov
     ({"ns": 2, "ws": 0}, -10), ({"ns": 2, "wsb": 100}, -10), ({"ns": 2, "ws": WS + 8}, -10),
     ({"ns": 2, "ws": Q}, -10), ({"ns": 2, "ws": LSE - 64}, -10),
     ({"ns": 0}, -11), ({"ns": 17}, -11), ({"ns": -3}, -11),
-    ({"ns": 2, "D": 96}, -3), ({"ns": 2, "q": 0}, -1), ({"ns": 2, "out": Q}, -8),
+    ({"ns": 2, "D": 72}, -3), ({"ns": 2, "q": 0}, -1), ({"ns": 2, "out": Q}, -8),
     ({"ns": 2, "dtype": 7}, -5),
 ])
 def test_splitkv_rejects_before_any_hip_call(kw, status):
@@ -180,7 +187,7 @@ MASK = 11 << 32  # a fake block-mask address disjoint from everything above
     ({"mask": 0}, -1), ({"bm": 64}, -12), ({"bm": 192}, -12), ({"bm": 0}, -12), ({"bn": 32}, -12),
     ({"bn": 96}, -12), ({"nm": 3}, -12), ({"nm": 0}, -12), ({"ws": 0}, -10), ({"wsb": 16}, -10),
     ({"ws": WS + 8}, -10), ({"ws": Q}, -10), ({"ws": MASK}, -10), ({"out": MASK}, -8),
-    ({"lse": MASK}, -8), ({"D": 80}, -3), ({"scale": float("nan")}, -6), ({"q": 0}, -1),
+    ({"lse": MASK}, -8), ({"D": 88}, -3), ({"scale": float("nan")}, -6), ({"q": 0}, -1),
 ])
 def test_blocksparse_rejects_before_any_hip_call(kw, status):
     """Invalid arguments return their status without touching the GPU."""
@@ -201,7 +208,7 @@ KP, VP, BT = 12 << 32, 13 << 32, 14 << 32  # fake page pools and block table
     ({"np": 0}, -13), ({"ts": 2}, -13), ({"kp": KP + 8}, -7), ({"bt": BT + 2}, -7),
     ({"out": KP}, -8), ({"lse": BT}, -8), ({"out": VP + 64}, -8), ({"ns": 17}, -11),
     ({"ns": 2, "ws": 0}, -10), ({"ns": 2, "ws": KP}, -10), ({"ns": 2, "ws": WS + 4}, -10),
-    ({"D": 96}, -3), ({"scale": -2.0}, -6), ({"window_right": -5}, -4),
+    ({"D": 40}, -3), ({"scale": -2.0}, -6), ({"window_right": -5}, -4),
 ])
 def test_paged_rejects_before_any_hip_call(kw, status):
     """Invalid arguments return their status without touching the GPU (S = 300
