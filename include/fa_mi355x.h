@@ -48,7 +48,7 @@ typedef enum {
     FA_ERR_SHAPE = -2,    /* B, H or S < 1, a size overflows int64 / the index range, or
                              64 rows of one tensor (64*H*D elements) exceed 2^31 - 1 bytes */
     FA_ERR_HEAD_DIM = -3, /* D not supported (bf16 / fp16 forward: a multiple of 16 in
-                             [16, 128]; fp32, fa_bwd, fa_fwd_kvcache: 64 or 128) */
+                             [16, 256]; fp32, fa_bwd, fa_fwd_kvcache: 64 or 128) */
     FA_ERR_WINDOW = -4,   /* window_left or window_right < -1, or causal not 0/1 */
     FA_ERR_DTYPE = -5,    /* dtype not one of fa_dtype_t */
     FA_ERR_SCALE = -6,    /* scale NaN, infinite or negative */
@@ -84,14 +84,15 @@ typedef enum {
  * lse      device pointer, contiguous [B, H, S] fp32; fully written with the
  *          natural-log log-sum-exp of the scaled, masked scores of each row.
  * B, H, S  batch, heads, sequence length (one S for queries and keys), >= 1.
- * D        head dimension.  bf16 / fp16: any multiple of 16 from 16 to 128
+ * D        head dimension.  bf16 / fp16: any multiple of 16 from 16 to 256
  *          (the pages ask Tensor Core shapes to be multiples of 8: section 4.2
  *          of "FlashAttention技术解析：加速GPT训练的核心优化"; 16 is the k
- *          step of the gfx950 MFMA); below 64, or between 64 and 128, the
- *          kernel for the next of 64 and 128 runs with the extra columns read
- *          as zeros and never written.  fp32: 64 or 128.  The same holds for
- *          fa_fwd_splitkv, fa_fwd_splitkv_noalloc, fa_fwd_blocksparse and
- *          fa_fwd_paged; fa_bwd and fa_fwd_kvcache take 64 or 128.
+ *          step of the gfx950 MFMA); a D other than 64, 128 and 256 runs the
+ *          kernel for the next of them with the extra columns read as zeros
+ *          and never written, and D above 128 uses 32-key K/V tiles.  fp32: 64
+ *          or 128.  The same holds for fa_fwd_splitkv, fa_fwd_splitkv_noalloc,
+ *          fa_fwd_blocksparse and fa_fwd_paged; fa_bwd and fa_fwd_kvcache
+ *          take 64 or 128.
  * scale    softmax scale applied to q.k in fp32 (finite, >= 0); callers that
  *          want the pages' default pass 1/sqrt(D).
  * causal   0 or 1.
@@ -309,9 +310,9 @@ int fa_fwd_blocksparse(const void* q, const void* k, const void* v, void* out, f
 
 /*
  * fa_fwd_blocksparse_workspace_size -- the workspace fa_fwd_blocksparse needs,
- * in *bytes: n_mask * ceil(S / 128) * (4 + 4 * ceil(ceil(S / 64) / 4)) * 4 for
- * bf16 / fp16 (one list of kept K/V tiles per mask head and Q tile), 0 for
- * fp32.  Pure function, no HIP call.  Returns FA_OK, FA_ERR_NULL,
+ * in *bytes: n_mask * ceil(S / 128) * (4 + 4 * ceil(ceil(S / BN) / 4)) * 4 for
+ * bf16 / fp16 (one list of kept K/V tiles per mask head and Q tile; BN = 64,
+ * or 32 above D = 128), 0 for fp32.  Pure function, no HIP call.  Returns FA_OK, FA_ERR_NULL,
  * FA_ERR_BLOCKMASK (n_mask not 1, H or B * H) or the status fa_fwd_check_args
  * gives for the shape, head dimension and dtype.
  */

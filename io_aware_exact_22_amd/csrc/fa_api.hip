@@ -28,8 +28,8 @@ int64_t elem_size(int dtype) { return dtype == fa::kDtypeFp32 ? 4 : 2; }
 
 // Shape / window / dtype checks shared by the entry points; *tensor_bytes and
 // *lse_bytes are set on success.  Head dimensions: the bf16 / fp16 forward
-// kernels take any multiple of 16 from 16 to 128 (below 64 or between 64 and
-// 128 they run the next kernel up with zero columns); fp32 inputs and the
+// kernels take any multiple of 16 from 16 to 256 (other than 64, 128 and 256
+// they run the next kernel up with zero columns); fp32 inputs and the
 // fixed_d callers (the backward, the KV-cache forward) take 64 or 128.
 int check_problem(int64_t B, int64_t H, int64_t S, int64_t D, int causal, int64_t wl, int64_t wr,
                   int dtype, int64_t* tensor_bytes, int64_t* lse_bytes, bool fixed_d = false) {
@@ -38,7 +38,7 @@ int check_problem(int64_t B, int64_t H, int64_t S, int64_t D, int causal, int64_
     if (B < 1 || H < 1 || S < 1) return FA_ERR_SHAPE;
     if (fixed_d || dtype == FA_DTYPE_FP32) {
         if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
-    } else if (D < 16 || D > 128 || D % 16 != 0) {
+    } else if (D < 16 || D > 256 || D % 16 != 0) {
         return FA_ERR_HEAD_DIM;
     }
     if ((causal != 0 && causal != 1) || wl < -1 || wr < -1) return FA_ERR_WINDOW;
@@ -70,7 +70,7 @@ FA_API const char* fa_status_string(int status) {
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "B, H and S must be >= 1 and the sizes must fit the index ranges";
     case FA_ERR_HEAD_DIM:
-        return "unsupported head dimension D (bf16 / fp16 forward: a multiple of 16 from 16 to 128; "
+        return "unsupported head dimension D (bf16 / fp16 forward: a multiple of 16 from 16 to 256; "
                "fp32 inputs, fa_bwd and fa_fwd_kvcache: 64 or 128)";
     case FA_ERR_WINDOW: return "causal must be 0 or 1 and window bounds must be >= -1";
     case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_FP32, FA_DTYPE_FP16 or FA_DTYPE_BF16";
@@ -416,7 +416,7 @@ FA_API int fa_fwd_blocksparse_workspace_size(int64_t B, int64_t H, int64_t S, in
     if (rc != FA_OK) return rc;
     if (n_mask != 1 && n_mask != H && n_mask != B * H) return FA_ERR_BLOCKMASK;
     // n_mask * ceil(S/128) rows of 4 + ceil(S/64) ints: below 2 * B*H*S*4 + small
-    *bytes = fa::blocksparse_lut_bytes(dtype, S, n_mask);
+    *bytes = fa::blocksparse_lut_bytes(dtype, D, S, n_mask);
     return FA_OK;
 }
 

@@ -212,8 +212,8 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     // LDS operand reads run this many MFMAs ahead of their score / P V MFMA;
     // at D = 128 longer leads hide more LDS latency (measured), at D = 64 the
     // extra registers cost more than they hide
-    constexpr int kLeadK = D == 128 ? FA_LEAD_K_D128 : FA_LEAD_K;
-    constexpr int kLeadV = D == 128 ? FA_LEAD_V_D128 : FA_LEAD_V;
+    constexpr int kLeadK = D >= 128 ? FA_LEAD_K_D128 : FA_LEAD_K;
+    constexpr int kLeadV = D >= 128 ? FA_LEAD_V_D128 : FA_LEAD_V;
     // one object per K / V stage: the compiler then sees that the direct-to-LDS
     // load of one stage never aliases the operand reads of the other, and does
     // not wait for the load before them
@@ -919,6 +919,22 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
         return;
     }
     if (qrow < S && hh == 0) lse[((int64_t)bb * H + h) * S + qrow] = lse_v;
+    if constexpr (D > 128) {
+        // The K stages hold half of the output tile: each lane stores its own
+        // 8-byte pieces (columns 32d + 8g + 4*hh .. +3 of its row) directly.
+        if (qrow < S) {
+            T* const orow = out + head_base + (int64_t)qrow * row_stride + 4 * hh;
+#pragma unroll
+            for (int d = 0; d < DB; ++d)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    if (!PAD || 32 * d + 8 * g < dv)
+                        *reinterpret_cast<u32x2*>(orow + 32 * d + 8 * g) =
+                            u32x2{Mfma<T>::pack2(o[d][4 * g] * inv, o[d][4 * g + 1] * inv),
+                                  Mfma<T>::pack2(o[d][4 * g + 2] * inv, o[d][4 * g + 3] * inv)};
+        }
+        return;
+    } else {
     // O leaves through LDS so that the global stores run along whole rows: a
     // lane holds one row's columns 32d + 8g + 4*hh .. +3, so it writes them
     // into the wave's 32 x D staging tile (16-byte chunk c of row r stored at
@@ -953,6 +969,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
                 *reinterpret_cast<u32x4*>(orow + (int64_t)(qw0 + r) * row_stride) = x;
         }
     }
+    }  // D <= 128
 }
 
 // ================================================================ block-sparse

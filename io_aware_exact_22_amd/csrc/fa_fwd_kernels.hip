@@ -25,8 +25,12 @@ static hipError_t launch_merge_cfg(const LaunchArgs& a) {
 
 hipError_t launch_merge_parts(const LaunchArgs& a) {
     if (a.dtype == kDtypeBf16)
-        return a.D <= 64 ? launch_merge_cfg<__bf16, 64>(a) : launch_merge_cfg<__bf16, 128>(a);
-    return a.D <= 64 ? launch_merge_cfg<_Float16, 64>(a) : launch_merge_cfg<_Float16, 128>(a);
+        return a.D <= 64    ? launch_merge_cfg<__bf16, 64>(a)
+               : a.D <= 128 ? launch_merge_cfg<__bf16, 128>(a)
+                            : launch_merge_cfg<__bf16, 256>(a);
+    return a.D <= 64    ? launch_merge_cfg<_Float16, 64>(a)
+           : a.D <= 128 ? launch_merge_cfg<_Float16, 128>(a)
+                        : launch_merge_cfg<_Float16, 256>(a);
 }
 
 template <typename T, int D>
@@ -71,10 +75,15 @@ static hipError_t launch_fp32(const LaunchArgs& a) {
 hipError_t launch_fwd(const LaunchArgs& a) {
     if (a.kv_lens) return launch_kvcache(a);
     switch (a.dtype) {
-    // bf16 / fp16: a head dimension below 64 or between 64 and 128 runs the
-    // kernel of the next one up, its extra columns zeros
-    case kDtypeBf16: return a.D <= 64 ? launch_mfma<__bf16, 64>(a) : launch_mfma<__bf16, 128>(a);
-    case kDtypeFp16: return a.D <= 64 ? launch_mfma<_Float16, 64>(a) : launch_mfma<_Float16, 128>(a);
+    // bf16 / fp16: a head dimension other than 64 and 128 runs the kernel of
+    // the next of 64, 128 and 256 up, its extra columns zeros (launch_mfma
+    // hands it to fa_fwd_padded.hip)
+    case kDtypeBf16:
+        return a.D <= 64 ? launch_mfma<__bf16, 64>(a)
+                         : a.D <= 128 ? launch_mfma<__bf16, 128>(a) : launch_fwd_padded(a);
+    case kDtypeFp16:
+        return a.D <= 64 ? launch_mfma<_Float16, 64>(a)
+                         : a.D <= 128 ? launch_mfma<_Float16, 128>(a) : launch_fwd_padded(a);
     default: return a.D == 64 ? launch_fp32<64>(a) : launch_fp32<128>(a);
     }
 }
@@ -92,7 +101,8 @@ constexpr int kMaxAutoSplits = 8;
 
 template <typename T, int D>
 static int auto_splits_cfg(const LaunchArgs& a) {
-    constexpr int BM = Tile<D, kMfmaWaves, kMfmaKeys>::BM;
+    constexpr int BN = D > 128 ? kWideKeys : kMfmaKeys;
+    constexpr int BM = Tile<D, kMfmaWaves, BN>::BM;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
@@ -104,7 +114,7 @@ static int auto_splits_cfg(const LaunchArgs& a) {
     int64_t longest = 1;
     for (int64_t t = 0; t < n_qt; ++t) {
         int64_t t0, t1;
-        q_tile_kv_range(m, t, BM, kMfmaKeys, &t0, &t1);
+        q_tile_kv_range(m, t, BM, BN, &t0, &t1);
         if (t1 - t0 > longest) longest = t1 - t0;
     }
     if (tiles >= 2 * (int64_t)cus) return 1;
@@ -116,25 +126,31 @@ static int auto_splits_cfg(const LaunchArgs& a) {
 
 int auto_splits(const LaunchArgs& a) {
     switch (a.dtype) {
-    case kDtypeBf16: return a.D <= 64 ? auto_splits_cfg<__bf16, 64>(a) : auto_splits_cfg<__bf16, 128>(a);
+    case kDtypeBf16:
+        return a.D <= 64    ? auto_splits_cfg<__bf16, 64>(a)
+               : a.D <= 128 ? auto_splits_cfg<__bf16, 128>(a)
+                            : auto_splits_cfg<__bf16, 256>(a);
     case kDtypeFp16:
-        return a.D <= 64 ? auto_splits_cfg<_Float16, 64>(a) : auto_splits_cfg<_Float16, 128>(a);
+        return a.D <= 64    ? auto_splits_cfg<_Float16, 64>(a)
+               : a.D <= 128 ? auto_splits_cfg<_Float16, 128>(a)
+                            : auto_splits_cfg<_Float16, 256>(a);
     default: return 1;  // fp32 inputs run in one part
     }
 }
 
-int64_t blocksparse_lut_bytes(int dtype, int64_t S, int64_t n_mask) {
+int64_t blocksparse_lut_bytes(int dtype, int64_t D, int64_t S, int64_t n_mask) {
     if (dtype == kDtypeFp32) return 0;  // the fp32 kernel reads the mask itself
     constexpr int BM = kMfmaWaves * kWaveRows;
-    const int64_t n_qt = (S + BM - 1) / BM, n_kt = (S + kMfmaKeys - 1) / kMfmaKeys;
+    const int64_t bn = kv_tile_keys(dtype, D, S, -1, -1);
+    const int64_t n_qt = (S + BM - 1) / BM, n_kt = (S + bn - 1) / bn;
     return n_mask * n_qt * sparse_lut_stride(n_kt) * 4;
 }
 
 int64_t q_tile_rows(int dtype, int64_t, int64_t, int64_t, int64_t) {
     return dtype == kDtypeFp32 ? kBM32 : kMfmaWaves * kWaveRows;
 }
-int64_t kv_tile_keys(int dtype, int64_t, int64_t, int64_t, int64_t) {
-    return dtype == kDtypeFp32 ? Lds32<64>::BN : kMfmaKeys;
+int64_t kv_tile_keys(int dtype, int64_t D, int64_t, int64_t, int64_t) {
+    return dtype == kDtypeFp32 ? Lds32<64>::BN : D > 128 ? kWideKeys : kMfmaKeys;
 }
 
 }  // namespace fa

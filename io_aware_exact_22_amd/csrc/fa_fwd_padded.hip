@@ -1,7 +1,8 @@
 // fa_fwd_padded.hip -- the bf16 / fp16 forward at head dimensions other than
-// 64 and 128 (any multiple of 16 from 16 to 128): the kernel for the next of
-// 64 and 128 with PAD = true, which reads the columns at or past the tensors'
-// own head dimension as zeros and never writes them.  The pages ask Tensor
+// 64 and 128 (any multiple of 16 up to 256): below 128, the kernel for the
+// next of 64 and 128 with PAD = true, which reads the columns at or past the
+// tensors' own head dimension as zeros and never writes them; above 128, the
+// D = 256 kernels of fa_fwd_wide_bf16.hip / fa_fwd_wide_fp16.hip.  The pages ask Tensor
 // Core shapes in multiples of 8 (section 4.2 of "FlashAttention技术解析：加速
 // GPT训练的核心优化"); 16 is the k step of the gfx950 MFMA.  A translation
 // unit of its own so that these instantiations compile beside the others.
@@ -13,6 +14,7 @@
 namespace fa {
 
 hipError_t launch_fwd_padded(const LaunchArgs& a) {
+    if (a.D > 128) return a.dtype == kDtypeBf16 ? launch_fwd_wide_bf16(a) : launch_fwd_wide_fp16(a);
     if (a.dtype == kDtypeBf16)
         return a.D < 64 ? launch_mfma_cfg<__bf16, 64, kMfmaWaves, kMfmaKeys, true>(a)
                         : launch_mfma_cfg<__bf16, 128, kMfmaWaves, kMfmaKeys, true>(a);

@@ -143,9 +143,11 @@ template <int D, int NW, int BN_ = 64> struct Tile {
     static_assert(DMA_PER_WAVE <= 4, "a wave's loads of a tile must fit the 12-bit immediate offset");
     static_assert(MAT % (1024 * NW) == 0, "tile must split into 1 KiB wave loads");
     static_assert(LDS_BYTES <= 65536, "LDS operand offsets must fit the 16-bit ds offset");
-    // chunk permutation of row r (D = 128: 16 chunks per row; D = 64: 8)
+    // chunk permutation of row r (D = 128: 16 chunks per row; D = 64: 8;
+    // D = 256: 32 chunks, two 256-byte bank lines per row, permuted within
+    // each 16-chunk half as at D = 128)
     __host__ __device__ static constexpr int swz(int r) {
-        if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+        if (D >= 128) return ((r & 3) << 2) | ((r >> 2) & 3);
         const int g = (r >> 1) & 7;
         return ((g & 1) << 2) | (g >> 1);
     }

@@ -11,8 +11,9 @@ constexpr int kDtypeFp32 = 0;
 constexpr int kDtypeFp16 = 1;
 constexpr int kDtypeBf16 = 2;
 
-// bf16 / fp16 kernels: 4 waves, 128-row Q tiles, 64-key K/V tiles
-constexpr int kMfmaWaves = 4, kMfmaKeys = 64;
+// bf16 / fp16 kernels: 4 waves, 128-row Q tiles, 64-key K/V tiles (32-key
+// tiles above D = 128, whose rows are twice as long)
+constexpr int kMfmaWaves = 4, kMfmaKeys = 64, kWideKeys = 32;
 // the most K/V parts per Q tile a KV-cache launch takes (FA_MAX_KV_SPLITS)
 constexpr int kMaxKvSplits = 64;
 
@@ -81,8 +82,11 @@ hipError_t launch_bwd(const BwdArgs& a);
 // validated arguments.
 hipError_t launch_fwd(const LaunchArgs& a);
 // The bf16 / fp16 forward at a head dimension other than 64 and 128 (a
-// multiple of 16 below 128), dense, split, block-sparse or paged.
+// multiple of 16 up to 256), dense, split, block-sparse or paged; above 128,
+// launch_fwd_wide_bf16 / _fp16 (one translation unit each).
 hipError_t launch_fwd_padded(const LaunchArgs& a);
+hipError_t launch_fwd_wide_bf16(const LaunchArgs& a);
+hipError_t launch_fwd_wide_fp16(const LaunchArgs& a);
 // The KV-cache forward (a.kv_lens set; bf16 / fp16), split or not.
 hipError_t launch_kvcache(const LaunchArgs& a);
 // The merge of a split launch's partial (O, LSE) into out / lse (bf16 / fp16).
@@ -90,7 +94,7 @@ hipError_t launch_merge_parts(const LaunchArgs& a);
 // K/V parts per Q tile for a KV-cache launch on the current device.
 int kvcache_auto_splits(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int dtype);
 // Bytes of the compacted tile lists a block-sparse launch needs (0 for fp32).
-int64_t blocksparse_lut_bytes(int dtype, int64_t S, int64_t n_mask);
+int64_t blocksparse_lut_bytes(int dtype, int64_t D, int64_t S, int64_t n_mask);
 
 // K/V parts per Q tile that fill the current device for this problem (1 for
 // fp32 inputs, or when the device cannot be queried).

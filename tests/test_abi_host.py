@@ -69,10 +69,11 @@ def check(**kw):
     ({"B": 0}, -2), ({"H": 0}, -2), ({"S": 0}, -2), ({"S": -5}, -2),
     ({"S": 1 << 40}, -2), ({"B": 1 << 40, "H": 1 << 30}, -2),
     ({"H": 131072, "D": 128, "S": 1}, -2), ({"H": 131071, "D": 128, "S": 1}, 0),
-    # bf16 / fp16: any multiple of 16 from 16 to 128; fp32: 64 or 128
-    ({"D": 96}, 0), ({"D": 16}, 0), ({"D": 48}, 0), ({"D": 112}, 0),
-    ({"D": 0}, -3), ({"D": 8}, -3), ({"D": 24}, -3), ({"D": 100}, -3), ({"D": 144}, -3),
-    ({"D": 256}, -3), ({"D": 96, "dtype": fa.FA_DTYPE_FP32}, -3),
+    # bf16 / fp16: any multiple of 16 from 16 to 256; fp32: 64 or 128
+    ({"D": 96}, 0), ({"D": 16}, 0), ({"D": 48}, 0), ({"D": 112}, 0), ({"D": 144}, 0),
+    ({"D": 256}, 0), ({"D": 0}, -3), ({"D": 8}, -3), ({"D": 24}, -3), ({"D": 100}, -3),
+    ({"D": 264}, -3), ({"D": 272}, -3), ({"D": 512}, -3),
+    ({"D": 96, "dtype": fa.FA_DTYPE_FP32}, -3), ({"D": 256, "dtype": fa.FA_DTYPE_FP32}, -3),
     ({"D": 64, "dtype": fa.FA_DTYPE_FP32}, 0), ({"D": 96, "dtype": fa.FA_DTYPE_FP16}, 0),
     ({"window_left": -2}, -4), ({"window_right": -7}, -4), ({"causal": 2}, -4),
     ({"dtype": 3}, -5), ({"dtype": -1}, -5),
@@ -99,7 +100,8 @@ def test_fa_fwd_rejects_before_any_hip_call():
                                                 (1, 2, 16384, 128, fa.FA_DTYPE_BF16, 4),
                                                 (3, 5, 389, 128, fa.FA_DTYPE_FP16, 16),
                                                 (2, 3, 300, 96, fa.FA_DTYPE_BF16, 5),
-                                                (1, 1, 77, 16, fa.FA_DTYPE_FP16, 2)])
+                                                (1, 1, 77, 16, fa.FA_DTYPE_FP16, 2),
+                                                (1, 2, 100, 256, fa.FA_DTYPE_BF16, 3)])
 def test_splitkv_workspace_size(B, H, S, D, dtype, ns):
     """fp32 partial O and LSE of every part: ns * B * H * S * (D + 1) * 4 bytes;
     nothing for one part or fp32 inputs."""
@@ -170,11 +172,18 @@ def test_bwd_rejects_before_any_hip_call(kw, status):
                                              (2, 4, 300, 1, fa.FA_DTYPE_FP32)])
 def test_blocksparse_workspace_size(B, H, S, nm, dtype):
     """One list row per (mask head, 128-row Q tile): a 4-int header and the
-    64-key tile count rounded up to 4 ints; nothing for fp32."""
+    K/V tile count (64-key tiles, 32-key above D = 128) rounded up to 4 ints;
+    nothing for fp32."""
     got = fa.fa_fwd_blocksparse_workspace_size(B, H, S, 128, dtype, nm)
     n_qt, n_kt = -(-S // 128), -(-S // 64)
     want = 0 if dtype == fa.FA_DTYPE_FP32 else nm * n_qt * (4 + -(-n_kt // 4) * 4) * 4
     assert got == want
+    if dtype != fa.FA_DTYPE_FP32:
+        n_kt32 = -(-S // 32)
+        assert fa.fa_fwd_blocksparse_workspace_size(B, H, S, 256, dtype, nm) == \
+            nm * n_qt * (4 + -(-n_kt32 // 4) * 4) * 4
+        assert fa.fa_fwd_blocksparse_workspace_size(B, H, S, 160, dtype, nm) == \
+            nm * n_qt * (4 + -(-n_kt32 // 4) * 4) * 4
     with pytest.raises(fa.FaError) as e:
         fa.fa_fwd_blocksparse_workspace_size(B, H, S, 128, dtype, 3)
     assert e.value.status == -12

@@ -2,9 +2,10 @@
 fa_fwd_splitkv, fa_fwd_paged and fa_fwd_blocksparse through the C ABI against
 the CPU oracle on the same seeded inputs, every element.
 
-The kernels run such a D as the next of 64 and 128 with the extra columns
-read as zeros and never written, so these cases check that the tensors' own
-row stride (H * D) is used everywhere, that the padding adds nothing to the
+The kernels run such a D as the next of 64, 128 and 256 with the extra
+columns read as zeros and never written (D = 256 itself runs its own kernel,
+with 32-key K/V tiles), so these cases check that the tensors' own row
+stride (H * D) is used everywhere, that the padding adds nothing to the
 scores or O, and that no byte outside O, LSE or the split partials is
 written (guard bands around the outputs).  H = 1 makes the tensors' rows
 shorter than the kernel's LDS rows.  Tolerances as for the dense forward
@@ -23,7 +24,7 @@ pytestmark = pytest.mark.gpu
 
 TOL_O = {torch.float16: 4e-3, torch.bfloat16: 2e-2}
 TOL_LSE = 1e-3
-D_OTHER = [16, 32, 48, 80, 96, 112]
+D_OTHER = [16, 32, 48, 80, 96, 112, 144, 192, 256]
 MASKS = [(False, (-1, -1)), (True, (-1, -1)), (False, (200, 100)), (True, (100, -1))]
 GUARD = 4096  # elements of guard band on each side of an output
 
@@ -87,7 +88,7 @@ def test_headdim_fwd(dtype, D, causal, window, B, S, H):
     compare(out, lse, ref_o, ref_l, dtype, what)
 
 
-@pytest.mark.parametrize("D", [32, 96])
+@pytest.mark.parametrize("D", [32, 96, 256])
 @pytest.mark.parametrize("causal", [False, True])
 def test_headdim_long_sequence(D, causal):
     """4100 rows (ragged last Q and K/V tiles), every element."""
@@ -104,7 +105,7 @@ def test_headdim_long_sequence(D, causal):
     compare(out, lse, ref_o, ref_l, dtype, what)
 
 
-@pytest.mark.parametrize("D", [16, 48, 80, 112])
+@pytest.mark.parametrize("D", [16, 48, 80, 112, 160, 256])
 @pytest.mark.parametrize("n_splits", [2, 5])
 @pytest.mark.parametrize("causal", [False, True])
 def test_headdim_splitkv(D, n_splits, causal):
@@ -144,7 +145,7 @@ def paginate(x, page_size, num_pages, seed):
     return pool.contiguous(), slots.to(torch.int32).to(x.device).contiguous()
 
 
-@pytest.mark.parametrize("D", [32, 80])
+@pytest.mark.parametrize("D", [32, 80, 208, 256])
 @pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (300, -1))])
 def test_headdim_paged(D, causal, window):
     """Paged K/V equals the contiguous result bit for bit, and the oracle."""
@@ -166,7 +167,7 @@ def test_headdim_paged(D, causal, window):
     compare(o1, l1, ref_o, ref_l, dtype, what)
 
 
-@pytest.mark.parametrize("D", [48, 96])
+@pytest.mark.parametrize("D", [48, 96, 224, 256])
 def test_headdim_blocksparse(D):
     """A random mask per (batch, head), 40% of the 128 x 64 blocks kept."""
     import io_aware_exact_22_amd as fa
@@ -191,7 +192,7 @@ def test_headdim_blocksparse(D):
     assert eo <= TOL_O[dtype] and el <= TOL_LSE, what
 
 
-@pytest.mark.parametrize("D,H", [(48, 1), (112, 2)])
+@pytest.mark.parametrize("D,H", [(48, 1), (112, 2), (176, 1), (256, 2)])
 def test_headdim_nonfinite_values_outside_the_mask(D, H):
     """NaN and inf in V at keys the causal mask hides from some rows of the
     same tile: the exact recomputation (columns past D read as zeros) gives
