@@ -47,8 +47,9 @@ typedef enum {
     FA_ERR_NULL = -1,     /* a required pointer is NULL */
     FA_ERR_SHAPE = -2,    /* B, H or S < 1, a size overflows int64 / the index range, or
                              64 rows of one tensor (64*H*D elements) exceed 2^31 - 1 bytes */
-    FA_ERR_HEAD_DIM = -3, /* D not supported (bf16 / fp16 forward: a multiple of 16 in
-                             [16, 256]; fp32, fa_bwd, fa_fwd_kvcache: 64 or 128) */
+    FA_ERR_HEAD_DIM = -3, /* D not supported (bf16 / fp16: a multiple of 16 in [16, 256]
+                             for the forward, [16, 128] for fa_bwd; fp32 and
+                             fa_fwd_kvcache: 64 or 128) */
     FA_ERR_WINDOW = -4,   /* window_left or window_right < -1, or causal not 0/1 */
     FA_ERR_DTYPE = -5,    /* dtype not one of fa_dtype_t */
     FA_ERR_SCALE = -6,    /* scale NaN, infinite or negative */
@@ -91,8 +92,8 @@ typedef enum {
  *          kernel for the next of them with the extra columns read as zeros
  *          and never written, and D above 128 uses 32-key K/V tiles.  fp32: 64
  *          or 128.  The same holds for fa_fwd_splitkv, fa_fwd_splitkv_noalloc,
- *          fa_fwd_blocksparse and fa_fwd_paged; fa_bwd and fa_fwd_kvcache
- *          take 64 or 128.
+ *          fa_fwd_blocksparse and fa_fwd_paged; fa_bwd takes multiples of 16
+ *          up to 128, fa_fwd_kvcache 64 or 128.
  * scale    softmax scale applied to q.k in fp32 (finite, >= 0); callers that
  *          want the pages' default pass 1/sqrt(D).
  * causal   0 or 1.
@@ -258,7 +259,10 @@ int fa_fwd_splitkv_workgroup_tile(int64_t B, int64_t H, int64_t S, int64_t D, in
  *          D_i), 16-byte aligned; owned by the caller, contents on return
  *          unspecified.
  * dtype    FA_DTYPE_BF16 or FA_DTYPE_FP16 (fp32 is not supported here:
- *          FA_ERR_DTYPE).  Other arguments as fa_fwd.
+ *          FA_ERR_DTYPE).
+ * D        a multiple of 16 from 16 to 128 (not 64 or 128: the kernels for the
+ *          next of them, the extra columns read as zeros and never written).
+ *          Other arguments as fa_fwd.
  * Pointers as in fa_fwd: 16-byte aligned tensors, lse 4-byte aligned; the
  * outputs and the workspace must not overlap the inputs or each other
  * (FA_ERR_ALIAS, FA_ERR_WORKSPACE).  Validation happens before any HIP call.

@@ -27,18 +27,19 @@ bool overlaps(const void* p, int64_t n, const void* q, int64_t m) {
 int64_t elem_size(int dtype) { return dtype == fa::kDtypeFp32 ? 4 : 2; }
 
 // Shape / window / dtype checks shared by the entry points; *tensor_bytes and
-// *lse_bytes are set on success.  Head dimensions: the bf16 / fp16 forward
-// kernels take any multiple of 16 from 16 to 256 (other than 64, 128 and 256
-// they run the next kernel up with zero columns); fp32 inputs and the
-// fixed_d callers (the backward, the KV-cache forward) take 64 or 128.
+// *lse_bytes are set on success.  Head dimensions: bf16 / fp16 take any
+// multiple of 16 from 16 to d_max (other than 64, 128 and 256 the kernels run
+// the next of those up with zero columns): 256 for the forward, 128 for the
+// backward; d_max = 0 (the KV-cache forward) and fp32 inputs take 64 or 128.
+constexpr int64_t kFwdMaxD = 256, kBwdMaxD = 128;
 int check_problem(int64_t B, int64_t H, int64_t S, int64_t D, int causal, int64_t wl, int64_t wr,
-                  int dtype, int64_t* tensor_bytes, int64_t* lse_bytes, bool fixed_d = false) {
+                  int dtype, int64_t* tensor_bytes, int64_t* lse_bytes, int64_t d_max = kFwdMaxD) {
     if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16)
         return FA_ERR_DTYPE;
     if (B < 1 || H < 1 || S < 1) return FA_ERR_SHAPE;
-    if (fixed_d || dtype == FA_DTYPE_FP32) {
+    if (d_max == 0 || dtype == FA_DTYPE_FP32) {
         if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
-    } else if (D < 16 || D > 256 || D % 16 != 0) {
+    } else if (D < 16 || D > d_max || D % 16 != 0) {
         return FA_ERR_HEAD_DIM;
     }
     if ((causal != 0 && causal != 1) || wl < -1 || wr < -1) return FA_ERR_WINDOW;
@@ -70,8 +71,8 @@ FA_API const char* fa_status_string(int status) {
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "B, H and S must be >= 1 and the sizes must fit the index ranges";
     case FA_ERR_HEAD_DIM:
-        return "unsupported head dimension D (bf16 / fp16 forward: a multiple of 16 from 16 to 256; "
-               "fp32 inputs, fa_bwd and fa_fwd_kvcache: 64 or 128)";
+        return "unsupported head dimension D (bf16 / fp16: a multiple of 16 from 16 to 256 for the "
+               "forward, to 128 for fa_bwd; fp32 inputs and fa_fwd_kvcache: 64 or 128)";
     case FA_ERR_WINDOW: return "causal must be 0 or 1 and window bounds must be >= -1";
     case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_FP32, FA_DTYPE_FP16 or FA_DTYPE_BF16";
     case FA_ERR_SCALE: return "scale must be finite and >= 0";
@@ -326,7 +327,7 @@ FA_API int fa_bwd_workspace_size(int64_t B, int64_t H, int64_t S, int64_t D, int
                                  int64_t* bytes) {
     if (!bytes) return FA_ERR_NULL;
     int64_t nbytes, lbytes;
-    const int rc = check_problem(B, H, S, D, 0, -1, -1, dtype, &nbytes, &lbytes, true);
+    const int rc = check_problem(B, H, S, D, 0, -1, -1, dtype, &nbytes, &lbytes, kBwdMaxD);
     if (rc != FA_OK) return rc;
     if (dtype == FA_DTYPE_FP32) return FA_ERR_DTYPE;
     *bytes = lbytes;  // fp32 [B, H, S], the size of lse
@@ -340,7 +341,7 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* out, 
     if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
     int64_t nbytes = 0, lbytes = 0;
     int rc = check_problem(B, H, S, D, causal, window_left, window_right, dtype, &nbytes, &lbytes,
-                           true);
+                           kBwdMaxD);
     if (rc != FA_OK) return rc;
     if (dtype == FA_DTYPE_FP32) return FA_ERR_DTYPE;
     if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_SCALE;
@@ -535,7 +536,7 @@ int64_t kvcache_workspace_bytes(int64_t B, int64_t H, int64_t S_q, int64_t D, in
 // cache capacity, and the dtypes the KV-cache kernels take (bf16, fp16).
 int check_kvcache_problem(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D, int causal,
                           int64_t wl, int64_t wr, int dtype, int64_t* q_bytes, int64_t* lse_bytes) {
-    const int rc = check_problem(B, H, S_q, D, causal, wl, wr, dtype, q_bytes, lse_bytes, true);
+    const int rc = check_problem(B, H, S_q, D, causal, wl, wr, dtype, q_bytes, lse_bytes, 0);
     if (rc != FA_OK) return rc;
     if (dtype == FA_DTYPE_FP32) return FA_ERR_DTYPE;
     if (S_k < 1 || S_k > INT32_MAX) return FA_ERR_SHAPE;

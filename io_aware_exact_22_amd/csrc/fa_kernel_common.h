@@ -1,5 +1,5 @@
 // fa_kernel_common.h -- device-side building blocks shared by the forward
-// (fa_fwd_kernels.hip) and backward (fa_bwd_kernels.hip) gfx950 kernels:
+// (fa_fwd_device.h) and backward (fa_bwd_device.h) gfx950 kernels:
 // vector types, constants, the MFMA dtype traits, the score-register key
 // map, the LDS tile geometry with its XOR swizzle and the direct-to-LDS tile
 // loader.  Not part of the public ABI.

@@ -75,8 +75,10 @@ struct BwdArgs {
     int dtype;
     hipStream_t stream;
 };
-// Enqueues the three backward kernels for validated arguments.
+// Enqueues the three backward kernels for validated arguments; D other than
+// 64 and 128 (a multiple of 16 up to 128) through launch_bwd_padded.
 hipError_t launch_bwd(const BwdArgs& a);
+hipError_t launch_bwd_padded(const BwdArgs& a);
 
 // Enqueues the forward kernel (and, for a split launch, the merge kernel) for
 // validated arguments.

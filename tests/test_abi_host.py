@@ -143,16 +143,20 @@ def test_bwd_workspace_size():
     with pytest.raises(fa.FaError) as e:
         fa.fa_bwd_workspace_size(2, 16, 2048, 64, fa.FA_DTYPE_FP32)
     assert e.value.status == -5
-    with pytest.raises(fa.FaError) as e:
-        fa.fa_bwd_workspace_size(2, 16, 2048, 80, fa.FA_DTYPE_BF16)
-    assert e.value.status == -3
+    # bf16 / fp16: any multiple of 16 up to 128
+    assert fa.fa_bwd_workspace_size(2, 16, 2048, 80, fa.FA_DTYPE_BF16) == 2 * 16 * 2048 * 4
+    for bad in (72, 144, 256):
+        with pytest.raises(fa.FaError) as e:
+            fa.fa_bwd_workspace_size(2, 16, 2048, bad, fa.FA_DTYPE_BF16)
+        assert e.value.status == -3
 
 
 DO, DQ, DK, DV = 7 << 32, 8 << 32, 9 << 32, 10 << 32
 
 
 @pytest.mark.parametrize("kw,status", [
-    ({"dq": 0}, -1), ({"dout": 0}, -1), ({"dtype": fa.FA_DTYPE_FP32}, -5), ({"D": 96}, -3),
+    ({"dq": 0}, -1), ({"dout": 0}, -1), ({"dtype": fa.FA_DTYPE_FP32}, -5), ({"D": 100}, -3),
+    ({"D": 144}, -3), ({"D": 256}, -3),
     ({"dq": Q}, -8), ({"dk": DV}, -8), ({"dv": LSE}, -8), ({"dq": DQ + 8}, -7), ({"lse": LSE + 2}, -7),
     ({"ws": 0}, -10), ({"wsb": 100}, -10), ({"ws": DQ}, -10), ({"ws": WS + 4}, -10),
     ({"scale": -1.0}, -6), ({"window_left": -3}, -4),

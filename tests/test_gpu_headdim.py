@@ -216,3 +216,41 @@ def test_headdim_nonfinite_values_outside_the_mask(D, H):
     el = float(np.max(np.abs(lse.double().cpu().numpy() - ref_l)))
     print(f"nonfinite D{D} H{H}: max|dO|={eo:.3e} max|dLSE|={el:.3e}", flush=True)
     assert eo <= TOL_O[dtype] and el <= TOL_LSE
+
+
+# ---------------------------------------------------------------- backward
+TOL_GRAD = {torch.float16: 4e-3, torch.bfloat16: 2e-2}
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("D", [16, 48, 80, 112])
+@pytest.mark.parametrize("causal,window", MASKS)
+@pytest.mark.parametrize("B,S,H", [(2, 389, 3), (1, 300, 1)])
+def test_headdim_bwd(dtype, D, causal, window, B, S, H):
+    """dq, dk, dv against the oracle's fp64 gradients (max-abs within
+    TOL_GRAD x max(1, max |reference|)), with NaN guard bands around each
+    gradient and around the row-dot workspace that must stay untouched."""
+    import io_aware_exact_22_amd as fa
+
+    q, k, v = make_qkv(B, S, H, D, dtype, 1000 + D)
+    do = make_qkv(B, S, H, D, dtype, 1001 + D)[0]
+    scale = 1.0 / math.sqrt(D)
+    what = f"bwd B{B} S{S} H{H} D{D} {dtype} causal={causal} window={window}"
+    print("run", what, flush=True)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    out, lse = fa.flash_attn_fwd(qd, kd, vd, causal=causal, window_size=window)
+    grads = [guarded((B, S, H, D), dtype) for _ in range(3)]
+    ws, wbuf = guarded((B * H * S,), torch.float32)
+    fa.flash_attn_bwd(dod, qd, kd, vd, out, lse, causal=causal, window_size=window, workspace=ws,
+                      dq=grads[0][0], dk=grads[1][0], dv=grads[2][0])
+    torch.cuda.synchronize()
+    assert all(guards_intact(b) for _, b in grads) and guards_intact(wbuf), \
+        "a write landed outside a gradient or the workspace"
+    ref = oracle.bwd(q, k, v, do, scale, causal, window)
+    for name, (g, _), r in zip(("dq", "dk", "dv"), grads, ref):
+        g = g.double().cpu().numpy()
+        assert np.all(np.isfinite(g)), f"{what}: non-finite {name}"
+        bound = TOL_GRAD[dtype] * max(1.0, float(np.max(np.abs(r))))
+        err = float(np.max(np.abs(g - r)))
+        print(f"{what}: {name} max err {err:.3e} (bound {bound:.3e})", flush=True)
+        assert err <= bound, f"{what}: {name} error {err} > {bound}"
