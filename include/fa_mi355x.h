@@ -48,8 +48,8 @@ typedef enum {
     FA_ERR_SHAPE = -2,    /* B, H or S < 1, a size overflows int64 / the index range, or
                              64 rows of one tensor (64*H*D elements) exceed 2^31 - 1 bytes */
     FA_ERR_HEAD_DIM = -3, /* D not supported (bf16 / fp16: a multiple of 16 in [16, 256]
-                             for the forward, [16, 128] for fa_bwd; fp32 and
-                             fa_fwd_kvcache: 64 or 128) */
+                             for the forward, [16, 128] for fa_bwd and
+                             fa_fwd_kvcache; fp32: 64 or 128) */
     FA_ERR_WINDOW = -4,   /* window_left or window_right < -1, or causal not 0/1 */
     FA_ERR_DTYPE = -5,    /* dtype not one of fa_dtype_t */
     FA_ERR_SCALE = -6,    /* scale NaN, infinite or negative */
@@ -92,8 +92,8 @@ typedef enum {
  *          kernel for the next of them with the extra columns read as zeros
  *          and never written, and D above 128 uses 32-key K/V tiles.  fp32: 64
  *          or 128.  The same holds for fa_fwd_splitkv, fa_fwd_splitkv_noalloc,
- *          fa_fwd_blocksparse and fa_fwd_paged; fa_bwd takes multiples of 16
- *          up to 128, fa_fwd_kvcache 64 or 128.
+ *          fa_fwd_blocksparse and fa_fwd_paged; fa_bwd and fa_fwd_kvcache take
+ *          multiples of 16 up to 128.
  * scale    softmax scale applied to q.k in fp32 (finite, >= 0); callers that
  *          want the pages' default pass 1/sqrt(D).
  * causal   0 or 1.
@@ -381,7 +381,9 @@ int fa_fwd_paged(const void* q, const void* k_pages, const void* v_pages,
  * in fa_fwd_splitkv -- the usual case for decoding, where B * H query blocks
  * of one row each cannot fill the device.
  *
- * q, out      device, contiguous [B, S_q, H, D] of `dtype` (bf16 or fp16).
+ * q, out      device, contiguous [B, S_q, H, D] of `dtype` (bf16 or fp16); D a
+ *             multiple of 16 from 16 to 128 (one query per sequence runs a
+ *             vector-ALU kernel at D = 64 and 128, the MFMA kernel otherwise).
  * lse         device, contiguous fp32 [B, H, S_q].
  * k_cache, v_cache  device, read only: contiguous [B, S_k, H, D] caches when
  *             block_table is NULL, else page pools [num_pages, page_size, H, D]

@@ -14,8 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libfa_mi355x.so")
 SOURCES = ["fa_api.hip", "fa_fwd_kernels.hip", "fa_fwd_padded.hip", "fa_fwd_wide_bf16.hip",
-           "fa_fwd_wide_fp16.hip", "fa_fwd_kvcache.hip", "fa_bwd_kernels.hip",
-           "fa_bwd_padded.hip"]
+           "fa_fwd_wide_fp16.hip", "fa_fwd_kvcache.hip", "fa_fwd_kvcache_padded.hip",
+           "fa_bwd_kernels.hip", "fa_bwd_padded.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -30,8 +30,9 @@ int64_t elem_size(int dtype) { return dtype == fa::kDtypeFp32 ? 4 : 2; }
 // *lse_bytes are set on success.  Head dimensions: bf16 / fp16 take any
 // multiple of 16 from 16 to d_max (other than 64, 128 and 256 the kernels run
 // the next of those up with zero columns): 256 for the forward, 128 for the
-// backward; d_max = 0 (the KV-cache forward) and fp32 inputs take 64 or 128.
-constexpr int64_t kFwdMaxD = 256, kBwdMaxD = 128;
+// backward and the KV-cache forward; fp32 inputs (and d_max = 0) take 64 or
+// 128.
+constexpr int64_t kFwdMaxD = 256, kBwdMaxD = 128, kKvcMaxD = 128;
 int check_problem(int64_t B, int64_t H, int64_t S, int64_t D, int causal, int64_t wl, int64_t wr,
                   int dtype, int64_t* tensor_bytes, int64_t* lse_bytes, int64_t d_max = kFwdMaxD) {
     if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16)
@@ -72,7 +73,7 @@ FA_API const char* fa_status_string(int status) {
     case FA_ERR_SHAPE: return "B, H and S must be >= 1 and the sizes must fit the index ranges";
     case FA_ERR_HEAD_DIM:
         return "unsupported head dimension D (bf16 / fp16: a multiple of 16 from 16 to 256 for the "
-               "forward, to 128 for fa_bwd; fp32 inputs and fa_fwd_kvcache: 64 or 128)";
+               "forward, to 128 for fa_bwd and fa_fwd_kvcache; fp32 inputs: 64 or 128)";
     case FA_ERR_WINDOW: return "causal must be 0 or 1 and window bounds must be >= -1";
     case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_FP32, FA_DTYPE_FP16 or FA_DTYPE_BF16";
     case FA_ERR_SCALE: return "scale must be finite and >= 0";
@@ -536,7 +537,7 @@ int64_t kvcache_workspace_bytes(int64_t B, int64_t H, int64_t S_q, int64_t D, in
 // cache capacity, and the dtypes the KV-cache kernels take (bf16, fp16).
 int check_kvcache_problem(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D, int causal,
                           int64_t wl, int64_t wr, int dtype, int64_t* q_bytes, int64_t* lse_bytes) {
-    const int rc = check_problem(B, H, S_q, D, causal, wl, wr, dtype, q_bytes, lse_bytes, 0);
+    const int rc = check_problem(B, H, S_q, D, causal, wl, wr, dtype, q_bytes, lse_bytes, kKvcMaxD);
     if (rc != FA_OK) return rc;
     if (dtype == FA_DTYPE_FP32) return FA_ERR_DTYPE;
     if (S_k < 1 || S_k > INT32_MAX) return FA_ERR_SHAPE;
@@ -564,7 +565,7 @@ FA_API int fa_fwd_kvcache_auto_splits(int64_t B, int64_t H, int64_t S_q, int64_t
     int64_t qb, lb;
     const int rc = check_kvcache_problem(B, H, S_q, S_k, D, 0, -1, -1, dtype, &qb, &lb);
     if (rc != FA_OK) return rc;
-    *n_splits = fa::kvcache_auto_splits(B, H, S_q, S_k, dtype);
+    *n_splits = fa::kvcache_auto_splits(B, H, S_q, S_k, D, dtype);
     return FA_OK;
 }
 

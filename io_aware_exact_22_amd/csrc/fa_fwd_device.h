@@ -198,7 +198,6 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     int pg_stride, int pg_rows, int pg_count, const int* __restrict__ kv_lens, int kv_cap,
     int dv_in) {
     static_assert(!(SPLIT && SPARSE), "a block-sparse launch runs in one part");
-    static_assert(!(PAD && KVC), "the KV-cache forward takes head dimensions 64 and 128");
     static_assert(!(SPARSE && PAGED), "block-sparse and paged K/V do not combine");
     static_assert(!(SPARSE && KVC), "a block mask does not apply to a KV cache");
     typedef Tile<D, NW, BN_> L;

@@ -13,6 +13,7 @@
 #include <stdint.h>
 
 #include "fa_fwd_device.h"
+#include "fa_fwd_launch_cfg.h"
 #include "fa_launch.h"
 #include "fa_schedule.h"
 
@@ -255,50 +256,14 @@ static hipError_t launch_decode_cfg(const LaunchArgs& a) {
 template <typename T, int D>
 static hipError_t launch_kvcache_cfg(const LaunchArgs& a) {
     if (a.S == 1) return launch_decode_cfg<T, D>(a);  // one query per sequence
-    constexpr int NW = kMfmaWaves, BN = kMfmaKeys;
-    constexpr int BM = Tile<D, NW, BN>::BM;
-    const int n_qt = (int)((a.S + BM - 1) / BM);
-    const int64_t n_wg = a.B * a.H * n_qt;
-    const bool paged = a.pg_table != nullptr;
-    const int pg_stride = (int)a.pg_stride, pg_rows = paged ? (int)a.pg_rows : 1,
-              pg_count = (int)a.pg_count;
-    const int cap = (int)a.kv_cap;
-    if (a.n_splits <= 1) {
-        if (paged)
-            hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, false, true, true>),
-                               dim3((unsigned)n_wg), dim3(NW * 64), 0, a.stream, (const T*)a.q,
-                               (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
-                               (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr,
-                               nullptr, nullptr, 0, 0, a.pg_table, pg_stride, pg_rows, pg_count,
-                               a.kv_lens, cap, (int)a.D);
-        else
-            hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, false, false, true>),
-                               dim3((unsigned)n_wg), dim3(NW * 64), 0, a.stream, (const T*)a.q,
-                               (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
-                               (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr,
-                               nullptr, nullptr, 0, 0, nullptr, 0, 1, 0, a.kv_lens, cap, (int)a.D);
-        return hipGetLastError();
-    }
-    if (paged)
-        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, true, false, true, true>),
-                           dim3((unsigned)(n_wg * a.n_splits)), dim3(NW * 64), 0, a.stream,
-                           (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B,
-                           (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt,
-                           a.n_splits, a.part_o, a.part_lse, nullptr, 0, 0, a.pg_table, pg_stride,
-                           pg_rows, pg_count, a.kv_lens, cap, (int)a.D);
-    else
-        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, true, false, false, true>),
-                           dim3((unsigned)(n_wg * a.n_splits)), dim3(NW * 64), 0, a.stream,
-                           (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B,
-                           (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt,
-                           a.n_splits, a.part_o, a.part_lse, nullptr, 0, 0, nullptr, 0, 1, 0,
-                           a.kv_lens, cap, (int)a.D);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_merge_parts(a);
+    return launch_kvc_mfma_cfg<T, D, false>(a);
 }
 
 hipError_t launch_kvcache(const LaunchArgs& a) {
+    // a head dimension other than 64 and 128 (a multiple of 16 up to 128):
+    // the MFMA kernel of the next of them with PAD (fa_fwd_kvcache_padded.hip), also
+    // for one query per sequence
+    if (a.D != 64 && a.D != 128) return launch_kvcache_padded(a);
     if (a.dtype == kDtypeBf16)
         return a.D == 64 ? launch_kvcache_cfg<__bf16, 64>(a) : launch_kvcache_cfg<__bf16, 128>(a);
     return a.D == 64 ? launch_kvcache_cfg<_Float16, 64>(a) : launch_kvcache_cfg<_Float16, 128>(a);
@@ -310,7 +275,7 @@ hipError_t launch_kvcache(const LaunchArgs& a) {
 // most kMaxKvSplits and at most one part per 4 K/V tiles of a full cache (a
 // part's partials and the merge cost about one tile step); 1 when the grid
 // already has two workgroups per unit or the device cannot be queried.
-int kvcache_auto_splits(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int dtype) {
+int kvcache_auto_splits(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D, int dtype) {
     (void)dtype;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -319,7 +284,7 @@ int kvcache_auto_splits(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int dtyp
         return 1;
     }
     const int64_t kv_tiles = (S_k + kMfmaKeys - 1) / kMfmaKeys;
-    if (S_q == 1) {
+    if (S_q == 1 && (D == 64 || D == 128)) {
         // the one-query kernel: a wave per (sequence, head, part).  Its HBM
         // stream peaks at about two waves per compute unit (more waves, each
         // on a shorter range, measured slower), each with at least 4 chunks

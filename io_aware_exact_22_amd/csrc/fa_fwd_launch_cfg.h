@@ -1,8 +1,9 @@
-// fa_fwd_launch_cfg.h -- the launch of fa_fwd_mfma_kernel for a dense, split,
-// block-sparse or paged forward, shared by fa_fwd_kernels.hip (head
-// dimensions 64 and 128) and fa_fwd_padded.hip (the others, PAD = true: the
-// kernel for the next of 64 and 128 with zero columns), so that the two sets
-// of instantiations compile in parallel.  Not part of the public ABI.
+// fa_fwd_launch_cfg.h -- the launches of fa_fwd_mfma_kernel for a dense,
+// split, block-sparse or paged forward and for the KV-cache forward, shared by
+// fa_fwd_kernels.hip and fa_fwd_kvcache.hip (head dimensions 64 and 128),
+// fa_fwd_padded.hip (PAD = true: the kernel for the next of 64 and 128 with
+// zero columns) and fa_fwd_wide_*.hip (D above 128), so that the sets of
+// instantiations compile in parallel.  Not part of the public ABI.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -69,6 +70,53 @@ hipError_t launch_mfma_cfg(const LaunchArgs& a) {
                            a.n_splits, a.part_o, a.part_lse, nullptr, 0, 0, nullptr, 0, 1, 0,
                            nullptr, 0, (int)a.D);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_merge_parts(a);
+}
+
+// The KV-cache forward on the MFMA kernel (KVC = true), split or not, paged
+// or not (fa_fwd_kvcache.hip; with PAD, fa_fwd_kvcache_padded.hip).
+template <typename T, int D, bool PAD>
+hipError_t launch_kvc_mfma_cfg(const LaunchArgs& a) {
+    constexpr int NW = kMfmaWaves, BN = kMfmaKeys;
+    constexpr int BM = Tile<D, NW, BN>::BM;
+    const int n_qt = (int)((a.S + BM - 1) / BM);
+    const int64_t n_wg = a.B * a.H * n_qt;
+    const bool paged = a.pg_table != nullptr;
+    const int pg_stride = (int)a.pg_stride, pg_rows = paged ? (int)a.pg_rows : 1,
+              pg_count = (int)a.pg_count;
+    const int cap = (int)a.kv_cap;
+    if (a.n_splits <= 1) {
+        if (paged)
+            hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, false, true, true, PAD>),
+                               dim3((unsigned)n_wg), dim3(NW * 64), 0, a.stream, (const T*)a.q,
+                               (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
+                               (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr,
+                               nullptr, nullptr, 0, 0, a.pg_table, pg_stride, pg_rows, pg_count,
+                               a.kv_lens, cap, (int)a.D);
+        else
+            hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, false, false, true, PAD>),
+                               dim3((unsigned)n_wg), dim3(NW * 64), 0, a.stream, (const T*)a.q,
+                               (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
+                               (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr,
+                               nullptr, nullptr, 0, 0, nullptr, 0, 1, 0, a.kv_lens, cap, (int)a.D);
+        return hipGetLastError();
+    }
+    if (paged)
+        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, true, false, true, true, PAD>),
+                           dim3((unsigned)(n_wg * a.n_splits)), dim3(NW * 64), 0, a.stream,
+                           (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B,
+                           (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt,
+                           a.n_splits, a.part_o, a.part_lse, nullptr, 0, 0, a.pg_table, pg_stride,
+                           pg_rows, pg_count, a.kv_lens, cap, (int)a.D);
+    else
+        hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, true, false, false, true, PAD>),
+                           dim3((unsigned)(n_wg * a.n_splits)), dim3(NW * 64), 0, a.stream,
+                           (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B,
+                           (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt,
+                           a.n_splits, a.part_o, a.part_lse, nullptr, 0, 0, nullptr, 0, 1, 0,
+                           a.kv_lens, cap, (int)a.D);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_merge_parts(a);
 }

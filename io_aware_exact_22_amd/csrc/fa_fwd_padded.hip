@@ -2,7 +2,8 @@
 // 64 and 128 (any multiple of 16 up to 256): below 128, the kernel for the
 // next of 64 and 128 with PAD = true, which reads the columns at or past the
 // tensors' own head dimension as zeros and never writes them; above 128, the
-// D = 256 kernels of fa_fwd_wide_bf16.hip / fa_fwd_wide_fp16.hip.  The pages ask Tensor
+// D = 256 kernels of fa_fwd_wide_bf16.hip / fa_fwd_wide_fp16.hip.  (The
+// KV-cache forward at such a D: fa_fwd_kvcache_padded.hip.)  The pages ask Tensor
 // Core shapes in multiples of 8 (section 4.2 of "FlashAttention技术解析：加速
 // GPT训练的核心优化"); 16 is the k step of the gfx950 MFMA.  A translation
 // unit of its own so that these instantiations compile beside the others.

@@ -89,12 +89,14 @@ hipError_t launch_fwd(const LaunchArgs& a);
 hipError_t launch_fwd_padded(const LaunchArgs& a);
 hipError_t launch_fwd_wide_bf16(const LaunchArgs& a);
 hipError_t launch_fwd_wide_fp16(const LaunchArgs& a);
-// The KV-cache forward (a.kv_lens set; bf16 / fp16), split or not.
+// The KV-cache forward (a.kv_lens set; bf16 / fp16), split or not; at a head
+// dimension other than 64 and 128, launch_kvcache_padded.
 hipError_t launch_kvcache(const LaunchArgs& a);
+hipError_t launch_kvcache_padded(const LaunchArgs& a);
 // The merge of a split launch's partial (O, LSE) into out / lse (bf16 / fp16).
 hipError_t launch_merge_parts(const LaunchArgs& a);
 // K/V parts per Q tile for a KV-cache launch on the current device.
-int kvcache_auto_splits(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int dtype);
+int kvcache_auto_splits(int64_t B, int64_t H, int64_t S_q, int64_t S_k, int64_t D, int dtype);
 // Bytes of the compacted tile lists a block-sparse launch needs (0 for fp32).
 int64_t blocksparse_lut_bytes(int dtype, int64_t D, int64_t S, int64_t n_mask);
 

@@ -463,7 +463,7 @@ def test_kvcache_workspace_size(B, H, S_q, D, dtype, ns):
 @pytest.mark.parametrize("kw,status", [
     ({}, None),
     ({"q": 0}, -1), ({"kc": 0}, -1), ({"vc": 0}, -1), ({"sl": 0}, -1), ({"out": 0}, -1),
-    ({"D": 96}, -3), ({"dtype": fa.FA_DTYPE_FP32}, -5), ({"Sk": 0}, -2), ({"Sq": 0}, -2),
+    ({"D": 100}, -3), ({"D": 144}, -3), ({"dtype": fa.FA_DTYPE_FP32}, -5), ({"Sk": 0}, -2), ({"Sq": 0}, -2),
     ({"scale": float("nan")}, -6), ({"window_left": -3}, -4),
     ({"kc": KC + 8}, -7), ({"sl": SL + 2}, -7), ({"lse": LSE + 2}, -7),
     ({"out": KC}, -8), ({"lse": SL}, -8), ({"out": VC + 4096}, -8),

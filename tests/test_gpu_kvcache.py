@@ -224,3 +224,53 @@ def test_kvcache_raw_c_call_on_a_side_stream():
     s.synchronize()
     ref_o, ref_l = oracle.fwd_kvcache(q, k, v, [123, 500], 1 / math.sqrt(D), True)
     compare(out.cpu(), lse.cpu(), ref_o, ref_l, torch.bfloat16, "kvcache raw C side stream")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("D", [16, 48, 80, 112])
+@pytest.mark.parametrize("causal,window", [(True, (-1, -1)), (True, (40, -1)), (False, (16, 16))])
+@pytest.mark.parametrize("S_q", [1, 5])
+@pytest.mark.parametrize("n_splits", [1, 3])
+def test_kvcache_other_head_dims(dtype, D, causal, window, S_q, n_splits):
+    """Head dimensions other than 64 and 128 (the MFMA kernel of the next of
+    them, its extra columns zeros; also for one query per sequence), ragged
+    cache lengths, against the oracle."""
+    B, S_k, H = 3, 300, 2
+    q, k, v = case(B, S_q, S_k, H, D, dtype, 1200 + D + S_q)
+    lens = [max(0, S_q - 3), 177, S_k]
+    out, lse, scale = run(q, k, v, lens, causal, window, n_splits)
+    ref_o, ref_l = oracle.fwd_kvcache(q, k, v, lens, scale, causal, window)
+    compare(out, lse, ref_o, ref_l, dtype, f"kvcache {dtype} D{D} S_q={S_q} causal={causal} "
+                                           f"{window} x{n_splits}")
+
+
+@pytest.mark.parametrize("D", [32, 96])
+@pytest.mark.parametrize("S_q", [1, 4])
+def test_kvcache_other_head_dims_paged(D, S_q):
+    """Paged pools (NaN in every unused row) at a padded head dimension equal
+    the contiguous cache bit for bit, and the oracle."""
+    B, S_k, H, dtype, page_size = 2, 256, 3, torch.bfloat16, 64
+    q, k, v = case(B, S_q, S_k, H, D, dtype, 1300 + D)
+    lens = [100, 256]
+    n_pg = S_k // page_size
+    perm = torch.randperm(B * n_pg + 3, generator=torch.Generator().manual_seed(5))[:B * n_pg]
+    table = perm.view(B, n_pg).to(torch.int32)
+    pools = []
+    for t in (k, v):
+        pool = torch.full((B * n_pg + 3, page_size, H, D), float("nan"), dtype=dtype)
+        for b in range(B):
+            rows = t[b, :lens[b]]
+            for p in range(-(-lens[b] // page_size)):
+                seg = rows[p * page_size:(p + 1) * page_size]
+                pool[table[b, p], :seg.shape[0]] = seg
+        pools.append(pool)
+    out, lse, scale = run(q, pools[0], pools[1], lens, True, (-1, -1), 2, block_table=table)
+    kd, vd = k.clone(), v.clone()
+    for b in range(B):
+        kd[b, lens[b]:] = float("nan")
+        vd[b, lens[b]:] = float("nan")
+    out_c, lse_c, _ = run(q, kd, vd, lens, True, (-1, -1), 2)
+    assert torch.equal(out.view(torch.int16), out_c.view(torch.int16))
+    assert torch.equal(lse, lse_c)
+    ref_o, ref_l = oracle.fwd_kvcache(q, k, v, lens, scale, True)
+    compare(out, lse, ref_o, ref_l, dtype, f"kvcache paged D{D} S_q={S_q}")
