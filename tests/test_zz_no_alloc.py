@@ -54,6 +54,9 @@ CALLS = [
      (1, 700, 2, 64, torch.float16, False, (100, 30), 3)],
     [(1, 4097, 8, 64, torch.float16, False, (-1, -1), 5),
      (2, 389, 3, 128, torch.bfloat16, True, (64, -1), 2)],
+    # head dimensions other than 64 and 128 (D = 256 and a padded 48)
+    [(1, 2000, 4, 256, torch.bfloat16, True, (-1, -1), 3),
+     (2, 500, 3, 48, torch.float16, False, (100, 30), 2)],
 ]
 
 
