@@ -47,9 +47,9 @@ typedef enum {
     FA_ERR_NULL = -1,     /* a required pointer is NULL */
     FA_ERR_SHAPE = -2,    /* B, H or S < 1, a size overflows int64 / the index range, or
                              64 rows of one tensor (64*H*D elements) exceed 2^31 - 1 bytes */
-    FA_ERR_HEAD_DIM = -3, /* D not supported (bf16 / fp16: a multiple of 16 in [16, 256]
-                             for the forward, [16, 128] for fa_bwd and
-                             fa_fwd_kvcache; fp32: 64 or 128) */
+    FA_ERR_HEAD_DIM = -3, /* D not supported (a multiple of 16 in [16, 256] for the
+                             bf16 / fp16 forward, [16, 128] for fp32 inputs, fa_bwd
+                             and fa_fwd_kvcache) */
     FA_ERR_WINDOW = -4,   /* window_left or window_right < -1, or causal not 0/1 */
     FA_ERR_DTYPE = -5,    /* dtype not one of fa_dtype_t */
     FA_ERR_SCALE = -6,    /* scale NaN, infinite or negative */
@@ -90,8 +90,8 @@ typedef enum {
  *          of "FlashAttention技术解析：加速GPT训练的核心优化"; 16 is the k
  *          step of the gfx950 MFMA); a D other than 64, 128 and 256 runs the
  *          kernel for the next of them with the extra columns read as zeros
- *          and never written, and D above 128 uses 32-key K/V tiles.  fp32: 64
- *          or 128.  The same holds for fa_fwd_splitkv, fa_fwd_splitkv_noalloc,
+ *          and never written, and D above 128 uses 32-key K/V tiles.  fp32: a
+ *          multiple of 16 up to 128.  The same holds for fa_fwd_splitkv, fa_fwd_splitkv_noalloc,
  *          fa_fwd_blocksparse and fa_fwd_paged; fa_bwd and fa_fwd_kvcache take
  *          multiples of 16 up to 128.
  * scale    softmax scale applied to q.k in fp32 (finite, >= 0); callers that

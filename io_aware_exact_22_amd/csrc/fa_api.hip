@@ -27,18 +27,18 @@ bool overlaps(const void* p, int64_t n, const void* q, int64_t m) {
 int64_t elem_size(int dtype) { return dtype == fa::kDtypeFp32 ? 4 : 2; }
 
 // Shape / window / dtype checks shared by the entry points; *tensor_bytes and
-// *lse_bytes are set on success.  Head dimensions: bf16 / fp16 take any
-// multiple of 16 from 16 to d_max (other than 64, 128 and 256 the kernels run
-// the next of those up with zero columns): 256 for the forward, 128 for the
-// backward and the KV-cache forward; fp32 inputs (and d_max = 0) take 64 or
-// 128.
-constexpr int64_t kFwdMaxD = 256, kBwdMaxD = 128, kKvcMaxD = 128;
+// *lse_bytes are set on success.  Head dimensions: any multiple of 16 from 16
+// to d_max (other than 64, 128 and 256 the kernels run the next of those up
+// with zero columns): 256 for the bf16 / fp16 forward, 128 for fp32 inputs,
+// the backward and the KV-cache forward (which reject fp32 by dtype).
+constexpr int64_t kFwdMaxD = 256, kBwdMaxD = 128, kKvcMaxD = 128, kFp32MaxD = 128;
 int check_problem(int64_t B, int64_t H, int64_t S, int64_t D, int causal, int64_t wl, int64_t wr,
                   int dtype, int64_t* tensor_bytes, int64_t* lse_bytes, int64_t d_max = kFwdMaxD) {
     if (dtype != FA_DTYPE_FP32 && dtype != FA_DTYPE_FP16 && dtype != FA_DTYPE_BF16)
         return FA_ERR_DTYPE;
     if (B < 1 || H < 1 || S < 1) return FA_ERR_SHAPE;
-    if (d_max == 0 || dtype == FA_DTYPE_FP32) {
+    if (dtype == FA_DTYPE_FP32 && d_max > kFp32MaxD) d_max = kFp32MaxD;
+    if (d_max == 0) {
         if (D != 64 && D != 128) return FA_ERR_HEAD_DIM;
     } else if (D < 16 || D > d_max || D % 16 != 0) {
         return FA_ERR_HEAD_DIM;
@@ -72,8 +72,8 @@ FA_API const char* fa_status_string(int status) {
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_SHAPE: return "B, H and S must be >= 1 and the sizes must fit the index ranges";
     case FA_ERR_HEAD_DIM:
-        return "unsupported head dimension D (bf16 / fp16: a multiple of 16 from 16 to 256 for the "
-               "forward, to 128 for fa_bwd and fa_fwd_kvcache; fp32 inputs: 64 or 128)";
+        return "unsupported head dimension D (a multiple of 16 from 16 to 256 for the bf16 / fp16 "
+               "forward, to 128 for fp32 inputs, fa_bwd and fa_fwd_kvcache)";
     case FA_ERR_WINDOW: return "causal must be 0 or 1 and window bounds must be >= -1";
     case FA_ERR_DTYPE: return "dtype must be FA_DTYPE_FP32, FA_DTYPE_FP16 or FA_DTYPE_BF16";
     case FA_ERR_SCALE: return "scale must be finite and >= 0";

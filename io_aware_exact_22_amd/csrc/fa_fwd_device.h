@@ -1100,14 +1100,17 @@ template <int D> struct Lds32 {
 // PAGED: k and v are pools [pg_count, pg_rows, H, D] read through the block
 // table (pg_rows a multiple of the K/V tile; a page index outside the pool
 // reads as zeros).
-template <int D, bool SPARSE, bool PAGED>
+// PAD: the tensors' head dimension is dv_in < D (a multiple of 16); the
+// columns past it are read as zeros and never stored.
+template <int D, bool SPARSE, bool PAGED, bool PAD = false>
 __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     float* __restrict__ out, float* __restrict__ lse, int B, int H, int S, float c, int causal,
     int wl, int wr, int n_qt, const uint8_t* __restrict__ bmask, int sp_heads, int n_qb, int n_kb,
     int block_m, int block_n, const int* __restrict__ pg_table, int pg_stride, int pg_rows,
-    int pg_count) {
+    int pg_count, int dv_in) {
     typedef Lds32<D> L;
+    const int dv = PAD ? dv_in : D;
     constexpr int BN = L::BN;
     constexpr int DB = D / 32;
     __shared__ float ks[BN * L::KS];
@@ -1123,8 +1126,8 @@ __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
     const MaskSpec ms{S, causal, wl, wr};
     int64_t kt0, kt1;
     q_tile_kv_range(ms, qt, kBM32, BN, &kt0, &kt1);
-    const int64_t row_stride = (int64_t)H * D;
-    const int64_t head_base = ((int64_t)bb * S * H + h) * D;
+    const int64_t row_stride = (int64_t)H * dv;
+    const int64_t head_base = ((int64_t)bb * S * H + h) * dv;
     const int qw0 = qt * kBM32 + wave * kWaveRows;
     const int qrow = qw0 + ql;
     const uint8_t* mrow = nullptr;  // SPARSE: the Q tile's row of the block mask
@@ -1139,7 +1142,8 @@ __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
         const bool ok = qrow < S;
         const float* qp = q + head_base + (int64_t)(ok ? qrow : 0) * row_stride;
 #pragma unroll
-        for (int kk = 0; kk < D / 2; ++kk) qf[kk] = ok ? qp[2 * kk + hh] : 0.f;
+        for (int kk = 0; kk < D / 2; ++kk)
+            qf[kk] = ok && (!PAD || 2 * kk + hh < dv) ? qp[2 * kk + hh] : 0.f;
     }
     float m_run = kNegInf, l_run = 0.f;
     f32x16 o[DB];
@@ -1160,9 +1164,11 @@ __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
         for (int id = tid; id < BN * (D / 4); id += kThreads32) {
             const int r = id / (D / 4), cc = id % (D / 4);
             const int64_t key = k0 + r;
-            const bool ok = key < S && tile_row0 >= 0;
-            const int64_t off = PAGED ? ((ok ? tile_row0 + r : 0) * H + h) * D + cc * 4
-                                      : head_base + (ok ? key : 0) * row_stride + cc * 4;
+            const bool ok = key < S && tile_row0 >= 0 && (!PAD || 4 * cc < dv);
+            // PAD: a column past dv reads (and discards) element 0 of a valid row
+            const int col = PAD && !ok ? 0 : cc * 4;
+            const int64_t off = PAGED ? ((ok ? tile_row0 + r : 0) * H + h) * dv + col
+                                      : head_base + (ok ? key : 0) * row_stride + col;
             f32x4 xk = *reinterpret_cast<const f32x4*>(k + off);
             f32x4 xv = *reinterpret_cast<const f32x4*>(v + off);
 #pragma unroll
@@ -1230,7 +1236,7 @@ __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
     if (any_nonfinite<DB>(o)) {
         constexpr int DH = D / 2;
         float acc[DH];
-        const int64_t kv_base = PAGED ? (int64_t)h * D : head_base;
+        const int64_t kv_base = PAGED ? (int64_t)h * dv : head_base;
         auto tile_of = [&](int pos, int& k0, int64_t& row0, bool& valid) __attribute__((always_inline)) {
             k0 = pos * BN;
             row0 = k0;
@@ -1249,14 +1255,15 @@ __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
             return ok && (!SPARSE || mrow[key / block_n] != 0);
         };
         const float* q_half = qrow < S ? q + head_base + (int64_t)qrow * row_stride + hh * DH : nullptr;
-        exact_row<float, D, BN, false>(q_half, k + kv_base, v + kv_base, row_stride, hh, D, S, (int)kt0,
+        exact_row<float, D, BN, PAD>(q_half, k + kv_base, v + kv_base, row_stride, hh, dv, S, (int)kt0,
                                 (int)kt1, tile_of, allowed, c, m_fin, inv, acc);
         if (qrow < S) {
             float* eo = out + head_base + (int64_t)qrow * row_stride + hh * DH;
 #pragma unroll
             for (int c4 = 0; c4 < DH / 4; ++c4)
-                *reinterpret_cast<f32x4*>(eo + 4 * c4) =
-                    f32x4{acc[4 * c4], acc[4 * c4 + 1], acc[4 * c4 + 2], acc[4 * c4 + 3]};
+                if (!PAD || hh * DH + 4 * c4 < dv)
+                    *reinterpret_cast<f32x4*>(eo + 4 * c4) =
+                        f32x4{acc[4 * c4], acc[4 * c4 + 1], acc[4 * c4 + 2], acc[4 * c4 + 3]};
             if (hh == 0) lse[((int64_t)bb * H + h) * S + qrow] = lse_v;
         }
         return;
@@ -1269,7 +1276,7 @@ __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
             for (int g = 0; g < 4; ++g) {
                 f32x4 w = {o[d][4 * g] * inv, o[d][4 * g + 1] * inv, o[d][4 * g + 2] * inv,
                            o[d][4 * g + 3] * inv};
-                *reinterpret_cast<f32x4*>(op + 32 * d + 8 * g) = w;
+                if (!PAD || 32 * d + 8 * g < dv) *reinterpret_cast<f32x4*>(op + 32 * d + 8 * g) = w;
             }
         if (hh == 0) lse[((int64_t)bb * H + h) * S + qrow] = lse_v;
     }

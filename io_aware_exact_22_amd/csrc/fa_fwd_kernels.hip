@@ -40,38 +40,6 @@ static hipError_t launch_mfma(const LaunchArgs& a) {
 }
 
 
-// fp32 inputs always run in one part (n_splits is ignored): the fp32 kernel
-// has no split path.
-template <int D>
-static hipError_t launch_fp32(const LaunchArgs& a) {
-    const int n_qt = (int)((a.S + kBM32 - 1) / kBM32);
-    const int64_t n_wg = a.B * a.H * n_qt;
-    if (a.bmask) {
-        hipLaunchKernelGGL((fa_fwd_fp32_kernel<D, true, false>), dim3((unsigned)n_wg),
-                           dim3(kThreads32), 0, a.stream, (const float*)a.q, (const float*)a.k,
-                           (const float*)a.v, (float*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S,
-                           a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, a.bmask, (int)a.n_mask,
-                           (int)((a.S + a.block_m - 1) / a.block_m),
-                           (int)((a.S + a.block_n - 1) / a.block_n), (int)a.block_m, (int)a.block_n,
-                           nullptr, 0, 1, 0);
-        return hipGetLastError();
-    }
-    if (a.pg_table) {
-        hipLaunchKernelGGL((fa_fwd_fp32_kernel<D, false, true>), dim3((unsigned)n_wg),
-                           dim3(kThreads32), 0, a.stream, (const float*)a.q, (const float*)a.k,
-                           (const float*)a.v, (float*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S,
-                           a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, nullptr, 0, 0, 0, 1, 1,
-                           a.pg_table, (int)a.pg_stride, (int)a.pg_rows, (int)a.pg_count);
-        return hipGetLastError();
-    }
-    hipLaunchKernelGGL((fa_fwd_fp32_kernel<D, false, false>), dim3((unsigned)n_wg),
-                       dim3(kThreads32), 0, a.stream, (const float*)a.q, (const float*)a.k,
-                       (const float*)a.v, (float*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S, a.c,
-                       a.causal, (int)a.wl, (int)a.wr, n_qt, nullptr, 0, 0, 0, 1, 1, nullptr, 0, 1,
-                       0);
-    return hipGetLastError();
-}
-
 hipError_t launch_fwd(const LaunchArgs& a) {
     if (a.kv_lens) return launch_kvcache(a);
     switch (a.dtype) {
@@ -84,7 +52,9 @@ hipError_t launch_fwd(const LaunchArgs& a) {
     case kDtypeFp16:
         return a.D <= 64 ? launch_mfma<_Float16, 64>(a)
                          : a.D <= 128 ? launch_mfma<_Float16, 128>(a) : launch_fwd_padded(a);
-    default: return a.D == 64 ? launch_fp32<64>(a) : launch_fp32<128>(a);
+    default:  // fp32: other head dimensions (multiples of 16 up to 128) in fa_fwd_padded.hip
+        if (a.D != 64 && a.D != 128) return launch_fwd_padded(a);
+        return a.D == 64 ? launch_fp32<64, false>(a) : launch_fp32<128, false>(a);
     }
 }
 

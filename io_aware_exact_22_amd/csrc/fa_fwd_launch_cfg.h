@@ -121,4 +121,36 @@ hipError_t launch_kvc_mfma_cfg(const LaunchArgs& a) {
     return launch_merge_parts(a);
 }
 
+// fp32 inputs always run in one part (n_splits is ignored): the fp32 kernel
+// has no split path.
+template <int D, bool PAD>
+hipError_t launch_fp32(const LaunchArgs& a) {
+    const int n_qt = (int)((a.S + kBM32 - 1) / kBM32);
+    const int64_t n_wg = a.B * a.H * n_qt;
+    if (a.bmask) {
+        hipLaunchKernelGGL((fa_fwd_fp32_kernel<D, true, false, PAD>), dim3((unsigned)n_wg),
+                           dim3(kThreads32), 0, a.stream, (const float*)a.q, (const float*)a.k,
+                           (const float*)a.v, (float*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S,
+                           a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, a.bmask, (int)a.n_mask,
+                           (int)((a.S + a.block_m - 1) / a.block_m),
+                           (int)((a.S + a.block_n - 1) / a.block_n), (int)a.block_m, (int)a.block_n,
+                           nullptr, 0, 1, 0, (int)a.D);
+        return hipGetLastError();
+    }
+    if (a.pg_table) {
+        hipLaunchKernelGGL((fa_fwd_fp32_kernel<D, false, true, PAD>), dim3((unsigned)n_wg),
+                           dim3(kThreads32), 0, a.stream, (const float*)a.q, (const float*)a.k,
+                           (const float*)a.v, (float*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S,
+                           a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, nullptr, 0, 0, 0, 1, 1,
+                           a.pg_table, (int)a.pg_stride, (int)a.pg_rows, (int)a.pg_count, (int)a.D);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((fa_fwd_fp32_kernel<D, false, false, PAD>), dim3((unsigned)n_wg),
+                       dim3(kThreads32), 0, a.stream, (const float*)a.q, (const float*)a.k,
+                       (const float*)a.v, (float*)a.out, a.lse, (int)a.B, (int)a.H, (int)a.S, a.c,
+                       a.causal, (int)a.wl, (int)a.wr, n_qt, nullptr, 0, 0, 0, 1, 1, nullptr, 0, 1,
+                       0, (int)a.D);
+    return hipGetLastError();
+}
+
 }  // namespace fa

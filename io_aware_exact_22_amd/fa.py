@@ -390,7 +390,7 @@ def flash_attn_fwd(q, k, v, softmax_scale: float | None = None, causal: bool = F
     """Exact attention forward on the GPU.
 
     q, k, v: CUDA (HIP) tensors [B, S, H, D], contiguous, one dtype (fp32,
-    fp16 or bf16); D a multiple of 16 from 16 to 256 for fp16 / bf16, 64 or
+    fp16 or bf16); D a multiple of 16 from 16 to 256 for fp16 / bf16, up to
     128 for fp32.  softmax_scale None means 1/sqrt(D).
     Returns (out [B, S, H, D] in the input dtype, lse [B, H, S] fp32).  Runs
     on ``stream`` (a torch stream) or torch's current stream, asynchronously.

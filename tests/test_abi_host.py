@@ -73,7 +73,8 @@ def check(**kw):
     ({"D": 96}, 0), ({"D": 16}, 0), ({"D": 48}, 0), ({"D": 112}, 0), ({"D": 144}, 0),
     ({"D": 256}, 0), ({"D": 0}, -3), ({"D": 8}, -3), ({"D": 24}, -3), ({"D": 100}, -3),
     ({"D": 264}, -3), ({"D": 272}, -3), ({"D": 512}, -3),
-    ({"D": 96, "dtype": fa.FA_DTYPE_FP32}, -3), ({"D": 256, "dtype": fa.FA_DTYPE_FP32}, -3),
+    ({"D": 96, "dtype": fa.FA_DTYPE_FP32}, 0), ({"D": 144, "dtype": fa.FA_DTYPE_FP32}, -3),
+    ({"D": 256, "dtype": fa.FA_DTYPE_FP32}, -3),
     ({"D": 64, "dtype": fa.FA_DTYPE_FP32}, 0), ({"D": 96, "dtype": fa.FA_DTYPE_FP16}, 0),
     ({"window_left": -2}, -4), ({"window_right": -7}, -4), ({"causal": 2}, -4),
     ({"dtype": 3}, -5), ({"dtype": -1}, -5),

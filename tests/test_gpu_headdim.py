@@ -8,8 +8,9 @@ with 32-key K/V tiles), so these cases check that the tensors' own row
 stride (H * D) is used everywhere, that the padding adds nothing to the
 scores or O, and that no byte outside O, LSE or the split partials is
 written (guard bands around the outputs).  H = 1 makes the tensors' rows
-shorter than the kernel's LDS rows.  Tolerances as for the dense forward
-(max-abs): O <= 4e-3 fp16, <= 2e-2 bf16; LSE <= 1e-3.
+shorter than the kernel's LDS rows.  fp32 inputs take D up to 128.
+Tolerances as for the dense forward (max-abs): O <= 1e-4 fp32, <= 4e-3 fp16,
+<= 2e-2 bf16; LSE <= 1e-3.
 """
 import math
 
@@ -22,7 +23,7 @@ from fa_inputs import make_qkv, random_block_mask
 
 pytestmark = pytest.mark.gpu
 
-TOL_O = {torch.float16: 4e-3, torch.bfloat16: 2e-2}
+TOL_O = {torch.float32: 1e-4, torch.float16: 4e-3, torch.bfloat16: 2e-2}
 TOL_LSE = 1e-3
 D_OTHER = [16, 32, 48, 80, 96, 112, 144, 192, 256]
 MASKS = [(False, (-1, -1)), (True, (-1, -1)), (False, (200, 100)), (True, (100, -1))]
@@ -70,12 +71,15 @@ def run_guarded(fn, B, S, H, D, dtype):
     return out, lse
 
 
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16, torch.float32])
 @pytest.mark.parametrize("D", D_OTHER)
 @pytest.mark.parametrize("causal,window", MASKS)
 @pytest.mark.parametrize("B,S,H", [(2, 389, 3), (1, 300, 1)])
 def test_headdim_fwd(dtype, D, causal, window, B, S, H):
     import io_aware_exact_22_amd as fa
+
+    if dtype == torch.float32 and D > 128:
+        pytest.skip("fp32 inputs take head dimensions up to 128")
 
     q, k, v = make_qkv(B, S, H, D, dtype, 400 + D)
     what = f"fwd B{B} S{S} H{H} D{D} {dtype} causal={causal} window={window}"
@@ -145,13 +149,15 @@ def paginate(x, page_size, num_pages, seed):
     return pool.contiguous(), slots.to(torch.int32).to(x.device).contiguous()
 
 
-@pytest.mark.parametrize("D", [32, 80, 208, 256])
+@pytest.mark.parametrize("D,dtype", [(32, torch.bfloat16), (80, torch.bfloat16),
+                                     (208, torch.bfloat16), (256, torch.bfloat16),
+                                     (48, torch.float32), (112, torch.float32)])
 @pytest.mark.parametrize("causal,window", [(False, (-1, -1)), (True, (300, -1))])
-def test_headdim_paged(D, causal, window):
+def test_headdim_paged(D, dtype, causal, window):
     """Paged K/V equals the contiguous result bit for bit, and the oracle."""
     import io_aware_exact_22_amd as fa
 
-    B, S, H, dtype, page = 2, 777, 3, torch.bfloat16, 128
+    B, S, H, page = 2, 777, 3, 128
     q, k, v = make_qkv(B, S, H, D, dtype, 700 + D)
     what = f"paged D{D} causal={causal} window={window}"
     print("run", what, flush=True)
@@ -167,12 +173,14 @@ def test_headdim_paged(D, causal, window):
     compare(o1, l1, ref_o, ref_l, dtype, what)
 
 
-@pytest.mark.parametrize("D", [48, 96, 224, 256])
-def test_headdim_blocksparse(D):
+@pytest.mark.parametrize("D,dtype", [(48, torch.float16), (96, torch.float16),
+                                     (224, torch.float16), (256, torch.float16),
+                                     (80, torch.float32)])
+def test_headdim_blocksparse(D, dtype):
     """A random mask per (batch, head), 40% of the 128 x 64 blocks kept."""
     import io_aware_exact_22_amd as fa
 
-    B, S, H, dtype = 2, 777, 3, torch.float16
+    B, S, H = 2, 777, 3
     q, k, v = make_qkv(B, S, H, D, dtype, 800 + D)
     mask = random_block_mask(B * H, -(-S // 128), -(-S // 64), 0.4, 900 + D)
     what = f"blocksparse D{D}"
@@ -192,14 +200,16 @@ def test_headdim_blocksparse(D):
     assert eo <= TOL_O[dtype] and el <= TOL_LSE, what
 
 
-@pytest.mark.parametrize("D,H", [(48, 1), (112, 2), (176, 1), (256, 2)])
-def test_headdim_nonfinite_values_outside_the_mask(D, H):
+@pytest.mark.parametrize("D,H,dtype", [(48, 1, torch.bfloat16), (112, 2, torch.bfloat16),
+                                       (176, 1, torch.bfloat16), (256, 2, torch.bfloat16),
+                                       (32, 2, torch.float32)])
+def test_headdim_nonfinite_values_outside_the_mask(D, H, dtype):
     """NaN and inf in V at keys the causal mask hides from some rows of the
     same tile: the exact recomputation (columns past D read as zeros) gives
     the oracle's NaN pattern, finite rows within tolerance."""
     import io_aware_exact_22_amd as fa
 
-    B, S, dtype = 1, 300, torch.bfloat16
+    B, S = 1, 300
     q, k, v = make_qkv(B, S, H, D, dtype, 950 + D)
     v[0, 100, 0, 3] = float("nan")      # rows 96..99 share its K/V tile but not the key
     v[0, 200, H - 1, D - 1] = float("inf")
