@@ -76,8 +76,6 @@ template <int N> __device__ inline float row_sum(float x) {
     return x;
 }
 
-// a buffer offset past any record count: the load returns zeros
-constexpr int kOutOfRange = 0x7ff00000;
 
 template <typename T, int D, int CK, bool PAGED, bool SPLIT>
 __global__ __launch_bounds__(64) void fa_decode_kernel(
@@ -143,7 +141,9 @@ __global__ __launch_bounds__(64) void fa_decode_kernel(
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int key = k0 + KPI * i + r;
-            const int off = (key >= lo && key < L) ? (KPI * i + r) * row_bytes + 16 * cc : kOutOfRange;
+            // a key outside [lo, L): an offset past every record count (a chunk's
+            // records are below 2^31 bytes), so the load returns zeros
+            const int off = (key >= lo && key < L) ? (KPI * i + r) * row_bytes + 16 * cc : kDmaPastRecords;
             s.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
             s.v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
         }

@@ -34,7 +34,8 @@ constexpr int kBufferFlags = 0x00020000;
 // before the tile, so that per-lane offsets stay >= 0 after the up to 3 KiB
 // of immediate offset are taken out of them; and an offset that lies past
 // every record count of such a resource (one tile plus kDmaBias is below
-// 2^31 + 4096 bytes), whose loads write zeros.
+// 2^31 + 4096 bytes) or of any one-tile resource, whose loads return (or
+// write) zeros.
 constexpr int kDmaBias = 4096;
 constexpr int kDmaPastRecords = (int)0xFFFF0000u;
 // log2-domain slack before the running reference max is moved (weights <= 2^8)
