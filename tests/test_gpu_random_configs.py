@@ -1,6 +1,7 @@
 """GPU parity on seeded random configurations: every entry point of the
 forward (fa_fwd, fa_fwd_splitkv, fa_fwd_paged, fa_fwd_blocksparse,
-fa_fwd_kvcache) through the C ABI against the CPU oracle, every element, on
+fa_fwd_kvcache) and the backward (fa_bwd) through the C ABI against the CPU
+oracle, every element, on
 shapes, head dimensions, dtypes and masks drawn from one fixed seed per case
 (small sizes: B <= 3, H <= 5, S <= 700), so that combinations no hand-written
 case names are still checked.  Tolerances as for the dense forward (max-abs):
@@ -154,3 +155,43 @@ def test_random_kvcache_configuration(seed):
         ref_o, ref_l = oracle.fwd_kvcache(q, k, v, lens, scale, causal, window)
     torch.cuda.synchronize()
     compare(out, lse, ref_o, ref_l, dtype, what)
+
+
+TOL_GRAD = {torch.float16: 4e-3, torch.bfloat16: 2e-2}
+
+
+def draw_bwd(seed):
+    r = random.Random(20_000 + seed)
+    dtype = r.choice(DTYPES[:2])
+    D = 16 * r.randint(1, 8)
+    B, H = r.randint(1, 3), r.randint(1, 4)
+    S = r.choice([r.randint(1, 64), r.randint(65, 300), r.randint(301, 600)])
+    causal = r.random() < 0.5
+    window = (r.choice([-1, -1, r.randint(0, 200)]), r.choice([-1, -1, r.randint(0, 200)]))
+    return B, H, S, D, dtype, causal, window
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_backward_configuration(seed):
+    """fa_bwd on random shapes, head dimensions and masks: dq, dk, dv within
+    TOL_GRAD x max(1, max |reference|) of the oracle's fp64 gradients."""
+    import io_aware_exact_22_amd as fa
+
+    B, H, S, D, dtype, causal, window = draw_bwd(seed)
+    what = f"bwd seed {seed}: B{B} H{H} S{S} D{D} {dtype} causal={causal} window={window}"
+    print("run", what, flush=True)
+    q, k, v = make_qkv(B, S, H, D, dtype, 11000 + seed)
+    do = make_qkv(B, S, H, D, dtype, 11500 + seed)[0]
+    scale = 1.0 / math.sqrt(D)
+    qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
+    out, lse = fa.flash_attn_fwd(qd, kd, vd, causal=causal, window_size=window)
+    dq, dk, dv = fa.flash_attn_bwd(dod, qd, kd, vd, out, lse, causal=causal, window_size=window)
+    torch.cuda.synchronize()
+    ref = oracle.bwd(q, k, v, do, scale, causal, window)
+    for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        g = g.double().cpu().numpy()
+        assert np.all(np.isfinite(g)), f"{what}: non-finite {name}"
+        bound = TOL_GRAD[dtype] * max(1.0, float(np.max(np.abs(r))))
+        err = float(np.max(np.abs(g - r)))
+        print(f"{what}: {name} max err {err:.3e} (bound {bound:.3e})", flush=True)
+        assert err <= bound, f"{what}: {name} error {err} > {bound}"
