@@ -1150,34 +1150,75 @@ __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
 #pragma unroll
     for (int d = 0; d < DB; ++d) o[d] = f32x16{0};
 
-    for (int64_t kt = kt0; kt < kt1; ++kt) {
+    // K/V tiles go global -> registers -> LDS; the loads of tile kt + 1 are
+    // issued right after tile kt is stored, so their latency runs under tile
+    // kt's MFMAs.  NLD f32x4 per thread and matrix; the tile's element (r, cc)
+    // of load i is id = tid + i * kThreads32.  At D = 128 the registers hold
+    // the next K tile only (both would spill): V is loaded when it is stored.
+    constexpr int NLD = BN * (D / 4) / kThreads32;
+    constexpr bool kAheadV = D <= 64;
+    static_assert(NLD * kThreads32 == BN * (D / 4), "the threads split a tile evenly");
+    f32x4 xk[NLD], xv[kAheadV ? NLD : 1];
+    int64_t fetched_row0 = 0;  // PAGED: pool row of the fetched tile's first key (-1: outside)
+    auto tile_ok = [&](int64_t k0, int64_t row0, int i, int& r, int& cc) __attribute__((always_inline)) {
+        const int id = tid + i * kThreads32;
+        r = id / (D / 4);
+        cc = id % (D / 4);
+        return k0 + r < S && row0 >= 0 && (!PAD || 4 * cc < dv);
+    };
+    // element offset of load i of the tile at k0 (a key past S, a page
+    // outside the pool or (PAD) a column past dv reads, and discards, element
+    // 0 of a valid row)
+    auto tile_off = [&](int64_t k0, int64_t row0, int i, bool& ok) __attribute__((always_inline)) {
+        int r, cc;
+        ok = tile_ok(k0, row0, i, r, cc);
+        const int col = !ok ? 0 : cc * 4;
+        return PAGED ? ((ok ? row0 + r : 0) * H + h) * dv + col
+                     : head_base + (ok ? k0 + r : 0) * row_stride + col;
+    };
+    auto fetch = [&](int64_t kt) __attribute__((always_inline)) {
         const int64_t k0 = kt * BN;
-        if (SPARSE && mrow[k0 / block_n] == 0) continue;  // the same for the whole workgroup
-        int64_t tile_row0 = 0;  // PAGED: pool row of the tile's first key (-1: outside the pool)
+        int64_t row0 = 0;
         if (PAGED) {
             const int page = pg_table[(int64_t)bb * pg_stride + k0 / pg_rows];
-            tile_row0 = (unsigned)page < (unsigned)pg_count
-                            ? (int64_t)page * pg_rows + k0 % pg_rows
-                            : -1;
+            row0 = (unsigned)page < (unsigned)pg_count ? (int64_t)page * pg_rows + k0 % pg_rows : -1;
         }
-        __syncthreads();
-        for (int id = tid; id < BN * (D / 4); id += kThreads32) {
-            const int r = id / (D / 4), cc = id % (D / 4);
-            const int64_t key = k0 + r;
-            const bool ok = key < S && tile_row0 >= 0 && (!PAD || 4 * cc < dv);
-            // PAD: a column past dv reads (and discards) element 0 of a valid row
-            const int col = PAD && !ok ? 0 : cc * 4;
-            const int64_t off = PAGED ? ((ok ? tile_row0 + r : 0) * H + h) * dv + col
-                                      : head_base + (ok ? key : 0) * row_stride + col;
-            f32x4 xk = *reinterpret_cast<const f32x4*>(k + off);
-            f32x4 xv = *reinterpret_cast<const f32x4*>(v + off);
+        fetched_row0 = row0;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                ks[r * L::KS + cc * 4 + t] = ok ? xk[t] : 0.f;
-                vs[r * L::VS + cc * 4 + t] = ok ? xv[t] : 0.f;
+        for (int i = 0; i < NLD; ++i) {
+            bool ok;
+            const int64_t off = tile_off(k0, row0, i, ok);
+            xk[i] = *reinterpret_cast<const f32x4*>(k + off);
+            if (kAheadV) xv[kAheadV ? i : 0] = *reinterpret_cast<const f32x4*>(v + off);
+        }
+    };
+    if (kt0 < kt1) fetch(kt0);
+    for (int64_t kt = kt0; kt < kt1; ++kt) {
+        const int64_t k0 = kt * BN;
+        // SPARSE: a dropped tile (the same for the whole workgroup) is neither
+        // stored nor computed, but the next one is still fetched
+        const bool keep = !SPARSE || mrow[k0 / block_n] != 0;
+        __syncthreads();  // every wave is done with the previous tile
+        if (keep) {
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) {
+                int r, cc;
+                const bool ok = tile_ok(k0, fetched_row0, i, r, cc);
+                f32x4 x = xv[kAheadV ? i : 0];
+                if (!kAheadV) {
+                    bool ok2;
+                    x = *reinterpret_cast<const f32x4*>(v + tile_off(k0, fetched_row0, i, ok2));
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    ks[r * L::KS + cc * 4 + t] = ok ? xk[i][t] : 0.f;
+                    vs[r * L::VS + cc * 4 + t] = ok ? x[t] : 0.f;
+                }
             }
         }
+        if (kt + 1 < kt1) fetch(kt + 1);
         __syncthreads();
+        if (!keep) continue;
         if (tile_fully_masked(ms, qw0, qw0 + kWaveRows - 1, k0, BN)) continue;
         // S^T (32 keys x 32 queries): A = K row (lane % 32), d = 2*kk + hh
         f32x16 s = f32x16{0};
