@@ -101,12 +101,14 @@ template <> __device__ inline void load8<float>(const float* p, float (&x)[8]) {
     }
 }
 
-// The normalised O columns [hh * D/2, hh * D/2 + D/2) of this lane's query row:
-// sum over the keys of K/V positions [w0, w1) that allowed(key) admits of
-// p_j * v_j, p_j = exp2(c * s_j - m_ref) * inv_l with the row's final
-// reference m_ref and normaliser inv_l = 1 / l.  The two lanes of a row (wave
-// halves) split the dot product s_j = q . k_j by the same column halves and
-// add the halves in the same order.  q_half points at the row's columns of
+// The normalised O columns [hh * D/2, hh * D/2 + D/2) of this lane's query row
+// over the keys of K/V positions [w0, w1) that allowed(key) admits, from the
+// definition in two passes: the row max m of x_j = c * s_j (a NaN score makes
+// it NaN), then l = sum of p_j = exp2(x_j - m) and sum of p_j * v_j, divided
+// by l.  m and l come back in m_row and l_row (l = 0: no allowed key, or
+// every allowed score -inf; O = 0).  The two lanes of a row (wave halves)
+// split the dot product s_j = q . k_j by the same column halves and add the
+// halves in the same order.  q_half points at the row's columns of
 // this half (nullptr for a padding row past S).  tile_of(pos, k0, row0, valid)
 // gives position pos's first key, the row of that key in the K/V tensors (or
 // pools) counted from k_head / v_head, and whether the tile lies inside them
@@ -118,10 +120,39 @@ template <typename T, int D, int BN, bool PAD, typename TileOf, typename Allowed
 __device__ inline __attribute__((always_inline)) void exact_row(
     const T* __restrict__ q_half, const T* __restrict__ k_head, const T* __restrict__ v_head,
     int64_t row_stride, int hh, int dv, int S, int w0, int w1, TileOf tile_of, Allowed allowed,
-    float c, float m_ref, float inv_l, float (&acc)[D / 2]) {
+    float c, float& m_row, float& l_row, float (&acc)[D / 2]) {
     constexpr int DH = D / 2;
+    // x_j of the key at element offset off (every lane of the wave calls it)
+    auto scaled_score = [&](int64_t off, bool valid) __attribute__((always_inline)) {
+        float part = 0.f;
+        // a rolled loop: unrolled, the compiler would hoist every chunk's
+        // loads at once and raise the kernel's register count
+#pragma unroll 1
+        for (int c8 = 0; c8 < DH / 8; ++c8) {
+            float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            const bool col = !PAD || hh * DH + 8 * c8 < dv;
+            if (valid && col) load8<T>(k_head + off + 8 * c8, x);
+            if (q_half && col) load8<T>(q_half + 8 * c8, y);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) part = __builtin_fmaf(y[i], x[i], part);
+        }
+        return halves_sum(part) * c;
+    };
+    float m = kNegInf;
+    for (int pos = w0; pos < w1; ++pos) {
+        int k0;
+        int64_t row0;
+        bool valid;
+        tile_of(pos, k0, row0, valid);
+        for (int jj = 0; jj < BN && k0 + jj < S; ++jj) {
+            const float x = scaled_score((row0 + jj) * row_stride + (int64_t)hh * DH, valid);
+            if (q_half && allowed(k0 + jj) && m == m && (x > m || x != x)) m = x;
+        }
+    }
 #pragma unroll
     for (int d = 0; d < DH; ++d) acc[d] = 0.f;
+    float l = 0.f;
     for (int pos = w0; pos < w1; ++pos) {
         int k0;
         int64_t row0;
@@ -129,33 +160,26 @@ __device__ inline __attribute__((always_inline)) void exact_row(
         tile_of(pos, k0, row0, valid);
         for (int jj = 0; jj < BN && k0 + jj < S; ++jj) {
             const int64_t off = (row0 + jj) * row_stride + (int64_t)hh * DH;
-            float part = 0.f;
-            // a rolled loop: unrolled, the compiler would hoist every chunk's
-            // loads at once and raise the kernel's register count
-#pragma unroll 1
-            for (int c8 = 0; c8 < DH / 8; ++c8) {
-                float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-                const bool col = !PAD || hh * DH + 8 * c8 < dv;
-                if (valid && col) load8<T>(k_head + off + 8 * c8, x);
-                if (q_half && col) load8<T>(q_half + 8 * c8, y);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) part = __builtin_fmaf(y[i], x[i], part);
-            }
-            const float s = halves_sum(part);
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s, c, -m_ref)) * inv_l;
-            if (q_half && allowed(k0 + jj)) {
+            const float x = scaled_score(off, valid);
+            if (q_half && m != kNegInf && allowed(k0 + jj)) {
+                const float p = __builtin_amdgcn_exp2f(x - m);
+                l += p;
 #pragma unroll
                 for (int c8 = 0; c8 < DH / 8; ++c8) {
-                    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                    float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
                     if (valid && (!PAD || hh * DH + 8 * c8 < dv))
-                        load8<T>(v_head + off + 8 * c8, x);
+                        load8<T>(v_head + off + 8 * c8, y);
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) acc[8 * c8 + i] = __builtin_fmaf(p, x[i], acc[8 * c8 + i]);
+                    for (int i = 0; i < 8; ++i) acc[8 * c8 + i] = __builtin_fmaf(p, y[i], acc[8 * c8 + i]);
                 }
             }
         }
     }
+    const float inv = l == 0.f ? 0.f : 1.f / l;
+#pragma unroll
+    for (int d = 0; d < DH; ++d) acc[d] *= inv;
+    m_row = m;
+    l_row = l;
 }
 
 // True in every lane when some lane's accumulator holds a NaN or an infinity.
@@ -488,6 +512,14 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     float m_prev = kNegInf; // running max before the current tile
     bool moved = false;     // some row's reference moved for the current tile (wave-uniform)
     float l_run = 0.f;      // running sum over this half's keys
+    float t_sum = 0.f;      // the current tile's weights of this lane (steps that check them)
+    // bf16: once every row of the wave has a reference, the steps skip the row
+    // max of the next tile and check the weights afterwards (check_sum).  The
+    // reference is then no longer a max of the scores, only a bound that
+    // keeps the weights finite, which is all O, l and LSE need: they are
+    // exact for any reference.  fp16 keeps the max on every tile, since an
+    // fp16 weight overflows past 2^16.
+    constexpr bool kRefBySum = __is_same(T, __bf16);
     f32x16 o[DB];
 #pragma unroll
     for (int d = 0; d < DB; ++d) o[d] = f32x16{0};
@@ -536,7 +568,9 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     // exp of weight i - 4, pack and sum of weights i - 9 and i - 8) so that the
     // interleave with the MFMAs hands each MFMA slot a mix of independent
     // instructions rather than an exp and the pack that waits for it.
-    auto softmax = [&](const f32x16(&s)[KB], u32x4(&p)[NCH]) __attribute__((always_inline)) {
+    // SEP: the tile's sum is kept apart in t_sum, then added to l_run.
+    auto softmax = [&](const f32x16(&s)[KB], u32x4(&p)[NCH], auto sep_tag) __attribute__((always_inline)) {
+        constexpr bool SEP = decltype(sep_tag)::value;
         constexpr int kExpLag = 4, kPackLag = 8;
         constexpr int NE = 16 * KB;  // weights per lane
         float e[NE];
@@ -560,7 +594,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
                     else ls[q & 1] = Mfma<T>::sum2(pk, ls[q & 1]);
                 } else {  // four partial sums of single weights
                     if (q == 0) {
-                        ls[0] = l_run + e[ip - 1];
+                        ls[0] = SEP ? e[ip - 1] : l_run + e[ip - 1];
                         ls[2] = e[ip];
                     } else if (q == 1) {
                         ls[1] = e[ip - 1];
@@ -572,7 +606,14 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
                 }
             }
         }
-        l_run = Mfma<T>::kSumRounded ? ls[0] + ls[1] : (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        if (Mfma<T>::kSumRounded) {
+            l_run = ls[0] + ls[1];
+        } else if (SEP) {
+            t_sum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+            l_run += t_sum;
+        } else {
+            l_run = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+        }
     };
     // O^T += V^T P^T with V^T from transposing LDS reads of the row-major tile
     auto pv = [&](const u32x4(&p)[NCH], const unsigned char* vst) __attribute__((always_inline)) {
@@ -589,6 +630,25 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
                 const u32x4 a = {l2[0], l2[1], h2[0], h2[1]};
                 o[d] = Mfma<T>::mma(a, p[cch], o[d]);
             }
+    };
+    // After a tile whose weights were made without its row max: when some
+    // lane's share of them exceeds kSumLimit (rare), each such row's reference
+    // moves up by n = ceil(log2) of the row's tile sum, and its O and l are
+    // scaled by 2^-n, exactly.  Its tile weights are then at most 1.  A sum
+    // that is not finite leaves O or l non-finite, and the epilogue's exact
+    // recomputation takes the wave.
+    auto check_sum = [&]() __attribute__((always_inline)) {
+        if (__any(t_sum > kSumLimit)) {
+            const float rt = halves_sum(t_sum);
+            const int n = rt > kSumLimit ? (int)__builtin_ceilf(__log2f(fminf(rt, 0x1p126f))) : 0;
+            m_run += (float)n;
+            m_use = (m_run == kNegInf) ? 0.f : m_run;
+            l_run = __builtin_amdgcn_ldexpf(l_run, -n);
+#pragma unroll
+            for (int d = 0; d < DB; ++d)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) o[d][i] = __builtin_amdgcn_ldexpf(o[d][i], -n);
+        }
     };
     auto rescale_if_moved = [&]() __attribute__((always_inline)) {
         if (moved) {  // only when some row's reference moved
@@ -733,11 +793,16 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     // of tile j, then O += P_j V_j and the row max of tile j+1.  STAGE = (j -
     // kt0) & 1: K_j sat in K stage STAGE (its slot is free now), K_{j+1} is in
     // K stage STAGE^1, V_j in V stage STAGE.  MASK_NEXT: tile j+1 needs the
-    // mask.  LAST: j is the final tile.
-    auto step = [&](int j, auto stage_tag, auto mask_next_tag, auto last_tag) __attribute__((always_inline)) {
+    // mask.  LAST: j is the final tile.  MODE 0: the row max of tile j+1 sets
+    // its reference; 1: no row max, tile j's weights are checked after the
+    // step (check_sum); 2: tile j's weights are checked, then the row max of
+    // tile j+1 (the step after a run of mode 1).
+    auto step = [&](int j, auto stage_tag, auto mask_next_tag, auto last_tag, auto mode_tag)
+                    __attribute__((always_inline)) {
         constexpr int ST = decltype(stage_tag)::value;
         constexpr bool MASK_NEXT = decltype(mask_next_tag)::value;
         constexpr bool LAST = decltype(last_tag)::value;
+        constexpr int MODE = decltype(mode_tag)::value;
         unsigned char* const k_this = ST ? lds_k1 : lds_k0;  // K_j (free), later K_{j+2}
         unsigned char* const k_next = ST ? lds_k0 : lds_k1;  // K_{j+1}
         unsigned char* const v_this = ST ? lds_v1 : lds_v0;  // V_j
@@ -758,10 +823,49 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
         if (!LAST) {
             f32x16 sn[KB];
             qk(sn, k_next);
-            softmax(sc, p);
+            softmax(sc, p, BoolTag<(MODE != 0)>{});
             pv(p, v_this);
+            // interleave: every MFMA of the step (score MFMAs first, then P V)
+            // carries the same share of the VALU work -- the weights of tile
+            // j, then (mode 0) the row max of tile j+1 -- so neither phase is
+            // VALU-bound while the other leaves the vector ALU idle.
+            // Operand reads from LDS run ahead of their MFMA: kLeadK score
+            // MFMAs, kLeadV P V MFMAs (LDS latency under load is several
+            // MFMAs).  Mode 2 branches between its P V MFMAs and the row max,
+            // so its interleave covers the weights only.
+            auto interleave = [&]() __attribute__((always_inline)) {
+                constexpr int NQK = KB * KSTEPS, NPV = NCH * DB;
+                // fma + exp per weight, one cvt per pair, the row sum, the max
+                constexpr int NVALU =
+                    KB * (32 + 8 + (MODE == 0 ? 8 : 0) + (Mfma<T>::kSumRounded ? 8 : 16)) +
+                    (MODE == 0 ? 16 : 4);
+                constexpr int VALU_PER = (NVALU + NQK + NPV - 1) / (NQK + NPV);
+                __builtin_amdgcn_sched_group_barrier(kSgDsRead, kLeadK, 0);
+#pragma unroll
+                for (int i = 0; i < NQK; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSgValu, VALU_PER, 0);
+                    if (i + kLeadK < NQK) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+                    // the first V reads start under the last score MFMAs
+                    if (i + kLeadV >= NQK) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < NPV; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(kSgValu, VALU_PER, 0);
+                    if (i + kLeadV < NPV) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+                }
+            };
+            if (MODE == 2) {
+                asm volatile("" : "+v"(l_run));
+                interleave();
+                check_sum();
+            }
             if (MASK_NEXT) apply_mask(sn, tn1 * BN);
-            update_max(sn);
+            if (MODE == 1)
+                moved = false;
+            else
+                update_max(sn);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) sc[kb] = sn[kb];
             // The row sum of this tile's weights is finished inside this step,
@@ -769,50 +873,28 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
             // every other step into the next one, ahead of its first MFMA,
             // where no MFMA hides them (and ten P V MFMAs go without VALU work).
             asm volatile("" : "+v"(l_run));
-            // interleave: every MFMA of the step (score MFMAs first, then P V)
-            // carries the same share of the VALU work -- the weights of tile
-            // j, then the row max of tile j+1 -- so neither phase is
-            // VALU-bound while the other leaves the vector ALU idle.
-            // Operand reads from LDS run ahead of their MFMA: kLeadK score
-            // MFMAs, kLeadV P V MFMAs (LDS latency under load is several
-            // MFMAs).
-            constexpr int NQK = KB * KSTEPS, NPV = NCH * DB;
-            // fma + exp per weight, one cvt per pair, the row sum, the max
-            constexpr int NVALU = KB * (32 + 8 + 8 + (Mfma<T>::kSumRounded ? 8 : 16)) + 16;
-            constexpr int VALU_PER = (NVALU + NQK + NPV - 1) / (NQK + NPV);
-            __builtin_amdgcn_sched_group_barrier(kSgDsRead, kLeadK, 0);
-#pragma unroll
-            for (int i = 0; i < NQK; ++i) {
-                __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(kSgValu, VALU_PER, 0);
-                if (i + kLeadK < NQK) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-                // the first V reads start under the last score MFMAs
-                if (i + kLeadV >= NQK) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < NPV; ++i) {
-                __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(kSgValu, VALU_PER, 0);
-                if (i + kLeadV < NPV) __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-            }
+            if (MODE != 2) interleave();
+            if (MODE == 1) check_sum();
         } else {
-            softmax(sc, p);
+            softmax(sc, p, BoolTag<kRefBySum>{});
             pv(p, v_this);
+            if (kRefBySum) check_sum();
         }
     };
     // iterations [j0, j1), none of them the last; the stage alternates
-    auto run = [&](int j0, int j1, auto mask_next_tag) __attribute__((always_inline)) {
+    auto run = [&](int j0, int j1, auto mask_next_tag, auto mode_tag) __attribute__((always_inline)) {
         int j = j0;
         if (j < j1 && ((j - kt0) & 1)) {
-            step(j, IntTag<1>{}, mask_next_tag, BoolTag<false>{});
+            step(j, IntTag<1>{}, mask_next_tag, BoolTag<false>{}, mode_tag);
             ++j;
         }
         for (; j + 1 < j1; j += 2) {
-            step(j, IntTag<0>{}, mask_next_tag, BoolTag<false>{});
-            step(j + 1, IntTag<1>{}, mask_next_tag, BoolTag<false>{});
+            step(j, IntTag<0>{}, mask_next_tag, BoolTag<false>{}, mode_tag);
+            step(j + 1, IntTag<1>{}, mask_next_tag, BoolTag<false>{}, mode_tag);
         }
-        if (j < j1) step(j, IntTag<0>{}, mask_next_tag, BoolTag<false>{});
+        if (j < j1) step(j, IntTag<0>{}, mask_next_tag, BoolTag<false>{}, mode_tag);
     };
+
     // a step of the workgroup's loads and barrier only (outside [kw0, kw1))
     auto idle_step = [&](int j) __attribute__((always_inline)) {
         const bool st = ((j - kt0) & 1) != 0;
@@ -840,13 +922,25 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     if (ja > jl) ja = jl;
     int jb = ki1 - 1 < jl ? ki1 - 1 : jl;
     if (jb < ja) jb = ja;
-    run(kw0, ja, BoolTag<true>{});
-    run(ja, jb, BoolTag<false>{});
-    run(jb, jl, BoolTag<true>{});
+    if constexpr (kRefBySum) {
+        // The row max of the first mask-free tile gives every row of the wave
+        // a reference (all its keys are allowed for every row): the head
+        // steps take it too (its mask changes nothing).  The mask-free steps
+        // after it skip the row max; the steps after them check their tile
+        // before the row max of the next (mode 2), and so does the last.
+        const int jh = ja < jb ? ja + 1 : ja;
+        run(kw0, jh, BoolTag<true>{}, IntTag<0>{});
+        run(jh, jb, BoolTag<false>{}, IntTag<1>{});
+        run(jb, jl, BoolTag<true>{}, IntTag<2>{});
+    } else {
+        run(kw0, ja, BoolTag<true>{}, IntTag<0>{});
+        run(ja, jb, BoolTag<false>{}, IntTag<0>{});
+        run(jb, jl, BoolTag<true>{}, IntTag<0>{});
+    }
     if ((jl - kt0) & 1)
-        step(jl, IntTag<1>{}, BoolTag<false>{}, BoolTag<true>{});
+        step(jl, IntTag<1>{}, BoolTag<false>{}, BoolTag<true>{}, IntTag<0>{});
     else
-        step(jl, IntTag<0>{}, BoolTag<false>{}, BoolTag<true>{});
+        step(jl, IntTag<0>{}, BoolTag<false>{}, BoolTag<true>{}, IntTag<0>{});
     if (!SPARSE)
         for (int j = kw1; j < kt1; ++j) idle_step(j);
     }  // the wave computes
@@ -858,9 +952,10 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     const float inv = (l_tot == 0.f) ? 0.f : 1.f / l_tot;
     const float m_fin = (m_run == kNegInf) ? 0.f : m_run;
     const float lse_v = (l_tot == 0.f) ? kNegInf : 0.69314718055994531f * (m_fin + __log2f(l_tot));
-    // a NaN or an infinity in O: this wave recomputes its rows over their
-    // allowed keys only (exact_row), stores them and its LSE, and is done
-    if (any_nonfinite<DB>(o)) {
+    // a NaN or an infinity in O, or a row sum that is not finite: this wave
+    // recomputes its rows over their allowed keys only (exact_row), stores
+    // them and their LSE, and is done
+    if (any_nonfinite<DB>(o) || __any(!(l_tot < __builtin_inff()))) {
         constexpr int DH = D / 2;
         float acc[DH];
         auto tile_of = [&](int pos, int& k0, int64_t& row0, bool& valid) __attribute__((always_inline)) {
@@ -878,18 +973,20 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
             return (unsigned)(key - key_lo) <= (unsigned)key_w;
         };
         const T* q_half = qrow < S ? q + head_base + (int64_t)qrow * row_stride + hh * DH : nullptr;
+        float m_x, l_x;
         exact_row<T, D, BN, PAD>(q_half, (const T*)k_head, (const T*)v_head, row_stride, hh, dv, Sk, ex_w0,
-                            ex_w1, tile_of, allowed, c, m_fin, inv, acc);
+                            ex_w1, tile_of, allowed, c, m_x, l_x, acc);
+        const float lse_x = (l_x == 0.f) ? kNegInf : 0.69314718055994531f * (m_x + __log2f(l_x));
         if (qrow < S) {
             if (SPLIT) {
-                if (hh == 0) part_lse[part_row] = lse_v;
+                if (hh == 0) part_lse[part_row] = lse_x;
 #pragma unroll
                 for (int c4 = 0; c4 < DH / 4; ++c4)
                     if (!PAD || hh * DH + 4 * c4 < dv)
                         *reinterpret_cast<f32x4*>(part_o + part_row * dv + hh * DH + 4 * c4) =
                             f32x4{acc[4 * c4], acc[4 * c4 + 1], acc[4 * c4 + 2], acc[4 * c4 + 3]};
             } else {
-                if (hh == 0) lse[((int64_t)bb * H + h) * S + qrow] = lse_v;
+                if (hh == 0) lse[((int64_t)bb * H + h) * S + qrow] = lse_x;
                 T* const orow = out + head_base + (int64_t)qrow * row_stride + hh * DH;
 #pragma unroll
                 for (int c8 = 0; c8 < DH / 8; ++c8)
@@ -1296,8 +1393,10 @@ __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
             return ok && (!SPARSE || mrow[key / block_n] != 0);
         };
         const float* q_half = qrow < S ? q + head_base + (int64_t)qrow * row_stride + hh * DH : nullptr;
+        float m_x, l_x;
         exact_row<float, D, BN, PAD>(q_half, k + kv_base, v + kv_base, row_stride, hh, dv, S, (int)kt0,
-                                (int)kt1, tile_of, allowed, c, m_fin, inv, acc);
+                                (int)kt1, tile_of, allowed, c, m_x, l_x, acc);
+        const float lse_x = (l_x == 0.f) ? kNegInf : 0.69314718055994531f * (m_x + __log2f(l_x));
         if (qrow < S) {
             float* eo = out + head_base + (int64_t)qrow * row_stride + hh * DH;
 #pragma unroll
@@ -1305,7 +1404,7 @@ __global__ __launch_bounds__(kThreads32, 2) void fa_fwd_fp32_kernel(
                 if (!PAD || hh * DH + 4 * c4 < dv)
                     *reinterpret_cast<f32x4*>(eo + 4 * c4) =
                         f32x4{acc[4 * c4], acc[4 * c4 + 1], acc[4 * c4 + 2], acc[4 * c4 + 3]};
-            if (hh == 0) lse[((int64_t)bb * H + h) * S + qrow] = lse_v;
+            if (hh == 0) lse[((int64_t)bb * H + h) * S + qrow] = lse_x;
         }
         return;
     }

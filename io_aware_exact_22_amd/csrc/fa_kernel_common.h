@@ -40,6 +40,9 @@ constexpr int kDmaBias = 4096;
 constexpr int kDmaPastRecords = (int)0xFFFF0000u;
 // log2-domain slack before the running reference max is moved (weights <= 2^8)
 constexpr float kRescaleSlack = 8.f;
+// A step that skips the row max checks the weights it made instead: when one
+// lane's share of a tile's weights exceeds this, the reference moves up
+constexpr float kSumLimit = 256.f;
 
 #ifndef FA_LEAD_K
 #define FA_LEAD_K 3
