@@ -168,6 +168,32 @@ int fa_fwd_workgroup_tile(int64_t B, int64_t H, int64_t S, int64_t D, int dtype,
                           int64_t* q_tile);
 
 /*
+ * fa_fwd_launch_order -- host-side view of the order fa_fwd runs its tiles in
+ * on a device with n_cus compute units.  Pure function, no HIP call.  A
+ * causal bf16 / fp16 launch with more workgroups than the device holds at
+ * once (3 per compute unit at D <= 64, 2 at D <= 128, 1 above) runs its
+ * lightest Q tiles, about 10% of its K/V tile steps, in a dynamic order, so
+ * that faster XCDs take more of them (thread-block load balance, the note
+ * closing [FA] section 1).  All heads' Q tiles then form one list, heaviest
+ * first (rank r = Q tile n_q_tiles - 1 - r, heads next to each other, the
+ * heads of a rank rotated by one: position p is (b * H + h, Q tile) =
+ * ((p + 1) mod (B * H), n_q_tiles - 1 - p / (B * H))).  Workgroups below
+ * *first_dynamic take the heavy positions [0, *first_dynamic) in the static
+ * order's fashion (snake order, or blocks of whole heads per XCD, as
+ * fa_fwd_workgroup_tile describes); each later workgroup takes the next
+ * position when it starts, and wg >= *first_dynamic reports position wg,
+ * the tile of the (wg - *first_dynamic)-th of them to start.  During the
+ * call the word of LSE row 0 of (b, h) = (0, 0) counts the positions taken
+ * (that row is the last position, whose workgroup writes it afterwards).
+ * Otherwise *first_dynamic = -1 and the order is fa_fwd_workgroup_tile's.
+ * Returns FA_OK, or FA_ERR_* for bad arguments (n_cus < 1 or wg outside the
+ * grid: FA_ERR_SHAPE).
+ */
+int fa_fwd_launch_order(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int causal,
+                        int64_t window_left, int64_t window_right, int64_t n_cus, int64_t wg,
+                        int64_t* bh, int64_t* q_tile, int64_t* first_dynamic);
+
+/*
  * fa_fwd_splitkv -- fa_fwd with the K/V tiles of every Q tile cut into
  * n_splits contiguous parts that separate workgroups process at the same
  * time.  Each workgroup writes the partial (O, LSE) of its part, in fp32, to

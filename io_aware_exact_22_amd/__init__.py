@@ -13,7 +13,8 @@ from .fa import (FA_DTYPE_BF16, FA_DTYPE_FP16, FA_DTYPE_FP32, FA_ERR_SCRATCH, FA
                  fa_bwd_workspace_size, fa_fwd, fa_fwd_blocksparse,
                  fa_fwd_blocksparse_workspace_size, fa_fwd_check_args, fa_fwd_paged, fa_fwd_splitkv,
                  fa_fwd_splitkv_auto_splits, fa_fwd_splitkv_noalloc, fa_fwd_splitkv_workgroup_tile,
-                 fa_fwd_splitkv_workspace_size, fa_fwd_tile_schedule, fa_fwd_workgroup_tile, fa_status_string, flash_attn_bwd, flash_attn_fwd,
+                 fa_fwd_splitkv_workspace_size, fa_fwd_tile_schedule, fa_fwd_workgroup_tile,
+                 fa_fwd_launch_order, fa_status_string, flash_attn_bwd, flash_attn_fwd,
                  flash_attn_fwd_blocksparse, flash_attn_fwd_paged, flash_attn_fwd_splitkv,
                  library_path)
 
@@ -24,7 +25,8 @@ __all__ = [
     "fa_bwd_workspace_size", "fa_fwd", "fa_fwd_blocksparse", "fa_fwd_blocksparse_workspace_size",
     "fa_fwd_check_args", "fa_fwd_paged", "fa_fwd_splitkv", "fa_fwd_splitkv_auto_splits",
     "fa_fwd_splitkv_noalloc",
-    "fa_fwd_splitkv_workgroup_tile", "fa_fwd_splitkv_workspace_size", "fa_fwd_tile_schedule", "fa_fwd_workgroup_tile",
+    "fa_fwd_splitkv_workgroup_tile", "fa_fwd_splitkv_workspace_size", "fa_fwd_tile_schedule",
+    "fa_fwd_workgroup_tile", "fa_fwd_launch_order",
     "fa_status_string", "flash_attn_bwd", "flash_attn_fwd", "flash_attn_fwd_blocksparse",
     "flash_attn_fwd_paged", "flash_attn_fwd_splitkv", "library_path",
 ]

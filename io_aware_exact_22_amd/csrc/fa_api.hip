@@ -251,7 +251,42 @@ FA_API int fa_fwd_workgroup_tile(int64_t B, int64_t H, int64_t S, int64_t D, int
     uint32_t r_bh, r_qt;
     const int64_t esz = dtype == FA_DTYPE_FP32 ? 4 : 2;
     fa::workgroup_tile((uint32_t)wg, (uint32_t)(B * H), (uint32_t)nq, causal != 0,
-                       fa::snake_launch(B * H, S, D, esz), &r_bh, &r_qt);
+                       fa::snake_launch(B * H, S, fa::kernel_head_dim(D), esz), &r_bh, &r_qt);
+    *bh = r_bh;
+    *q_tile = r_qt;
+    return FA_OK;
+}
+
+FA_API int fa_fwd_launch_order(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int causal,
+                               int64_t window_left, int64_t window_right, int64_t n_cus,
+                               int64_t wg, int64_t* bh, int64_t* q_tile,
+                               int64_t* first_dynamic) {
+    if (!bh || !q_tile || !first_dynamic) return FA_ERR_NULL;
+    if (n_cus < 1) return FA_ERR_SHAPE;
+    int64_t nbytes, lbytes;
+    const int rc = check_problem(B, H, S, D, causal, window_left, window_right, dtype, &nbytes,
+                                 &lbytes);
+    if (rc != FA_OK) return rc;
+    const int64_t wlc = window_left >= S ? -1 : window_left;
+    const int64_t wrc = window_right >= S ? -1 : window_right;
+    const int64_t BM = fa::q_tile_rows(dtype, D, S, wlc, wrc);
+    const int64_t nq = (S + BM - 1) / BM, n_bh = B * H;
+    if (wg < 0 || wg >= n_bh * nq) return FA_ERR_SHAPE;
+    int64_t first = -1;
+    if (dtype != FA_DTYPE_FP32)  // the fp32 kernel keeps the static order
+        first = fa::dyn_first_position(fa::MaskSpec{S, causal, wlc, wrc}, n_bh, BM,
+                                       fa::kv_tile_keys(dtype, D, S, wlc, wrc),
+                                       fa::resident_wgs_per_cu(D) * n_cus);
+    *first_dynamic = first;
+    if (first < 0)
+        return fa_fwd_workgroup_tile(B, H, S, D, dtype, causal, window_left, window_right, wg, bh,
+                                     q_tile);
+    const uint32_t pos =
+        wg < first ? fa::dyn_static_position((uint32_t)wg, (uint32_t)n_bh, (uint32_t)first,
+                                             fa::snake_launch(n_bh, S, fa::kernel_head_dim(D), 2))
+                   : (uint32_t)wg;
+    uint32_t r_bh, r_qt;
+    fa::dyn_list_tile(pos, (uint32_t)n_bh, (uint32_t)nq, &r_bh, &r_qt);
     *bh = r_bh;
     *q_tile = r_qt;
     return FA_OK;

@@ -195,6 +195,11 @@ template <int DB> __device__ inline bool any_nonfinite(const f32x16 (&o)[DB]) {
     return __any((z0 + z1) != (z0 + z1));
 }
 
+// Zeroes the word the dynamic order counts in (lane 0 of one workgroup).
+template <int kUnused = 0> __global__ void fa_zero_word_kernel(unsigned* p) {
+    if (threadIdx.x == 0) *p = 0u;
+}
+
 // SPLIT: the K/V tiles of each Q tile are cut into n_splits contiguous parts,
 // one workgroup per (Q tile, part); each writes the partial (O, LSE) of its
 // part, in fp32, to part_o [n_splits, B, H, S, D] and part_lse
@@ -220,7 +225,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     int n_splits, float* __restrict__ part_o, float* __restrict__ part_lse,
     const int* __restrict__ sp_lut, int sp_heads, int sp_stride, const int* __restrict__ pg_table,
     int pg_stride, int pg_rows, int pg_count, const int* __restrict__ kv_lens, int kv_cap,
-    int dv_in) {
+    int dv_in, int dyn_first) {
     static_assert(!(SPLIT && SPARSE), "a block-sparse launch runs in one part");
     static_assert(!(SPARSE && PAGED), "block-sparse and paged K/V do not combine");
     static_assert(!(SPARSE && KVC), "a block mask does not apply to a KV cache");
@@ -255,12 +260,32 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     uint32_t bh, qt32, sp32 = 0;
     // (KVC: the tiles' weights depend on cache lengths in device memory; the
     // tiles run in list order)
-    if (SPLIT)  // K/V part sp of the tile
+    if (SPLIT) {  // K/V part sp of the tile
         workgroup_tile_part(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt,
                             (uint32_t)n_splits, !KVC && causal != 0, &bh, &qt32, &sp32);
-    else
+    } else if (!SPARSE && !PAGED && !KVC && dyn_first >= 0) {
+        // The dynamic tail of a causal launch (dyn_first_position): workgroups
+        // from dyn_first on take the next list position from a counter in the
+        // word of lse row 0 of (b, h) = (0, 0), which the host zeroes before
+        // the launch.  That row belongs to the last position, so its
+        // workgroup writes the word only after every position has been taken.
+        __shared__ uint32_t s_pos;
+        const uint32_t n_bh = (uint32_t)B * (uint32_t)H;
+        uint32_t pos;
+        if ((int)blockIdx.x < dyn_first) {
+            pos = dyn_static_position(blockIdx.x, n_bh, (uint32_t)dyn_first,
+                                      snake_launch((int64_t)B * H, S, D, sizeof(T)));
+        } else {
+            if (threadIdx.x == 0)
+                s_pos = (uint32_t)dyn_first + atomicAdd(reinterpret_cast<unsigned*>(lse), 1u);
+            __syncthreads();
+            pos = s_pos;
+        }
+        dyn_list_tile(pos, n_bh, (uint32_t)n_qt, &bh, &qt32);
+    } else {
         workgroup_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt, !KVC && causal != 0,
                        snake_launch((int64_t)B * H, S, D, sizeof(T)), &bh, &qt32);
+    }
     const int sp = (int)sp32;
     const int qt = (int)qt32;
     const int bb = (int)(bh / (uint32_t)H), h = (int)(bh % (uint32_t)H);

@@ -14,6 +14,22 @@
 
 namespace fa {
 
+// The first dynamic list position of a dense launch (dyn_first_position),
+// for a device holding three workgroups per compute unit at D = 64, two at
+// 128 and one above; -1 (the static order) when the device cannot be queried.
+template <int D, int BM, int BN>
+int dynamic_first(const LaunchArgs& a) {
+    if (!a.causal) return -1;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return -1;
+    }
+    const MaskSpec m{a.S, a.causal, a.wl, a.wr};
+    return (int)dyn_first_position(m, a.B * a.H, BM, BN, resident_wgs_per_cu(D) * (int64_t)cus);
+}
+
 template <typename T, int D, int NW, int BN, bool PAD>
 hipError_t launch_mfma_cfg(const LaunchArgs& a) {
     constexpr int BM = Tile<D, NW, BN>::BM;
@@ -33,7 +49,7 @@ hipError_t launch_mfma_cfg(const LaunchArgs& a) {
                            dim3((unsigned)n_wg), dim3(NW * 64), 0, a.stream, (const T*)a.q,
                            (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
                            (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr, nullptr,
-                           (const int*)a.lut, (int)a.n_mask, stride, nullptr, 0, 1, 0, nullptr, 0, (int)a.D);
+                           (const int*)a.lut, (int)a.n_mask, stride, nullptr, 0, 1, 0, nullptr, 0, (int)a.D, -1);
         return hipGetLastError();
     }
     const bool paged = a.pg_table != nullptr;
@@ -46,13 +62,21 @@ hipError_t launch_mfma_cfg(const LaunchArgs& a) {
                                (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
                                (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr,
                                nullptr, nullptr, 0, 0, a.pg_table, pg_stride, pg_rows, pg_count,
-                               nullptr, 0, (int)a.D);
-        else
+                               nullptr, 0, (int)a.D, -1);
+        else {
+            const int dyn = dynamic_first<D, BM, BN>(a);
+            if (dyn >= 0) {  // the dynamic order's counter starts at 0
+                hipLaunchKernelGGL((fa_zero_word_kernel<>), dim3(1), dim3(64), 0, a.stream,
+                                   reinterpret_cast<unsigned*>(a.lse));
+                hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+            }
             hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, false, false, false, PAD>),
                                dim3((unsigned)n_wg), dim3(NW * 64), 0, a.stream, (const T*)a.q,
                                (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
                                (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr,
-                               nullptr, nullptr, 0, 0, nullptr, 0, 1, 0, nullptr, 0, (int)a.D);
+                               nullptr, nullptr, 0, 0, nullptr, 0, 1, 0, nullptr, 0, (int)a.D, dyn);
+        }
         return hipGetLastError();
     }
     if (paged)
@@ -61,14 +85,14 @@ hipError_t launch_mfma_cfg(const LaunchArgs& a) {
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B,
                            (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt,
                            a.n_splits, a.part_o, a.part_lse, nullptr, 0, 0, a.pg_table, pg_stride,
-                           pg_rows, pg_count, nullptr, 0, (int)a.D);
+                           pg_rows, pg_count, nullptr, 0, (int)a.D, -1);
     else
         hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, true, false, false, false, PAD>),
                            dim3((unsigned)(n_wg * a.n_splits)), dim3(NW * 64), 0, a.stream,
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B,
                            (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt,
                            a.n_splits, a.part_o, a.part_lse, nullptr, 0, 0, nullptr, 0, 1, 0,
-                           nullptr, 0, (int)a.D);
+                           nullptr, 0, (int)a.D, -1);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_merge_parts(a);
@@ -93,13 +117,13 @@ hipError_t launch_kvc_mfma_cfg(const LaunchArgs& a) {
                                (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
                                (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr,
                                nullptr, nullptr, 0, 0, a.pg_table, pg_stride, pg_rows, pg_count,
-                               a.kv_lens, cap, (int)a.D);
+                               a.kv_lens, cap, (int)a.D, -1);
         else
             hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, false, false, true, PAD>),
                                dim3((unsigned)n_wg), dim3(NW * 64), 0, a.stream, (const T*)a.q,
                                (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
                                (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr,
-                               nullptr, nullptr, 0, 0, nullptr, 0, 1, 0, a.kv_lens, cap, (int)a.D);
+                               nullptr, nullptr, 0, 0, nullptr, 0, 1, 0, a.kv_lens, cap, (int)a.D, -1);
         return hipGetLastError();
     }
     if (paged)
@@ -108,14 +132,14 @@ hipError_t launch_kvc_mfma_cfg(const LaunchArgs& a) {
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B,
                            (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt,
                            a.n_splits, a.part_o, a.part_lse, nullptr, 0, 0, a.pg_table, pg_stride,
-                           pg_rows, pg_count, a.kv_lens, cap, (int)a.D);
+                           pg_rows, pg_count, a.kv_lens, cap, (int)a.D, -1);
     else
         hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, true, false, false, true, PAD>),
                            dim3((unsigned)(n_wg * a.n_splits)), dim3(NW * 64), 0, a.stream,
                            (const T*)a.q, (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B,
                            (int)a.H, (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt,
                            a.n_splits, a.part_o, a.part_lse, nullptr, 0, 0, nullptr, 0, 1, 0,
-                           a.kv_lens, cap, (int)a.D);
+                           a.kv_lens, cap, (int)a.D, -1);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_merge_parts(a);

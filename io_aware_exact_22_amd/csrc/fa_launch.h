@@ -16,6 +16,12 @@ constexpr int kDtypeBf16 = 2;
 constexpr int kMfmaWaves = 4, kMfmaKeys = 64, kWideKeys = 32;
 // the most K/V parts per Q tile a KV-cache launch takes (FA_MAX_KV_SPLITS)
 constexpr int kMaxKvSplits = 64;
+// workgroups of the bf16 / fp16 forward kernel one compute unit holds at once
+// (register and LDS limits): three at D = 64, two up to 128, one above
+constexpr int resident_wgs_per_cu(int64_t D) { return D <= 64 ? 3 : D <= 128 ? 2 : 1; }
+// the head dimension a kernel runs at for tensors of head dimension D (other
+// multiples of 16 run padded with zero columns)
+constexpr int64_t kernel_head_dim(int64_t D) { return D <= 64 ? 64 : D <= 128 ? 128 : 256; }
 
 struct LaunchArgs {
     const void* q;

@@ -256,4 +256,64 @@ __host__ __device__ inline void workgroup_tile_part(uint32_t w, uint32_t n_bh, u
     *qt = n_qt - 1 - t / n_bh;
 }
 
+// ---- Dynamic tail of a causal launch.  A causal launch with more
+// workgroups than the device holds at once takes its lightest tiles, about
+// kDynSharePct of its K/V steps, in a dynamic order: the Q tiles of all heads
+// form one list by rank (rank r: Q tile n_qt - 1 - r, heaviest first), heads
+// next to each other.  The ranks below r0 keep the static order by workgroup
+// id (snake order, or blocks of whole heads as workgroup_tile deals them);
+// each workgroup from id first = r0 * n_bh on takes the next free position
+// of the list from a device counter when it starts.  The light tiles then go
+// wherever a slot frees up, so a faster XCD takes more of them: XCDs differ
+// in speed by a few percent, and with a fixed share each the fast ones idle
+// at the end of the launch (measured: 92% of the slot time busy at the 16K
+// causal workload, with XCDs ending up to 8% apart).
+constexpr int kDynSharePct = 10;
+
+// List position pos -> (b * H + h, Q tile).  The heads rotate by one, so that
+// the last position, n_bh * n_qt - 1, is (0, Q tile 0): the tile holding row
+// 0 of (b, h) = (0, 0), whose LSE word serves as the counter.
+__host__ __device__ inline void dyn_list_tile(uint32_t pos, uint32_t n_bh, uint32_t n_qt,
+                                              uint32_t* bh, uint32_t* qt) {
+    *bh = (pos + 1) % n_bh;
+    *qt = n_qt - 1 - pos / n_bh;
+}
+
+// Workgroup w < first -> its list position (a bijection onto [0, first)).
+__host__ __device__ inline uint32_t dyn_static_position(uint32_t w, uint32_t n_bh, uint32_t first,
+                                                        bool snake) {
+    if (snake) return snake_item(w, first);
+    const uint32_t r0 = first / n_bh;
+    uint32_t bh, q;
+    workgroup_tile(w, n_bh, r0, true, false, &bh, &q);  // Q tile q of ranks [0, r0): rank r0-1-q
+    return (r0 - 1 - q) * n_bh + (bh + n_bh - 1) % n_bh;
+}
+
+// The first dynamic position of a launch of Q tiles bm x K/V tiles bn over
+// n_bh (batch, head) pairs on a device that holds `slots` workgroups at once,
+// or -1 for the static order (not causal, or no more workgroups than slots):
+// r0 * n_bh, r0 the first rank whose tail (ranks r0 .. n_qt - 1 of all heads)
+// holds at most kDynSharePct of the K/V steps.
+inline int64_t dyn_first_position(const MaskSpec& m, int64_t n_bh, int64_t bm, int64_t bn,
+                                  int64_t slots) {
+    if (!m.causal) return -1;
+    const int64_t n_qt = (m.S + bm - 1) / bm;
+    if (n_bh * n_qt <= slots) return -1;
+    int64_t total = 0;
+    for (int64_t qt = 0; qt < n_qt; ++qt) {
+        int64_t t0, t1;
+        q_tile_kv_range(m, qt, bm, bn, &t0, &t1);
+        total += t1 - t0;
+    }
+    int64_t tail = 0, r0 = n_qt;
+    for (int64_t r = n_qt - 1; r >= 0; --r) {
+        int64_t t0, t1;
+        q_tile_kv_range(m, n_qt - 1 - r, bm, bn, &t0, &t1);
+        if (100 * (tail + t1 - t0) > kDynSharePct * total) break;
+        tail += t1 - t0;
+        r0 = r;
+    }
+    return r0 < n_qt ? r0 * n_bh : -1;
+}
+
 }  // namespace fa

@@ -1,7 +1,7 @@
 """ctypes binding of libfa_mi355x (declared in include/fa_mi355x.h).
 
 Same names as the C ABI: ``fa_fwd``, ``fa_fwd_check_args``,
-``fa_status_string``, ``fa_fwd_tile_schedule``, ``fa_fwd_workgroup_tile``,
+``fa_status_string``, ``fa_fwd_tile_schedule``, ``fa_fwd_workgroup_tile``, ``fa_fwd_launch_order``,
 ``fa_fwd_splitkv_workgroup_tile``, ``fa_fwd_splitkv``,
 ``fa_fwd_splitkv_workspace_size``, ``fa_fwd_splitkv_auto_splits``, ``fa_bwd``,
 ``fa_bwd_workspace_size``, ``fa_fwd_blocksparse``, ``fa_fwd_blocksparse_workspace_size``,
@@ -75,6 +75,9 @@ def _load():
         lib.fa_fwd_workgroup_tile.argtypes = [i64, i64, i64, i64, cint, cint, i64, i64, i64, p64,
                                               p64]
         lib.fa_fwd_workgroup_tile.restype = cint
+        lib.fa_fwd_launch_order.argtypes = [i64, i64, i64, i64, cint, cint, i64, i64, i64, i64,
+                                            p64, p64, p64]
+        lib.fa_fwd_launch_order.restype = cint
         lib.fa_fwd_splitkv_workgroup_tile.argtypes = [i64, i64, i64, i64, cint, cint, i64, i64,
                                                       i64, i64, p64, p64, p64]
         lib.fa_fwd_splitkv_workgroup_tile.restype = cint
@@ -161,6 +164,19 @@ def fa_fwd_workgroup_tile(B: int, H: int, S: int, D: int, dtype: int, causal: in
     if rc != 0:
         raise FaError(rc, "fa_fwd_workgroup_tile")
     return bh.value, qt.value
+
+
+def fa_fwd_launch_order(B: int, H: int, S: int, D: int, dtype: int, causal: int,
+                        window_left: int, window_right: int, n_cus: int,
+                        wg: int) -> tuple[int, int, int]:
+    """Host view of the launch order on a device of ``n_cus`` compute units:
+    (b * H + h, Q tile, first dynamic workgroup or -1) of workgroup ``wg``."""
+    bh, qt, first = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    rc = _load().fa_fwd_launch_order(B, H, S, D, dtype, causal, window_left, window_right, n_cus,
+                                     wg, ctypes.byref(bh), ctypes.byref(qt), ctypes.byref(first))
+    if rc != 0:
+        raise FaError(rc, "fa_fwd_launch_order")
+    return bh.value, qt.value, first.value
 
 
 def fa_fwd_splitkv_workgroup_tile(B: int, H: int, S: int, D: int, dtype: int, causal: int,

@@ -25,7 +25,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_check_args", "fa_status_string", "fa_fwd_tile_schedule",
-                          "fa_fwd_workgroup_tile", "fa_fwd_splitkv_workgroup_tile",
+                          "fa_fwd_workgroup_tile", "fa_fwd_launch_order",
+                          "fa_fwd_splitkv_workgroup_tile",
                           "fa_fwd_splitkv",
                           "fa_fwd_splitkv_workspace_size", "fa_fwd_splitkv_auto_splits",
                           "fa_bwd", "fa_bwd_workspace_size", "fa_fwd_blocksparse",
@@ -337,6 +338,68 @@ def test_workgroup_order(B, H, S, causal):
             assert [bh * nq + qt for bh, qt in seq] == pos
     with pytest.raises(fa.FaError):
         fa.fa_fwd_workgroup_tile(B, H, S, 128, dt, causal, -1, -1, n)
+
+
+@pytest.mark.parametrize("B,H,S,D,window", [(1, 16, 16384, 128, (-1, -1)),
+                                             (1, 16, 32768, 128, (-1, -1)),
+                                             (2, 16, 2048, 64, (-1, -1)),
+                                             (1, 32, 4096, 64, (-1, -1)),
+                                             (1, 20, 4096, 128, (1024, -1)),
+                                             (1, 10, 4096, 256, (-1, -1)),
+                                             (1, 3, 30000, 96, (-1, -1)),
+                                             (4, 16, 4096, 64, (-1, -1))])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_launch_order_dynamic_tail(B, H, S, D, window, causal):
+    """The order on a 256-CU device: a bijection onto the (batch-head, Q tile)
+    pairs.  A causal launch with more workgroups than the device holds (3, 2 or
+    1 per CU for D <= 64, <= 128, above) has a dynamic tail: it starts at a
+    multiple of B * H, its positions are the lightest ranks of all heads
+    (heaviest first, heads rotated by one, ending on row 0 of head 0), and it
+    holds at most 10% of the K/V steps while the rank before it would push it
+    over.  The static part keeps the static order's shape: snake order
+    (each XCD heaviest first, summed steps balanced) or blocks of whole heads
+    per XCD.  Other launches keep fa_fwd_workgroup_tile's order."""
+    dt = fa.FA_DTYPE_BF16
+    wl, wr = window
+    nq = fa.fa_fwd_tile_schedule(S, D, dt, causal, wl, wr, 0)["n_q_tiles"]
+    n_bh = B * H
+    n = n_bh * nq
+    steps = []
+    for t_ in range(nq):
+        x = fa.fa_fwd_tile_schedule(S, D, dt, causal, wl, wr, t_)
+        steps.append(x["kt_end"] - x["kt_begin"])
+    res = [fa.fa_fwd_launch_order(B, H, S, D, dt, causal, wl, wr, 256, w) for w in range(n)]
+    tiles = [(bh, qt) for bh, qt, _ in res]
+    first = res[0][2]
+    assert all(f == first for _, _, f in res)
+    assert sorted(tiles) == [(bh, qt) for bh in range(n_bh) for qt in range(nq)]
+    slots = 256 * (3 if D <= 64 else 2 if D <= 128 else 1)
+    if not causal or n <= slots:
+        assert first == -1
+        assert tiles == [fa.fa_fwd_workgroup_tile(B, H, S, D, dt, causal, wl, wr, w)
+                         for w in range(n)]
+        return
+    assert first >= 0 and first % n_bh == 0
+    r0 = first // n_bh
+    # dynamic positions: rank-major, heads rotated by one, last = (0, Q tile 0)
+    assert tiles[first:] == [((p + 1) % n_bh, nq - 1 - p // n_bh) for p in range(first, n)]
+    assert tiles[-1] == (0, 0)
+    total = n_bh * sum(steps)
+    tail = n_bh * sum(steps[qt] for qt in range(nq - r0))  # ranks r0 .. nq-1
+    assert 100 * tail <= 10 * total
+    assert r0 == 0 or 100 * (tail + n_bh * steps[nq - r0]) > 10 * total
+    heavy = tiles[:first]
+    assert sorted(heavy) == sorted((bh, qt) for bh in range(n_bh) for qt in range(nq - r0, nq))
+    if snake_launch(n_bh, S, 64 if D <= 64 else 128 if D <= 128 else 256, 2):
+        check_snake_order([steps[qt] for _, qt in heavy])
+    else:  # each XCD: a contiguous block of whole heads' heavy ranks
+        for x in range(8):
+            pos = sorted(bh * r0 + (nq - 1 - qt) for bh, qt in heavy[x::8])
+            assert pos == list(range(pos[0], pos[0] + len(pos))) if pos else True
+    with pytest.raises(fa.FaError):
+        fa.fa_fwd_launch_order(B, H, S, D, dt, causal, wl, wr, 256, n)
+    with pytest.raises(fa.FaError):
+        fa.fa_fwd_launch_order(B, H, S, D, dt, causal, wl, wr, 0, 0)
 
 
 def check_snake_order(weights):

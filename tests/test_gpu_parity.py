@@ -119,6 +119,47 @@ def test_parity_launch_order_many_workgroups():
     check_every_row(w, q, k, v, out, lse)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("H,D,window", [(32, 64, (-1, -1)), (20, 128, (1024, -1)),
+                                        (10, 256, (-1, -1)), (3, 96, (-1, -1))])
+def test_parity_dynamic_tail(dtype, H, D, window):
+    """Causal launches with more workgroups than the device holds at once run
+    their lightest tiles in the dynamic order (workgroups take list positions
+    from a counter in the LSE word of row 0 of head 0, zeroed before the
+    launch): every element against the oracle, on two calls in a row into
+    the same buffers, whose LSE starts as NaN."""
+    import io_aware_exact_22_amd as fa
+
+    B = 1
+    S = 4096 if H > 3 else 30000
+    dcode = fa.FA_DTYPE_BF16 if dtype == torch.bfloat16 else fa.FA_DTYPE_FP16
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    first = fa.fa_fwd_launch_order(B, H, S, D, dcode, 1, window[0], window[1], cus, 0)[2]
+    assert first >= 0, "the case must take the dynamic order"
+    scale = 1.0 / math.sqrt(D)
+    q, k, v = make_qkv(B, S, H, D, dtype, 77 + H)
+    what = f"dynamic tail: B{B} S{S} H{H} D{D} {dtype} window={window} first={first}"
+    print("run", what, flush=True)
+    qd, kd, vd = (x.cuda() for x in (q, k, v))
+    out = torch.empty_like(qd)
+    lse = torch.full((B, H, S), float("nan"), dtype=torch.float32, device="cuda")
+    res = []
+    for _ in range(2):
+        fa.flash_attn_fwd(qd, kd, vd, softmax_scale=scale, causal=True, window_size=window,
+                          out=out, lse=lse)
+        torch.cuda.synchronize()
+        res.append((out.cpu(), lse.cpu()))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+    if S > 4096:  # the 30000-row case: every row through the row-chunked oracle
+        from types import SimpleNamespace
+        w = SimpleNamespace(name="dyn", B=B, H=H, S=S, D=D, dtype=dtype, causal=True,
+                            window=window, scale=scale)
+        check_every_row(w, q, k, v, res[0][0], res[0][1], chunk_rows=4096)
+        return
+    ref_out, ref_lse = oracle.fwd(q, k, v, scale, True, window)
+    assert_close(res[0][0], res[0][1], ref_out, ref_lse, dtype, what)
+
+
 @pytest.mark.parametrize("name", ["tiny_fp32", "gpt_causal_2k", "full_4k_d64"])
 @pytest.mark.parametrize("seed", [None, 101, 102])
 def test_parity_named_small_workloads(name, seed):
