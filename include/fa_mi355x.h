@@ -300,7 +300,8 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* out, const f
            int64_t D, float scale, int causal, int64_t window_left, int64_t window_right,
            int dtype, void* workspace, int64_t workspace_bytes, void* stream);
 
-/* fa_bwd_workspace_size -- the workspace fa_bwd needs in *bytes: B * H * S * 4.
+/* fa_bwd_workspace_size -- the workspace fa_bwd needs in *bytes: B * H * S * 4
+ * (fp32 D_i per row) plus 64 (the counters of the passes' dynamic order).
  * Pure function.  Returns FA_OK, FA_ERR_NULL or the shape / head-dimension /
  * dtype status of fa_fwd_check_args (fp32: FA_ERR_DTYPE). */
 int fa_bwd_workspace_size(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int64_t* bytes);

@@ -366,7 +366,7 @@ FA_API int fa_bwd_workspace_size(int64_t B, int64_t H, int64_t S, int64_t D, int
     const int rc = check_problem(B, H, S, D, 0, -1, -1, dtype, &nbytes, &lbytes, kBwdMaxD);
     if (rc != FA_OK) return rc;
     if (dtype == FA_DTYPE_FP32) return FA_ERR_DTYPE;
-    *bytes = lbytes;  // fp32 [B, H, S], the size of lse
+    *bytes = lbytes + fa::kBwdCounterBytes;  // fp32 [B, H, S] (the size of lse), two counters
     return FA_OK;
 }
 
@@ -394,12 +394,13 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* out, 
         for (int p = o + 1; p < 3; ++p)
             if (overlaps(outs[o], nbytes, outs[p], nbytes)) return FA_ERR_ALIAS;
     }
-    if (!workspace || workspace_bytes < lbytes || ((uintptr_t)workspace & 15u))
+    const int64_t wbytes = lbytes + fa::kBwdCounterBytes;
+    if (!workspace || workspace_bytes < wbytes || ((uintptr_t)workspace & 15u))
         return FA_ERR_WORKSPACE;
     for (int i = 0; i < 6; ++i)
-        if (overlaps(workspace, lbytes, ins[i], in_bytes[i])) return FA_ERR_WORKSPACE;
+        if (overlaps(workspace, wbytes, ins[i], in_bytes[i])) return FA_ERR_WORKSPACE;
     for (int o = 0; o < 3; ++o)
-        if (overlaps(workspace, lbytes, outs[o], nbytes)) return FA_ERR_WORKSPACE;
+        if (overlaps(workspace, wbytes, outs[o], nbytes)) return FA_ERR_WORKSPACE;
     const fa::LaunchArgs f = make_args(q, k, v, nullptr, nullptr, B, H, S, D, scale, causal,
                                        window_left, window_right, dtype, stream);
     fa::BwdArgs a;
@@ -413,6 +414,7 @@ FA_API int fa_bwd(const void* q, const void* k, const void* v, const void* out, 
     a.dk = dk;
     a.dv = dv;
     a.di = (float*)workspace;
+    a.counters = (unsigned*)((char*)workspace + lbytes);
     a.B = B;
     a.H = H;
     a.S = S;

@@ -47,12 +47,15 @@ template <> __device__ inline void unpack2<_Float16>(unsigned x, float& a, float
 }
 
 // D_i = dO_i . O_i in fp32, [B, H, S]; one thread per row.  PAD: the
-// tensors' head dimension is dv_in < D (a multiple of 16); otherwise D.
+// tensors' head dimension is dv_in < D (a multiple of 16); otherwise D.  Also
+// zeroes the two dynamic-order counters of the passes that follow.
 template <typename T, int D, bool PAD>
 __global__ __launch_bounds__(256) void fa_bwd_rowdot_kernel(const T* __restrict__ out,
                                                             const T* __restrict__ dout,
                                                             float* __restrict__ di, int B, int H,
-                                                            int S, int dv_in) {
+                                                            int S, int dv_in,
+                                                            unsigned* __restrict__ counters) {
+    if (blockIdx.x == 0 && threadIdx.x < 2) counters[threadIdx.x] = 0u;
     const int dv = PAD ? dv_in : D;
     const int64_t R = (int64_t)B * H * S;
     const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (b * H + h) * S + s
@@ -93,7 +96,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ di,
     T* __restrict__ dq, int B, int H, int S, float c, float scale, int causal, int wl, int wr,
-    int n_qt, int dv_in) {
+    int n_qt, int dv_in, unsigned* __restrict__ counter, int dyn_first) {
     const int dv = PAD ? dv_in : D;
     constexpr int kBias = PAD ? kDmaBias : 0;
     typedef Tile<D, 4, 64> L;
@@ -108,8 +111,12 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_kernel(
     const int hh = lane >> 5, ql = lane & 31;
 
     uint32_t bh, qt32;
-    workgroup_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt, causal != 0,
-                   snake_launch((int64_t)B * H, S, D, sizeof(T)), &bh, &qt32);
+    if (dyn_first >= 0)  // the forward's dynamic tail (dyn_first_position)
+        dynamic_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt, dyn_first,
+                     snake_launch((int64_t)B * H, S, D, sizeof(T)), counter, &bh, &qt32);
+    else
+        workgroup_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt, causal != 0,
+                       snake_launch((int64_t)B * H, S, D, sizeof(T)), &bh, &qt32);
     const int qt = (int)qt32;
     const int bb = (int)(bh / (uint32_t)H), h = (int)(bh % (uint32_t)H);
     const MaskSpec ms{S, causal, wl, wr};
@@ -316,7 +323,7 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 1) void fa_bwd_dkdv_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const T* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ di,
     T* __restrict__ dk, T* __restrict__ dv, int B, int H, int S, float c, float scale, int causal,
-    int wl, int wr, int n_kt, int dv_in) {
+    int wl, int wr, int n_kt, int dv_in, unsigned* __restrict__ counter, int dyn_first) {
     // PAD: the tensors' head dimension is ncol = dv_in < D, as in the dQ kernel
     const int ncol = PAD ? dv_in : D;
     constexpr int kBias = PAD ? kDmaBias : 0;
@@ -338,9 +345,14 @@ __global__ __launch_bounds__(256, D == 128 ? 2 : 1) void fa_bwd_dkdv_kernel(
 
     // key blocks: with the causal mask block 0 sees every row, so the lowest
     // blocks (the heaviest) run first
+    // (the dynamic tail, dyn_first_key_blocks: rank r = key block r)
     uint32_t bh, t32;
-    workgroup_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_kt, causal != 0,
-                   snake_launch((int64_t)B * H, S, D, sizeof(T)), &bh, &t32);
+    if (dyn_first >= 0)
+        dynamic_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_kt, dyn_first,
+                     snake_launch((int64_t)B * H, S, D, sizeof(T)), counter, &bh, &t32);
+    else
+        workgroup_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_kt, causal != 0,
+                       snake_launch((int64_t)B * H, S, D, sizeof(T)), &bh, &t32);
     const int kblk = causal ? n_kt - 1 - (int)t32 : (int)t32;
     const int bb = (int)(bh / (uint32_t)H), h = (int)(bh % (uint32_t)H);
     const int64_t row_stride = (int64_t)H * ncol;
@@ -569,22 +581,37 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
     const int64_t rows = a.B * a.H * a.S;
     hipLaunchKernelGGL((fa_bwd_rowdot_kernel<T, D, PAD>), dim3((unsigned)((rows + 255) / 256)),
                        dim3(256), 0, a.stream, (const T*)a.out, (const T*)a.dout, a.di, (int)a.B,
-                       (int)a.H, (int)a.S, (int)a.D);
+                       (int)a.H, (int)a.S, (int)a.D, a.counters);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // the dynamic tails of causal passes (dyn_first_position, dyn_first_key_blocks):
+    // three dQ workgroups per compute unit at D = 64, two at 128; two dK / dV
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        cus = 0;  // the static order
+    }
+    const MaskSpec ms{a.S, a.causal, a.wl, a.wr};
     const int n_qt = (int)((a.S + 127) / 128);
+    const int dyn_q = cus > 0 ? (int)dyn_first_position(ms, a.B * a.H, 128, 64,
+                                                        resident_wgs_per_cu(D) * (int64_t)cus)
+                              : -1;
     hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, PAD>), dim3((unsigned)(a.B * a.H * n_qt)), dim3(256),
                        0, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout,
                        a.lse, (const float*)a.di, (T*)a.dq, (int)a.B, (int)a.H, (int)a.S, a.c,
-                       a.scale, a.causal, (int)a.wl, (int)a.wr, n_qt, (int)a.D);
+                       a.scale, a.causal, (int)a.wl, (int)a.wr, n_qt, (int)a.D, a.counters,
+                       dyn_q);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int n_kt = (int)((a.S + kBwdKeys - 1) / kBwdKeys);
+    const int dyn_k = cus > 0 ? (int)dyn_first_key_blocks(ms, a.B * a.H, kBwdKeys, 2 * (int64_t)cus)
+                              : -1;
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, PAD>), dim3((unsigned)(a.B * a.H * n_kt)),
                        dim3(256), 0, a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
                        (const T*)a.dout, a.lse, (const float*)a.di, (T*)a.dk, (T*)a.dv, (int)a.B,
                        (int)a.H, (int)a.S, a.c, a.scale, a.causal, (int)a.wl, (int)a.wr, n_kt,
-                       (int)a.D);
+                       (int)a.D, a.counters + 1, dyn_k);
     return hipGetLastError();
 }
 

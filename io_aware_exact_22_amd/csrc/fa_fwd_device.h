@@ -269,19 +269,9 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
         // word of lse row 0 of (b, h) = (0, 0), which the host zeroes before
         // the launch.  That row belongs to the last position, so its
         // workgroup writes the word only after every position has been taken.
-        __shared__ uint32_t s_pos;
-        const uint32_t n_bh = (uint32_t)B * (uint32_t)H;
-        uint32_t pos;
-        if ((int)blockIdx.x < dyn_first) {
-            pos = dyn_static_position(blockIdx.x, n_bh, (uint32_t)dyn_first,
-                                      snake_launch((int64_t)B * H, S, D, sizeof(T)));
-        } else {
-            if (threadIdx.x == 0)
-                s_pos = (uint32_t)dyn_first + atomicAdd(reinterpret_cast<unsigned*>(lse), 1u);
-            __syncthreads();
-            pos = s_pos;
-        }
-        dyn_list_tile(pos, n_bh, (uint32_t)n_qt, &bh, &qt32);
+        dynamic_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt, dyn_first,
+                     snake_launch((int64_t)B * H, S, D, sizeof(T)),
+                     reinterpret_cast<unsigned*>(lse), &bh, &qt32);
     } else {
         workgroup_tile(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt, !KVC && causal != 0,
                        snake_launch((int64_t)B * H, S, D, sizeof(T)), &bh, &qt32);

@@ -73,6 +73,9 @@ struct BwdArgs {
     void* dk;
     void* dv;
     float* di;  // workspace: D_i = dO_i . O_i, fp32 [B, H, S]
+    // workspace, after di: the dynamic-order counters of the dQ and the
+    // dK / dV pass (zeroed by the D_i pass)
+    unsigned* counters;
     int64_t B, H, S, D;
     float c;      // as in LaunchArgs
     float scale;  // softmax scale
@@ -81,6 +84,8 @@ struct BwdArgs {
     int dtype;
     hipStream_t stream;
 };
+// workspace bytes after D_i: the two counters, padded
+constexpr int64_t kBwdCounterBytes = 64;
 // Enqueues the three backward kernels for validated arguments; D other than
 // 64 and 128 (a multiple of 16 up to 128) through launch_bwd_padded.
 hipError_t launch_bwd(const BwdArgs& a);

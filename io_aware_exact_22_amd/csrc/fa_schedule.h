@@ -289,31 +289,81 @@ __host__ __device__ inline uint32_t dyn_static_position(uint32_t w, uint32_t n_b
     return (r0 - 1 - q) * n_bh + (bh + n_bh - 1) % n_bh;
 }
 
-// The first dynamic position of a launch of Q tiles bm x K/V tiles bn over
-// n_bh (batch, head) pairs on a device that holds `slots` workgroups at once,
-// or -1 for the static order (not causal, or no more workgroups than slots):
-// r0 * n_bh, r0 the first rank whose tail (ranks r0 .. n_qt - 1 of all heads)
-// holds at most kDynSharePct of the K/V steps.
+// Workgroup w's (b * H + h, tile) in a launch with a dynamic tail from
+// position first: by id below it, else the next position from *counter (zero
+// before the launch), taken by thread 0 and shared through LDS.  Every thread
+// of the workgroup calls it (it holds a barrier).  tile = n_tiles - 1 - rank.
+__device__ inline void dynamic_tile(uint32_t w, uint32_t n_bh, uint32_t n_tiles, int first,
+                                    bool snake, unsigned* counter, uint32_t* bh,
+                                    uint32_t* tile) {
+    __shared__ uint32_t s_pos;
+    uint32_t pos;
+    if ((int)w < first) {
+        pos = dyn_static_position(w, n_bh, (uint32_t)first, snake);
+    } else {
+        if (threadIdx.x == 0) s_pos = (uint32_t)first + atomicAdd(counter, 1u);
+        __syncthreads();
+        pos = s_pos;
+    }
+    dyn_list_tile(pos, n_bh, n_tiles, bh, tile);
+}
+
+// The first dynamic position of a list of n_tiles ranks over n_bh (batch,
+// head) pairs on a device that holds `slots` workgroups at once, where rank r
+// weighs weight(r) steps: r0 * n_bh, r0 the first rank whose tail (ranks r0 ..
+// n_tiles - 1 of all heads) holds at most kDynSharePct of the steps, or -1
+// for the static order (no more workgroups than slots, or an empty tail).
+template <typename Weight>
+inline int64_t dyn_first_from_weights(int64_t n_bh, int64_t n_tiles, int64_t slots,
+                                      Weight weight) {
+    if (n_bh * n_tiles <= slots) return -1;
+    int64_t total = 0;
+    for (int64_t r = 0; r < n_tiles; ++r) total += weight(r);
+    int64_t tail = 0, r0 = n_tiles;
+    for (int64_t r = n_tiles - 1; r >= 0; --r) {
+        if (100 * (tail + weight(r)) > kDynSharePct * total) break;
+        tail += weight(r);
+        r0 = r;
+    }
+    return r0 < n_tiles ? r0 * n_bh : -1;
+}
+
+// The forward (and the dQ pass): Q tiles bm x K/V tiles bn, rank r = Q tile
+// n_qt - 1 - r weighing its K/V tiles; -1 unless causal.
 inline int64_t dyn_first_position(const MaskSpec& m, int64_t n_bh, int64_t bm, int64_t bn,
                                   int64_t slots) {
     if (!m.causal) return -1;
     const int64_t n_qt = (m.S + bm - 1) / bm;
-    if (n_bh * n_qt <= slots) return -1;
-    int64_t total = 0;
-    for (int64_t qt = 0; qt < n_qt; ++qt) {
-        int64_t t0, t1;
-        q_tile_kv_range(m, qt, bm, bn, &t0, &t1);
-        total += t1 - t0;
-    }
-    int64_t tail = 0, r0 = n_qt;
-    for (int64_t r = n_qt - 1; r >= 0; --r) {
+    return dyn_first_from_weights(n_bh, n_qt, slots, [&](int64_t r) {
         int64_t t0, t1;
         q_tile_kv_range(m, n_qt - 1 - r, bm, bn, &t0, &t1);
-        if (100 * (tail + t1 - t0) > kDynSharePct * total) break;
-        tail += t1 - t0;
-        r0 = r;
-    }
-    return r0 < n_qt ? r0 * n_bh : -1;
+        return t1 - t0;
+    });
+}
+
+// Query rows [*r0, *r1] that hold an allowed key of key block [j0, j0 + bk)
+// (empty when *r0 > *r1).
+__host__ __device__ inline void key_block_rows(const MaskSpec& m, int64_t j0, int64_t bk,
+                                               int64_t* r0, int64_t* r1) {
+    const int64_t j1 = j0 + bk - 1 < m.S - 1 ? j0 + bk - 1 : m.S - 1;
+    int64_t lo = m.causal ? j0 : 0, hi = m.S - 1;
+    if (m.wr >= 0 && j0 - m.wr > lo) lo = j0 - m.wr;
+    if (m.wl >= 0 && j1 + m.wl < hi) hi = j1 + m.wl;
+    *r0 = lo;
+    *r1 = hi;
+}
+
+// The dK / dV pass: key blocks of bk keys, rank r = key block r (with the
+// causal mask the lowest blocks hold the most rows) weighing its rows; -1
+// unless causal.
+inline int64_t dyn_first_key_blocks(const MaskSpec& m, int64_t n_bh, int64_t bk, int64_t slots) {
+    if (!m.causal) return -1;
+    const int64_t n_kt = (m.S + bk - 1) / bk;
+    return dyn_first_from_weights(n_bh, n_kt, slots, [&](int64_t r) {
+        int64_t r0, r1;
+        key_block_rows(m, r * bk, bk, &r0, &r1);
+        return r1 >= r0 ? r1 - r0 + 1 : 0;
+    });
 }
 
 }  // namespace fa

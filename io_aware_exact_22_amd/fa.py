@@ -630,8 +630,8 @@ def flash_attn_bwd(dout, q, k, v, out, lse, softmax_scale: float | None = None,
                    dv=None, stream=None):
     """Gradients (dq, dk, dv) of flash_attn_fwd's output for the output
     gradient ``dout``, given the forward's q, k, v and its out and lse.
-    bf16 / fp16 tensors [B, S, H, D]; the fp32 workspace (B * H * S floats)
-    and the gradients are allocated here when None."""
+    bf16 / fp16 tensors [B, S, H, D]; the workspace (fa_bwd_workspace_size
+    bytes) and the gradients are allocated here when None."""
     import torch
 
     _check_qkv(q, k, v)
@@ -647,7 +647,7 @@ def flash_attn_bwd(dout, q, k, v, out, lse, softmax_scale: float | None = None,
     dv = torch.empty_like(v) if dv is None else dv
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         _check_like(name, t, q)
-    need = B * H * S * 4
+    need = fa_bwd_workspace_size(B, H, S, D, dtype)
     ws_ptr, ws_bytes, _ws = _workspace(workspace, need, q, torch.float32, stream)
     with torch.cuda.device(q.device):
         rc = fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),

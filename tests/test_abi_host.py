@@ -141,12 +141,12 @@ def test_splitkv_rejects_before_any_hip_call(kw, status):
 
 
 def test_bwd_workspace_size():
-    assert fa.fa_bwd_workspace_size(2, 16, 2048, 64, fa.FA_DTYPE_BF16) == 2 * 16 * 2048 * 4
+    assert fa.fa_bwd_workspace_size(2, 16, 2048, 64, fa.FA_DTYPE_BF16) == 2 * 16 * 2048 * 4 + 64
     with pytest.raises(fa.FaError) as e:
         fa.fa_bwd_workspace_size(2, 16, 2048, 64, fa.FA_DTYPE_FP32)
     assert e.value.status == -5
     # bf16 / fp16: any multiple of 16 up to 128
-    assert fa.fa_bwd_workspace_size(2, 16, 2048, 80, fa.FA_DTYPE_BF16) == 2 * 16 * 2048 * 4
+    assert fa.fa_bwd_workspace_size(2, 16, 2048, 80, fa.FA_DTYPE_BF16) == 2 * 16 * 2048 * 4 + 64
     for bad in (72, 144, 256):
         with pytest.raises(fa.FaError) as e:
             fa.fa_bwd_workspace_size(2, 16, 2048, bad, fa.FA_DTYPE_BF16)

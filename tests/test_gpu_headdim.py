@@ -250,7 +250,8 @@ def test_headdim_bwd(dtype, D, causal, window, B, S, H):
     qd, kd, vd, dod = (t.cuda() for t in (q, k, v, do))
     out, lse = fa.flash_attn_fwd(qd, kd, vd, causal=causal, window_size=window)
     grads = [guarded((B, S, H, D), dtype) for _ in range(3)]
-    ws, wbuf = guarded((B * H * S,), torch.float32)
+    dcode = fa.FA_DTYPE_BF16 if dtype == torch.bfloat16 else fa.FA_DTYPE_FP16
+    ws, wbuf = guarded(((fa.fa_bwd_workspace_size(B, H, S, D, dcode) + 3) // 4,), torch.float32)
     fa.flash_attn_bwd(dod, qd, kd, vd, out, lse, causal=causal, window_size=window, workspace=ws,
                       dq=grads[0][0], dk=grads[1][0], dv=grads[2][0])
     torch.cuda.synchronize()

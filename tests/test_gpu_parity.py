@@ -477,6 +477,16 @@ def test_bwd_lengths(S, causal):
     check_bwd(1, S, 2, 128, torch.bfloat16, causal, (-1, -1), seed=S + 3)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float16])
+@pytest.mark.parametrize("H,D", [(32, 64), (20, 128)])
+def test_bwd_dynamic_tail(dtype, H, D):
+    """Causal backward passes with more workgroups than the device holds at
+    once take their lightest tiles (Q tiles for dQ, key blocks for dK / dV) in
+    the dynamic order, with counters in the workspace: every element against
+    the oracle."""
+    check_bwd(1, 4096, H, D, dtype, True, (-1, -1), seed=90 + H)
+
+
 def test_bwd_gpt_causal_2k():
     """The 2K causal workload's shape (B2 H16 S2048 D64 bf16), every element."""
     check_bwd(2, 2048, 16, 64, torch.bfloat16, True, (-1, -1), seed=81)
