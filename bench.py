@@ -45,6 +45,7 @@ KERNEL_SOURCES = ["io_aware_exact_22_amd/csrc/fa_fwd_device.h",
                   "io_aware_exact_22_amd/csrc/fa_fwd_kernels.hip",
                   "io_aware_exact_22_amd/csrc/fa_fwd_launch_cfg.h",
                   "io_aware_exact_22_amd/csrc/fa_kernel_common.h",
+                  "io_aware_exact_22_amd/csrc/fa_launch.h",
                   "io_aware_exact_22_amd/csrc/fa_schedule.h"]
 
 
@@ -541,7 +542,9 @@ def main() -> int:
         g.manual_seed(w.seed + 1000)
         do_cpu = torch.randn(qd.shape, generator=g, dtype=torch.float32).to(w.dtype)
         dod = do_cpu.to(dev)
-        ws_b = torch.empty((w.B, w.H, w.S), dtype=torch.float32, device=dev)
+        need = fa.fa_bwd_workspace_size(
+            w.B, w.H, w.S, w.D, fa.FA_DTYPE_BF16 if w.dtype == torch.bfloat16 else fa.FA_DTYPE_FP16)
+        ws_b = torch.empty((need + 3) // 4, dtype=torch.float32, device=dev)
         dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
 
         def step():

@@ -81,8 +81,8 @@ FA_API const char* fa_status_string(int status) {
     case FA_ERR_ALIAS: return "out and lse must not overlap the inputs or each other";
     case FA_ERR_HIP: return "the HIP kernel launch failed";
     case FA_ERR_WORKSPACE:
-        return "the split-KV workspace is NULL, too small, not 16-byte aligned or overlaps an "
-               "input or output";
+        return "the workspace is NULL, too small, not 16-byte aligned or overlaps an input or "
+               "output";
     case FA_ERR_SPLITS:
         return "n_splits must be in [1, FA_MAX_SPLITS] (fa_fwd_kvcache: [1, FA_MAX_KV_SPLITS])";
     case FA_ERR_BLOCKMASK:
