@@ -39,7 +39,9 @@
 //    while the VALU computes exp / pack / row sum of tile j, and the P V MFMAs
 //    of tile j run while the VALU takes the row max of tile j+1.  The
 //    interleave is fixed with scheduling-group barriers so the matrix cores
-//    and the vector ALU work at the same time.
+//    and the vector ALU work at the same time.  bf16 skips the row max on the
+//    mask-free tiles after the first and checks each tile's weight sum
+//    instead (check_sum): the reference only has to bound the weights.
 //  * Whole K/V tiles outside the causal / window mask are not visited; the
 //    tiles inside it for every row of the workgroup run a loop body that has
 //    no mask code at all; the few boundary tiles apply the mask.
@@ -48,7 +50,10 @@
 //    all its heads first, so the light tiles fill the end of the launch.  When
 //    every head's K/V fits in half the MALL, or there are fewer heads than
 //    XCDs, and for causal split launches, the tiles (parts) of all heads are
-//    instead dealt to the XCDs in snake order of weight (fa_schedule.h).
+//    instead dealt to the XCDs in snake order of weight (fa_schedule.h).  A
+//    causal launch larger than the device runs its lightest tenth of the
+//    work in a dynamic order, each late workgroup taking the next tile from a
+//    counter (dynamic_tile), so faster XCDs take more of it.
 //  * Probabilities are rounded to the input dtype (RNE, v_cvt_pk_*) for the
 //    P V MFMA.  The row sum adds the fp32 weights for bf16 and the fp16-rounded
 //    weights two at a time (v_dot2c with ones) for fp16.  Max, exp and the
