@@ -84,6 +84,9 @@ typedef enum {
  *          O is rounded to nearest-even from fp32.
  * lse      device pointer, contiguous [B, H, S] fp32; fully written with the
  *          natural-log log-sum-exp of the scaled, masked scores of each row.
+ *          A causal bf16 / fp16 launch larger than the device also counts its
+ *          dynamic tile order in the word of row 0 of (b, h) = (0, 0) while it
+ *          runs (fa_fwd_launch_order); the word holds its LSE on return.
  * B, H, S  batch, heads, sequence length (one S for queries and keys), >= 1.
  * D        head dimension.  bf16 / fp16: any multiple of 16 from 16 to 256
  *          (the pages ask Tensor Core shapes to be multiples of 8: section 4.2
