@@ -163,7 +163,9 @@ int fa_fwd_tile_schedule(int64_t S, int64_t D, int dtype, int causal, int64_t wi
  * within 128 MiB (half the MALL, so every XCD can work on every head), the
  * tiles of all heads are instead ordered heaviest first and dealt to the XCDs
  * in snake order (0..7, 7..0, ...): every XCD gets the same share of the work
- * and runs it heaviest first.
+ * and runs it heaviest first, in groups of 32 workgroups (one per compute
+ * unit of the XCD), every odd whole group lightest first, so that the units
+ * that got the heaviest tiles also get lighter ones.
  * Returns FA_OK, or FA_ERR_* for bad arguments or wg outside the grid.
  */
 int fa_fwd_workgroup_tile(int64_t B, int64_t H, int64_t S, int64_t D, int dtype, int causal,

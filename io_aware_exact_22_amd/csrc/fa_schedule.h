@@ -143,6 +143,8 @@ __host__ __device__ inline void q_tile_interior_range(const MaskSpec& m, int64_t
 // closer fit to longest-first scheduling whenever every head's K/V can stay in
 // the MALL while all XCDs work on all heads (snake_launch).
 constexpr uint32_t kXcds = 8;
+// compute units per XCD of the MI355X (256 / 8)
+constexpr uint32_t kCusPerXcd = 32;
 // K/V bytes of all heads up to which a causal launch is dealt in snake order:
 // half of the MI355X's 256 MB MALL
 constexpr int64_t kSnakeKvBytes = int64_t(128) << 20;
@@ -166,7 +168,16 @@ __host__ __device__ inline void workgroup_tile(uint32_t w, uint32_t n_bh, uint32
                                                uint32_t* qt) {
     const uint32_t n = n_bh * n_qt;
     if (by_weight && snake) {  // list: rank-major, heads next to each other
-        const uint32_t p = snake_item(w, n);
+        // An XCD places its first kCusPerXcd workgroups one per compute unit,
+        // then the next kCusPerXcd on the same units again, and so on; every
+        // odd such group takes its positions in reverse, so that a unit that
+        // got one of the heaviest tiles shares with one of the lighter ones
+        // (whole groups of 8 * kCusPerXcd workgroups only: a bijection).
+        const uint32_t x = w % kXcds, k = w / kXcds, g = k / kCusPerXcd;
+        uint32_t ww = w;
+        if ((g & 1) && kXcds * kCusPerXcd * (g + 1) <= n)
+            ww = x + kXcds * (g * kCusPerXcd + (kCusPerXcd - 1 - k % kCusPerXcd));
+        const uint32_t p = snake_item(ww, n);
         *bh = p % n_bh;
         *qt = n_qt - 1 - p / n_bh;
         return;

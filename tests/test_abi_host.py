@@ -314,10 +314,20 @@ def test_workgroup_order(B, H, S, causal):
     tiles = [fa.fa_fwd_workgroup_tile(B, H, S, 128, dt, causal, -1, -1, w) for w in range(n)]
     assert sorted(tiles) == [(bh, qt) for bh in range(B * H) for qt in range(nq)]
     if causal and snake_launch(B * H, S, 128, 2):
-        check_snake_order([visits[qt] for _, qt in tiles])
-        # the list is rank-major: heads next to each other, heaviest rank first
-        order = sorted(range(n), key=lambda w: (w // 8, w % 8 if (w // 8) % 2 == 0 or
-                                                (w // 8 + 1) * 8 > n else 7 - w % 8))
+        check_snake_order([visits[qt] for _, qt in tiles], cu_groups=True)
+        # the list is rank-major: heads next to each other, heaviest rank first;
+        # within an XCD every odd group of 32 workgroups (one per compute unit)
+        # takes its positions in reverse
+        def unpaired(w):
+            x, k = w % 8, w // 8
+            g = k // 32
+            if g % 2 == 1 and 256 * (g + 1) <= n:
+                return x + 8 * (32 * g + 31 - k % 32)
+            return w
+        order = sorted(range(n), key=lambda w: (unpaired(w) // 8, unpaired(w) % 8
+                                                if (unpaired(w) // 8) % 2 == 0 or
+                                                (unpaired(w) // 8 + 1) * 8 > n
+                                                else 7 - unpaired(w) % 8))
         assert [tiles[w] for w in order] == [(p % (B * H), nq - 1 - p // (B * H))
                                              for p in range(n)]
         return
@@ -402,14 +412,26 @@ def test_launch_order_dynamic_tail(B, H, S, D, window, causal):
         fa.fa_fwd_launch_order(B, H, S, D, dt, causal, wl, wr, 0, 0)
 
 
-def check_snake_order(weights):
+def check_snake_order(weights, cu_groups=False):
     """weights[w]: the K/V steps of workgroup w.  Every XCD (workgroups x, x + 8,
     ...) runs its items heaviest first, and the XCDs' summed steps differ by at
-    most twice the heaviest item."""
+    most twice the heaviest item.  cu_groups: the XCD's items come in groups of
+    32 (one per compute unit), each group at least as heavy as the next; an odd
+    group that is whole runs lightest first, so that the units that got the
+    heaviest items get the lighter ones of the next group."""
     sums = []
     for x in range(8):
         seq = weights[x::8]
-        assert all(a >= b for a, b in zip(seq, seq[1:])), (x, seq[:20])
+        if not cu_groups:
+            assert all(a >= b for a, b in zip(seq, seq[1:])), (x, seq[:20])
+        else:
+            groups = [seq[i:i + 32] for i in range(0, len(seq), 32)]
+            for g, grp in enumerate(groups):
+                whole = 256 * (g + 1) <= len(weights)
+                run = grp[::-1] if g % 2 == 1 and whole else grp
+                assert all(a >= b for a, b in zip(run, run[1:])), (x, g, grp[:20])
+                if g + 1 < len(groups):
+                    assert min(grp) >= max(groups[g + 1]), (x, g)
         sums.append(sum(seq))
     assert max(sums) - min(sums) <= 2 * max(weights), sums
 
