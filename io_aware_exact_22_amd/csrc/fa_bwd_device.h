@@ -222,11 +222,13 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_kernel(
         }
     }
     // S^T (or dP^T) of one tile: rows of `tile` against the fragment f
+    // (block by block: the weights of block 0 can start while block 1 is
+    // still on the matrix core)
     auto scores = [&](f32x16(&s)[KB], const unsigned char* tile, const u32x4(&f)[KSTEPS]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
+            for (int kk = 0; kk < KSTEPS; ++kk) {
                 const u32x4 a = *reinterpret_cast<const u32x4*>(tile + 32 * kb * RB + kaddr[kk]);
                 s[kb] = Mfma<T>::mma(a, f[kk], kk == 0 ? f32x16{0} : s[kb]);
             }
@@ -250,7 +252,9 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_kernel(
 
     load(k, kt0, lds_k0);
     load(v, kt0, lds_v0);
-    for (int j = kt0; j < kt1; ++j) {
+    // one tile; MASK: it holds a masked pair (outside [ki0, ki1))
+    auto step = [&](int j, auto mask_tag) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         const bool st = ((j - kt0) & 1) != 0;
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();  // tile j has landed; every wave is done with tile j-1
@@ -263,7 +267,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_kernel(
         f32x16 s[KB], dp[KB];
         scores(s, kst, qf);
         scores(dp, vst, gf);
-        if (j < ki0 || j >= ki1) {
+        if (MASK) {
             const int a = j * BN + 8 * hh - key_lo;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
@@ -282,6 +286,14 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_kernel(
             ds[e >> 3][(e & 7) >> 1] = Mfma<T>::pack2(p0 * (dp[kb][i] - Dr), p1 * (dp[kb][i + 1] - Dr));
         }
         tmul(acc, ds, kst);
+    };
+    // the masked tiles before and after the mask-free run get a loop of their
+    // own, so no branch splits the mask-free step's MFMA / VALU schedule
+    {
+        int j = kt0;
+        for (; j < ki0; ++j) step(j, BoolTag<true>{});
+        for (; j < ki1; ++j) step(j, BoolTag<false>{});
+        for (; j < kt1; ++j) step(j, BoolTag<true>{});
     }
     if (qrow < S) {
         T* op = dq + head_base + (int64_t)qrow * row_stride + 4 * hh;
