@@ -106,8 +106,9 @@ typedef enum {
  *
  * Ownership: the caller owns all five buffers; the library allocates nothing.
  * The call validates its arguments first (no HIP call, no write on error),
- * then enqueues one kernel and returns without synchronising.  Results are
- * valid once `stream` has been synchronised; faults during execution surface
+ * then enqueues one kernel (after a one-thread kernel that zeroes that LSE
+ * word, when the dynamic order is taken) and returns without synchronising.
+ * Results are valid once `stream` has been synchronised; faults during execution surface
  * there.  Repeated calls on the same inputs give bitwise identical results.
  * Returns FA_OK or a negative fa_status_t.
  */
@@ -383,8 +384,12 @@ int fa_fwd_blocksparse_workspace_size(int64_t B, int64_t H, int64_t S, int64_t D
  * Other arguments as fa_fwd.  out and lse must not overlap q, the pools, the
  * table or each other (FA_ERR_ALIAS); bad page geometry is FA_ERR_PAGES.
  * Validation happens before any HIP call.  Enqueues one kernel on `stream`
- * (two with a split) and returns without synchronising.  Returns FA_OK or a
- * negative fa_status_t.
+ * (two with a split) and returns without synchronising.  A causal bf16 / fp16
+ * call in one part with more workgroups than the device holds (two per
+ * compute unit at D <= 64, as at D <= 128) takes fa_fwd's dynamic order, with
+ * the same counter in the LSE word of row 0 of (b, h) = (0, 0) and the same
+ * one-thread kernel that zeroes it first.  Returns FA_OK or a negative
+ * fa_status_t.
  */
 int fa_fwd_paged(const void* q, const void* k_pages, const void* v_pages,
                  const int32_t* block_table, void* out, float* lse, int64_t B, int64_t H,

@@ -268,7 +268,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     if (SPLIT) {  // K/V part sp of the tile
         workgroup_tile_part(blockIdx.x, (uint32_t)B * (uint32_t)H, (uint32_t)n_qt,
                             (uint32_t)n_splits, !KVC && causal != 0, &bh, &qt32, &sp32);
-    } else if (!SPARSE && !PAGED && !KVC && dyn_first >= 0) {
+    } else if (!SPARSE && !KVC && dyn_first >= 0) {
         // The dynamic tail of a causal launch (dyn_first_position): workgroups
         // from dyn_first on take the next list position from a counter in the
         // word of lse row 0 of (b, h) = (0, 0), which the host zeroes before

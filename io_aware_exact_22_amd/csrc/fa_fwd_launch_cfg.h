@@ -14,11 +14,11 @@
 
 namespace fa {
 
-// The first dynamic list position of a dense launch (dyn_first_position),
-// for a device holding three workgroups per compute unit at D = 64, two at
-// 128 and one above; -1 (the static order) when the device cannot be queried.
+// The first dynamic list position of a dense or paged launch
+// (dyn_first_position), for a device holding per_cu workgroups per compute
+// unit; -1 (the static order) when the device cannot be queried.
 template <int D, int BM, int BN>
-int dynamic_first(const LaunchArgs& a) {
+int dynamic_first(const LaunchArgs& a, int per_cu) {
     if (!a.causal) return -1;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -27,7 +27,16 @@ int dynamic_first(const LaunchArgs& a) {
         return -1;
     }
     const MaskSpec m{a.S, a.causal, a.wl, a.wr};
-    return (int)dyn_first_position(m, a.B * a.H, BM, BN, resident_wgs_per_cu(D) * (int64_t)cus);
+    return (int)dyn_first_position(m, a.B * a.H, BM, BN, per_cu * (int64_t)cus);
+}
+
+// Zeroes the dynamic order's counter (the LSE word of row 0 of head 0) ahead
+// of a launch that takes the dynamic tail (dyn >= 0).
+inline hipError_t zero_dynamic_counter(const LaunchArgs& a, int dyn) {
+    if (dyn < 0) return hipSuccess;
+    hipLaunchKernelGGL((fa_zero_word_kernel<>), dim3(1), dim3(64), 0, a.stream,
+                       reinterpret_cast<unsigned*>(a.lse));
+    return hipGetLastError();
 }
 
 template <typename T, int D, int NW, int BN, bool PAD>
@@ -56,21 +65,21 @@ hipError_t launch_mfma_cfg(const LaunchArgs& a) {
     const int pg_stride = (int)a.pg_stride, pg_rows = paged ? (int)a.pg_rows : 1,
               pg_count = (int)a.pg_count;
     if (a.n_splits <= 1) {
-        if (paged)
+        if (paged) {
+            // (the paged kernel holds two workgroups per compute unit at D = 64)
+            const int dyn = dynamic_first<D, BM, BN>(a, D <= 64 ? 2 : resident_wgs_per_cu(D));
+            const hipError_t e = zero_dynamic_counter(a, dyn);
+            if (e != hipSuccess) return e;
             hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, false, true, false, PAD>),
                                dim3((unsigned)n_wg), dim3(NW * 64), 0, a.stream, (const T*)a.q,
                                (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
                                (int)a.S, a.c, a.causal, (int)a.wl, (int)a.wr, n_qt, 1, nullptr,
                                nullptr, nullptr, 0, 0, a.pg_table, pg_stride, pg_rows, pg_count,
-                               nullptr, 0, (int)a.D, -1);
-        else {
-            const int dyn = dynamic_first<D, BM, BN>(a);
-            if (dyn >= 0) {  // the dynamic order's counter starts at 0
-                hipLaunchKernelGGL((fa_zero_word_kernel<>), dim3(1), dim3(64), 0, a.stream,
-                                   reinterpret_cast<unsigned*>(a.lse));
-                hipError_t e = hipGetLastError();
-                if (e != hipSuccess) return e;
-            }
+                               nullptr, 0, (int)a.D, dyn);
+        } else {
+            const int dyn = dynamic_first<D, BM, BN>(a, resident_wgs_per_cu(D));
+            const hipError_t e = zero_dynamic_counter(a, dyn);
+            if (e != hipSuccess) return e;
             hipLaunchKernelGGL((fa_fwd_mfma_kernel<T, D, NW, BN, false, false, false, false, PAD>),
                                dim3((unsigned)n_wg), dim3(NW * 64), 0, a.stream, (const T*)a.q,
                                (const T*)a.k, (const T*)a.v, (T*)a.out, a.lse, (int)a.B, (int)a.H,
