@@ -251,6 +251,25 @@ def test_large_scale_stable():
     assert_close(out, lse, ref_o, ref_l, torch.bfloat16, "scale=50")
 
 
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+def test_late_large_score_jump(dtype):
+    """Every row meets one key late in its K/V range (key 900 of 1000) whose
+    scaled score is about 32 above the others' (46 in log2 units): weights
+    made against the first tiles' reference overflow fp16 (the wave's exact
+    recomputation then takes over) and far exceed the bf16 weight-sum check
+    (the reference moves up).  Both match the oracle: O is close to that
+    key's value row."""
+    B, S, H, D = 1, 1000, 2, 64
+    q, k, v = make_qkv(B, S, H, D, dtype, 12)
+    u = q[0, 0, 0].clone()
+    q[0, :, 0] = u
+    k[0, 900, 0] = 4 * u
+    out, lse = gpu_fwd(q, k, v, 0.125, False, (-1, -1))
+    ref_o, ref_l = oracle.fwd(q, k, v, 0.125, False, (-1, -1))
+    assert float(ref_l[0, 0].min()) > 20, "the jump must dominate every row of head 0"
+    assert_close(out, lse, ref_o, ref_l, dtype, f"late jump {dtype}")
+
+
 # ---------------------------------------------------------------- robustness
 def test_nan_rows_propagate_like_the_oracle():
     q, k, v = make_qkv(1, 257, 1, 64, torch.bfloat16, 11)
