@@ -39,8 +39,8 @@
 //    while the VALU computes exp / pack / row sum of tile j, and the P V MFMAs
 //    of tile j run while the VALU takes the row max of tile j+1.  The
 //    interleave is fixed with scheduling-group barriers so the matrix cores
-//    and the vector ALU work at the same time.  The steps skip the row max on
-//    the mask-free tiles after the first and check each tile's weight sum
+//    and the vector ALU work at the same time.  bf16 skips the row max on the
+//    mask-free tiles after the first and checks each tile's weight sum
 //    instead (check_sum): the reference only has to bound the weights.
 //  * Whole K/V tiles outside the causal / window mask are not visited; the
 //    tiles inside it for every row of the workgroup run a loop body that has
@@ -533,14 +533,13 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     bool moved = false;     // some row's reference moved for the current tile (wave-uniform)
     float l_run = 0.f;      // running sum over this half's keys
     float t_sum = 0.f;      // the current tile's weights of this lane (steps that check them)
-    // Once every row of the wave has a reference, the steps skip the row max
-    // of the next tile and check the weights afterwards (check_sum).  The
+    // bf16: once every row of the wave has a reference, the steps skip the row
+    // max of the next tile and check the weights afterwards (check_sum).  The
     // reference is then no longer a max of the scores, only a bound that
     // keeps the weights finite, which is all O, l and LSE need: they are
-    // exact for any reference.  An fp16 weight overflows past 2^16: a score
-    // that far above the reference (45 log2 units above the first tiles'
-    // maximum, say) leaves O non-finite, and the epilogue's exact
-    // recomputation takes the wave.
+    // exact for any reference.  fp16 keeps the max on every tile, since an
+    // fp16 weight overflows past 2^16.
+    constexpr bool kRefBySum = __is_same(T, __bf16);
     f32x16 o[DB];
 #pragma unroll
     for (int d = 0; d < DB; ++d) o[d] = f32x16{0};
@@ -610,7 +609,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
                 p[ip >> 3][(ip & 7) >> 1] = Mfma<T>::pack2(e[ip - 1], e[ip]);
                 if (Mfma<T>::kSumRounded) {  // two partial sums of packed pairs
                     const unsigned pk = p[ip >> 3][(ip & 7) >> 1];
-                    if (q == 0) ls[0] = Mfma<T>::sum2(pk, SEP ? 0.f : l_run);
+                    if (q == 0) ls[0] = Mfma<T>::sum2(pk, l_run);
                     else if (q == 1) ls[1] = Mfma<T>::sum2(pk, 0.f);
                     else ls[q & 1] = Mfma<T>::sum2(pk, ls[q & 1]);
                 } else {  // four partial sums of single weights
@@ -627,10 +626,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
                 }
             }
         }
-        if (Mfma<T>::kSumRounded && SEP) {
-            t_sum = ls[0] + ls[1];
-            l_run += t_sum;
-        } else if (Mfma<T>::kSumRounded) {
+        if (Mfma<T>::kSumRounded) {
             l_run = ls[0] + ls[1];
         } else if (SEP) {
             t_sum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
@@ -900,9 +896,9 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
             if (MODE != 2) interleave();
             if (MODE == 1) check_sum();
         } else {
-            softmax(sc, p, BoolTag<true>{});
+            softmax(sc, p, BoolTag<kRefBySum>{});
             pv(p, v_this);
-            check_sum();
+            if (kRefBySum) check_sum();
         }
     };
     // iterations [j0, j1), none of them the last; the stage alternates
@@ -946,7 +942,7 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
     if (ja > jl) ja = jl;
     int jb = ki1 - 1 < jl ? ki1 - 1 : jl;
     if (jb < ja) jb = ja;
-    {
+    if constexpr (kRefBySum) {
         // The row max of the first mask-free tile gives every row of the wave
         // a reference (all its keys are allowed for every row): the head
         // steps take it too (its mask changes nothing).  The mask-free steps
@@ -956,6 +952,10 @@ __global__ __launch_bounds__(NW * 64, D == 64 ? (PAGED ? 2 : 3) : 1) void fa_fwd
         run(kw0, jh, BoolTag<true>{}, IntTag<0>{});
         run(jh, jb, BoolTag<false>{}, IntTag<1>{});
         run(jb, jl, BoolTag<true>{}, IntTag<2>{});
+    } else {
+        run(kw0, ja, BoolTag<true>{}, IntTag<0>{});
+        run(ja, jb, BoolTag<false>{}, IntTag<0>{});
+        run(jb, jl, BoolTag<true>{}, IntTag<0>{});
     }
     if ((jl - kt0) & 1)
         step(jl, IntTag<1>{}, BoolTag<false>{}, BoolTag<true>{}, IntTag<0>{});

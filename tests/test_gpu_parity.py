@@ -254,11 +254,10 @@ def test_large_scale_stable():
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
 def test_late_large_score_jump(dtype):
     """Every row meets one key late in its K/V range (key 900 of 1000) whose
-    scaled score is about 32 above the others' (46 in log2 units): weights
-    made against the first tiles' reference overflow fp16 (the wave's exact
-    recomputation then takes over) and far exceed the bf16 weight-sum check
-    (the reference moves up).  Both match the oracle: O is close to that
-    key's value row."""
+    scaled score is about 32 above the others' (46 in log2 units): the bf16
+    steps, which skip the row max, see the tile's weights far exceed the
+    weight-sum check and move the reference up; fp16 takes the row max of
+    that tile.  Both match the oracle: O is close to that key's value row."""
     B, S, H, D = 1, 1000, 2, 64
     q, k, v = make_qkv(B, S, H, D, dtype, 12)
     u = q[0, 0, 0].clone()
