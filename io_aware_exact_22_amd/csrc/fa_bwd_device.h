@@ -252,7 +252,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_dq_kernel(
 
     load(k, kt0, lds_k0);
     load(v, kt0, lds_v0);
-    // one tile; MASK: it holds a masked pair (outside [ki0, ki1))
+    // one tile; MASK: it lies outside the mask-free run [ki0, ki1) and takes the mask
     auto step = [&](int j, auto mask_tag) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const bool st = ((j - kt0) & 1) != 0;
