@@ -197,9 +197,12 @@ def test_paged_raw_c_abi_call():
     compare(out, lse, *ref, torch.float16, "raw C ABI")
 
 
-@pytest.mark.parametrize("dtype,H,D", [(torch.bfloat16, 20, 128), (torch.float16, 32, 64),
-                                       (torch.bfloat16, 32, 64), (torch.float16, 6, 96)])
-def test_paged_dynamic_tail_equals_contiguous(dtype, H, D):
+@pytest.mark.parametrize("dtype,H,D,window", [(torch.bfloat16, 20, 128, (-1, -1)),
+                                              (torch.float16, 32, 64, (-1, -1)),
+                                              (torch.bfloat16, 32, 64, (-1, -1)),
+                                              (torch.float16, 6, 96, (-1, -1)),
+                                              (torch.bfloat16, 20, 128, (1024, -1))])
+def test_paged_dynamic_tail_equals_contiguous(dtype, H, D, window):
     """Causal paged launches with more workgroups than the device holds take
     fa_fwd's dynamic order (workgroups take the light tiles' list positions
     from a counter in the LSE word of row 0 of head 0, zeroed first): on two
@@ -212,10 +215,10 @@ def test_paged_dynamic_tail_equals_contiguous(dtype, H, D):
     S = 4096 if H > 6 else 12000
     dcode = fa.FA_DTYPE_BF16 if dtype == torch.bfloat16 else fa.FA_DTYPE_FP16
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    first = fa.fa_fwd_launch_order(B, H, S, D, dcode, 1, -1, -1, cus, 0)[2]
+    first = fa.fa_fwd_launch_order(B, H, S, D, dcode, 1, window[0], window[1], cus, 0)[2]
     assert first >= 0, "the case must take the dynamic order"
     q, k, v = make_qkv(B, S, H, D, dtype, 300 + H + D)
-    what = f"paged dynamic tail: B{B} S{S} H{H} D{D} {dtype}"
+    what = f"paged dynamic tail: B{B} S{S} H{H} D{D} {dtype} window={window}"
     print("run", what, flush=True)
     qd, kd, vd = (t.cuda() for t in (q, k, v))
     page_size = 256
@@ -226,13 +229,14 @@ def test_paged_dynamic_tail_equals_contiguous(dtype, H, D):
     lse = torch.full((B, H, S), float("nan"), dtype=torch.float32, device="cuda")
     res = []
     for _ in range(2):
-        fa.flash_attn_fwd_paged(qd, kp, vp, table, causal=True, out=out, lse=lse)
+        fa.flash_attn_fwd_paged(qd, kp, vp, table, causal=True, window_size=window, out=out,
+                                lse=lse)
         torch.cuda.synchronize()
         res.append((out.clone(), lse.clone()))
-    o2, l2 = fa.flash_attn_fwd(qd, kd, vd, causal=True)
+    o2, l2 = fa.flash_attn_fwd(qd, kd, vd, causal=True, window_size=window)
     torch.cuda.synchronize()
     for o1, l1 in res:
         assert torch.equal(o1, o2) and torch.equal(l1, l2), what
     if S <= 4096:
-        ref_o, ref_l = oracle.fwd(q, k, v, 1 / math.sqrt(D), True, (-1, -1))
+        ref_o, ref_l = oracle.fwd(q, k, v, 1 / math.sqrt(D), True, window)
         compare(res[0][0], res[0][1], ref_o, ref_l, dtype, what)
